@@ -1,0 +1,21 @@
+"""Plain fp64 CPU oracle for the exact attention forward.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute anything in this package: only the test-suite, the smoke entry point
+and the benchmark's CPU-baseline leg use it.  It shares no code with the HIP
+library (no kernels, headers, helpers, tables or pre/post-processing).
+
+What it computes and which passage of the source pages each function follows
+is stated in ``attention_ref``'s docstrings.  Every function here is pinned by
+CPU tests against values the pages print, closed forms, invariants, a library
+routine and pure-Python brute force (tests/test_oracle.py).
+"""
+
+from .attention_ref import (  # noqa: F401
+    attention_fp64,
+    attention_bruteforce,
+    attention_online_blocked,
+    probabilities_fp64,
+    kv_head_of,
+    allowed_keys,
+)

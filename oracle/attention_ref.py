@@ -1,0 +1,256 @@
+"""fp64 reference for O = softmax(scale * Q K^T) V with per-row logsumexp.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Slow and plain on
+purpose: it materialises every score row and never uses online softmax.
+
+Sources (three web pages on FlashAttention, cited by title and section):
+
+* [P1] "FlashAttention: IO-aware attention kernel" (inference-learning-path
+  course, part 2): §3.1 gives the attention formula and the three
+  materialised tensors S, P, O; §3.2 the running-max / normaliser / output
+  recurrence and its block-merge form; §4 the CPU proof program with a fully
+  worked example whose output it prints.
+* [P2] FlashAttention exam notes (omica.com.cn news item 1422242): §一 the
+  formula and shapes, §二.3 the merge rule for (m, l, o) between K/V blocks
+  (its extracted formulas lost their "=" and "+" signs), §三 the claim that
+  the tiled result carries no approximation error.
+* [P3] "FlashAttention" walkthrough (kyonqi.github.io, nano-vllm series):
+  the three-step standard attention, the "Safe Softmax" section (subtract
+  the row maximum), the "online softmax" section and its proof by induction
+  that the running sum equals the sum of exponentials taken against the
+  running maximum, and "Flash Attention Backward" (what the forward keeps).
+
+Tensor conventions (the plainest reading where the pages are silent):
+
+* q: [B, Hq, Nq, D]; k, v: [B, Hkv, Nkv, D]; o: [B, Hq, Nq, D]; lse: [B, Hq, Nq].
+* Query head h reads key/value head floor(h / (Hq / Hkv)) (consecutive
+  grouping; the pages only use Hq == Hkv).
+* causal: key j is allowed for query i iff j <= i (literal indices, top-left
+  alignment when Nq != Nkv).  Key 0 is always allowed, so no row is empty.
+* scale is taken as the float32 value the GPU receives, widened exactly to
+  float64 (1/sqrt(128) is not exact in float32).
+* lse_i = m_i + ln(l_i): natural log over the scaled scores of the allowed
+  keys.  [P3] "Flash Attention Backward" keeps the row max m and the row sum
+  l for the backward pass; one fp32 number per row carries both.
+"""
+
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+
+def kv_head_of(h: int, Hq: int, Hkv: int) -> int:
+    """Key/value head read by query head ``h`` (consecutive grouping)."""
+    return h // (Hq // Hkv)
+
+
+def allowed_keys(i: int, Nkv: int, causal: bool) -> range:
+    """Key indices query row ``i`` attends to ([P1] §5 uses is_causal=True)."""
+    if causal:
+        return range(0, min(i, Nkv - 1) + 1)
+    return range(Nkv)
+
+
+def _sigma(scale: float) -> float:
+    return float(np.float32(scale))
+
+
+def _check_shapes(q, k, v):
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, N, D]")
+    B, Hq, Nq, D = q.shape
+    Bk, Hkv, Nkv, Dk = k.shape
+    if v.shape != k.shape or Bk != B or Dk != D:
+        raise ValueError(f"shape mismatch q{q.shape} k{k.shape} v{v.shape}")
+    if Hkv < 1 or Hq % Hkv != 0:
+        raise ValueError(f"Hq={Hq} must be a multiple of Hkv={Hkv}")
+    if min(B, Hq, Nq, Nkv, D) < 1:
+        raise ValueError("every dimension must be >= 1")
+    return B, Hq, Hkv, Nq, Nkv, D
+
+
+def _default_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover - non-Linux
+        n = os.cpu_count() or 1
+    return max(1, n)
+
+
+def attention_fp64(q, k, v, scale: float, causal: bool = False,
+                   row_chunk: int = 256, threads: int | None = None):
+    """Exact attention by definition, in float64, materialising full rows.
+
+    For each (b, h) and a chunk of query rows it forms the whole score block
+    S = sigma * Q_chunk K^T ([P1] §3.1, [P3] standard attention step 1),
+    applies the causal mask, then takes the safe softmax of each row: subtract
+    the row maximum, exponentiate, divide by the row sum ([P3] "Safe
+    Softmax"; [P1] §4 ``full_attention``), and forms O = P V ([P3] step 3).
+    lse = m + ln(l).
+
+    Chunking over query rows only bounds memory (a 32768-key row block is
+    256 MiB in fp64); each row is still computed whole.  For causal rows the
+    keys beyond the chunk's last row are never allowed, so they are not
+    formed at all; this drops only terms that are exactly zero.
+
+    Returns (o, lse) as float64 arrays.  Work units (b, h, chunk) run on a
+    thread pool (numpy releases the GIL); BLAS is held to one thread meanwhile.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, Hkv, Nq, Nkv, D = _check_shapes(q, k, v)
+    sigma = _sigma(scale)
+    o = np.empty((B, Hq, Nq, D), dtype=np.float64)
+    lse = np.empty((B, Hq, Nq), dtype=np.float64)
+
+    def work(unit):
+        b, h, r0 = unit
+        r1 = min(r0 + row_chunk, Nq)
+        g = kv_head_of(h, Hq, Hkv)
+        kend = min(Nkv, r1) if causal else Nkv
+        kb = k[b, g, :kend]
+        vb = v[b, g, :kend]
+        s = sigma * (q[b, h, r0:r1] @ kb.T)                  # [R, kend]
+        if causal:
+            rows = np.arange(r0, r1)[:, None]
+            cols = np.arange(kend)[None, :]
+            s = np.where(cols <= rows, s, -np.inf)
+        m = s.max(axis=1)                                    # row maximum
+        e = np.exp(s - m[:, None])                           # masked -> 0
+        l = e.sum(axis=1)                                    # row sum
+        p = e / l[:, None]                                   # probabilities
+        o[b, h, r0:r1] = p @ vb
+        lse[b, h, r0:r1] = m + np.log(l)
+
+    units = [(b, h, r0) for b in range(B) for h in range(Hq)
+             for r0 in range(0, Nq, row_chunk)]
+    nthr = threads or _default_threads()
+    if nthr <= 1 or len(units) == 1:
+        for u in units:
+            work(u)
+    else:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1), ThreadPoolExecutor(max_workers=nthr) as ex:
+            list(ex.map(work, units))
+    return o, lse
+
+
+def probabilities_fp64(q, k, scale: float, causal: bool = False):
+    """Full probability tensor P [B, Hq, Nq, Nkv] (masked entries are 0).
+
+    Same definition as ``attention_fp64`` ([P3] standard attention step 2),
+    for small shapes only; used by tests that read P back through V.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    B, Hq, Hkv, Nq, Nkv, D = _check_shapes(q, k, k)
+    sigma = _sigma(scale)
+    P = np.zeros((B, Hq, Nq, Nkv), dtype=np.float64)
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            s = sigma * (q[b, h] @ k[b, g].T)
+            if causal:
+                s = np.where(np.arange(Nkv)[None, :] <= np.arange(Nq)[:, None],
+                             s, -np.inf)
+            e = np.exp(s - s.max(axis=1, keepdims=True))
+            P[b, h] = e / e.sum(axis=1, keepdims=True)
+    return P
+
+
+def attention_bruteforce(q, k, v, scale: float, causal: bool = False):
+    """Pure-Python element-by-element attention with compensated sums.
+
+    Each dot product, row sum and output sum is a ``math.fsum`` over Python
+    floats, so the only rounding is one per exp/log and per term product.
+    Intended for N <= 16.  Follows [P1] §4 ``full_attention`` (max, exp,
+    normaliser, weighted V) extended with masking and head grouping.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, Hkv, Nq, Nkv, D = _check_shapes(q, k, v)
+    sigma = _sigma(scale)
+    o = np.empty((B, Hq, Nq, D), dtype=np.float64)
+    lse = np.empty((B, Hq, Nq), dtype=np.float64)
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            for i in range(Nq):
+                qi = [float(x) for x in q[b, h, i]]
+                keys = list(allowed_keys(i, Nkv, causal))
+                s = [sigma * math.fsum(qi[t] * float(k[b, g, j, t]) for t in range(D))
+                     for j in keys]
+                m = max(s)
+                e = [math.exp(x - m) for x in s]
+                l = math.fsum(e)
+                for t in range(D):
+                    o[b, h, i, t] = math.fsum(e[n] * float(v[b, g, j, t])
+                                              for n, j in enumerate(keys)) / l
+                lse[b, h, i] = m + math.log(l)
+    return o, lse
+
+
+def attention_online_blocked(q, k, v, scale: float, causal: bool = False,
+                             block: int = 64, on_step=None):
+    """Tiled online-softmax attention in float64 (self-test companion only).
+
+    Streams keys in blocks of ``block``.  For each block it takes the block's
+    own row maximum m~, exponential sum l~ and unnormalised weighted sum o~,
+    then merges with the running (m, l, o) by rescaling both sides to the new
+    maximum ([P1] §3.2; [P2] §二.3, read with the lost "=" and "+" restored:
+    m_new = max(m_old, m_j), l_new = l_old e^(m_old - m_new) + l_j e^(m_j - m_new),
+    o_new likewise with o unnormalised).  A factor whose exponent base is -inf
+    is 0 ([P1] §4 sets the correction to 0 while the running max is -inf).
+    O = o / l once after the last block; lse = m + ln(l).
+
+    ``on_step(b, h, j1, m, l)`` is called after each block with the running
+    row statistics for keys [0, j1), so a test can check the induction
+    invariant of [P3] "online softmax": l equals the sum of e^(s - m) over
+    the keys seen so far.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, Hkv, Nq, Nkv, D = _check_shapes(q, k, v)
+    if block < 1:
+        raise ValueError("block must be >= 1")
+    sigma = _sigma(scale)
+    o_out = np.empty((B, Hq, Nq, D), dtype=np.float64)
+    lse = np.empty((B, Hq, Nq), dtype=np.float64)
+    rows = np.arange(Nq)[:, None]
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            m = np.full(Nq, -np.inf)
+            l = np.zeros(Nq)
+            acc = np.zeros((Nq, D))
+            for j0 in range(0, Nkv, block):
+                j1 = min(j0 + block, Nkv)
+                s = sigma * (q[b, h] @ k[b, g, j0:j1].T)      # [Nq, blk]
+                if causal:
+                    s = np.where(np.arange(j0, j1)[None, :] <= rows, s, -np.inf)
+                m_t = s.max(axis=1)
+                live_t = np.isfinite(m_t)
+                e = np.where(live_t[:, None],
+                             np.exp(s - np.where(live_t, m_t, 0.0)[:, None]), 0.0)
+                l_t = e.sum(axis=1)
+                o_t = e @ v[b, g, j0:j1]
+                m_new = np.maximum(m, m_t)
+                live_new = np.isfinite(m_new)
+                base = np.where(live_new, m_new, 0.0)
+                a_old = np.where(np.isfinite(m), np.exp(m - base), 0.0)
+                a_t = np.where(live_t, np.exp(m_t - base), 0.0)
+                l = a_old * l + a_t * l_t
+                acc = a_old[:, None] * acc + a_t[:, None] * o_t
+                m = m_new
+                if on_step is not None:
+                    on_step(b, h, j1, m.copy(), l.copy())
+            o_out[b, h] = acc / l[:, None]
+            lse[b, h] = m + np.log(l)
+    return o_out, lse

@@ -1,0 +1,299 @@
+"""Pins for the fp64 oracle, independent of the oracle's own code paths.
+
+Each test checks the oracle against something fixed outside it: the values
+the course page "FlashAttention: IO-aware attention kernel" prints for its
+worked example (section 4), closed forms, the induction invariant of the
+"online softmax" section of the kyonqi FlashAttention walkthrough,
+probability-row normalisation, a pure-Python compensated brute force and
+torch's float64 CPU scaled_dot_product_attention.  A dropped term, a wrong
+sign, a wrong index or a transposed operand in the oracle fails at least one.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import logsumexp, softmax
+
+from oracle import (attention_bruteforce, attention_fp64, attention_online_blocked,
+                    probabilities_fp64, kv_head_of)
+import workloads
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_example.json")
+
+
+def _worked():
+    with open(GOLDEN) as f:
+        g = json.load(f)
+    q = np.array(g["q"], dtype=np.float64)[None, None, None, :]
+    K = np.array(g["K"], dtype=np.float64)[None, None]
+    V = np.array(g["V"], dtype=np.float64)[None, None]
+    return g, q, K, V
+
+
+def _rand(B, Hq, Hkv, Nq, Nkv, D, seed, scale_q=1.0):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, Nq, D)) * scale_q
+    k = rng.standard_normal((B, Hkv, Nkv, D))
+    v = rng.standard_normal((B, Hkv, Nkv, D))
+    return q, k, v
+
+
+def _scores(q, k, sigma, causal):
+    """Independent score tensor [B,Hq,Nq,Nkv] via einsum over repeated K heads."""
+    Hq, Hkv = q.shape[1], k.shape[1]
+    kr = np.repeat(k, Hq // Hkv, axis=1)
+    s = sigma * np.einsum("bhid,bhjd->bhij", q, kr)
+    if causal:
+        Nq, Nkv = q.shape[2], k.shape[2]
+        s = np.where(np.arange(Nkv)[None, :] <= np.arange(Nq)[:, None], s, -np.inf)
+    return s
+
+
+# ---- T1: the page's worked example -----------------------------------------
+
+def test_worked_example_printed_output():
+    g, q, K, V = _worked()
+    printed = np.array(g["printed_output_6dp"])
+    for fn in (attention_fp64, attention_bruteforce):
+        o, _ = fn(q, K, V, g["scale"])
+        assert np.max(np.abs(o[0, 0, 0] - printed)) <= 5e-7 + 1e-12
+    for block in range(1, 7):
+        o_b, _ = attention_online_blocked(q, K, V, g["scale"], block=block)
+        assert np.max(np.abs(o_b[0, 0, 0] - printed)) <= 5e-7 + 1e-12
+
+
+def test_worked_example_online_matches_full_to_machine_precision():
+    g, q, K, V = _worked()
+    o_full, l_full = attention_fp64(q, K, V, g["scale"])
+    for block in range(1, 7):
+        o_b, l_b = attention_online_blocked(q, K, V, g["scale"], block=block)
+        # The page prints 1.11e-16 for its block size; allow a few ulps.
+        assert np.max(np.abs(o_b - o_full)) <= 4.5e-16
+        assert abs(l_b[0, 0, 0] - l_full[0, 0, 0]) <= 4.5e-16
+
+
+def test_worked_example_lse_and_probabilities_from_hand_scores():
+    g, q, K, V = _worked()
+    hand = np.array(g["hand_scores"]["values"])
+    o, lse = attention_fp64(q, K, V, g["scale"])
+    assert abs(lse[0, 0, 0] - logsumexp(hand)) <= 1e-13
+    # V's first four rows are the identity, row 5 is all 0.5, row 6 all ones:
+    # O_t = p_t + 0.5 p_5 + p_6 with p the softmax of the hand scores.
+    p = softmax(hand)
+    expect = p[:4] + 0.5 * p[4] + p[5]
+    assert np.max(np.abs(o[0, 0, 0] - expect)) <= 1e-15
+    P = probabilities_fp64(q, K, g["scale"])
+    assert np.max(np.abs(P[0, 0, 0] - p)) <= 1e-15
+
+
+# ---- T2/T3: block-size independence and the induction invariant ------------
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(1, 1, 1, 37, 300, 16), (2, 4, 2, 64, 129, 8),
+                                   (1, 3, 1, 100, 77, 12)])
+def test_blocked_equals_full_for_every_block(causal, shape):
+    B, Hq, Hkv, Nq, Nkv, D = shape
+    q, k, v = _rand(B, Hq, Hkv, Nq, Nkv, D, seed=11)
+    o_f, l_f = attention_fp64(q, k, v, 0.3, causal)
+    for block in (1, 2, 3, 5, 7, 64, Nkv):
+        o_b, l_b = attention_online_blocked(q, k, v, 0.3, causal, block=block)
+        assert np.max(np.abs(o_b - o_f)) <= 1e-14
+        assert np.max(np.abs(l_b - l_f)) <= 1e-13
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_running_sum_invariant_after_every_block(causal):
+    q, k, v = _rand(1, 2, 1, 40, 90, 8, seed=5, scale_q=3.0)
+    sigma = float(np.float32(0.4))
+    s = _scores(q, k, sigma, causal)
+    checked = []
+
+    def on_step(b, h, j1, m, l):
+        seen = s[b, h, :, :j1]
+        m_ref = seen.max(axis=1)
+        fin = np.isfinite(m_ref)
+        assert np.array_equal(np.isfinite(m), fin)
+        assert np.allclose(m[fin], m_ref[fin], rtol=1e-14, atol=1e-14)
+        l_ref = np.where(fin[:, None], np.exp(seen - np.where(fin, m_ref, 0)[:, None]),
+                         0).sum(axis=1)
+        assert np.max(np.abs(l - l_ref) / np.maximum(l_ref, 1)) <= 1e-14
+        checked.append(j1)
+
+    attention_online_blocked(q, k, v, 0.4, causal, block=7, on_step=on_step)
+    assert len(checked) == 2 * math.ceil(90 / 7)
+
+
+# ---- T4/T5: normalisation, V = ones, V = identity --------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_probability_rows_sum_to_one_via_lse(causal):
+    q, k, v = _rand(2, 4, 2, 50, 70, 16, seed=3, scale_q=2.0)
+    _, lse = attention_fp64(q, k, v, 0.25, causal)
+    s = _scores(q, k, float(np.float32(0.25)), causal)
+    P = np.exp(s - lse[..., None])
+    assert np.max(np.abs(P.sum(axis=-1) - 1.0)) <= 1e-13
+    if causal:
+        assert np.all(P[..., np.triu_indices(50, 1, 70)[0], np.triu_indices(50, 1, 70)[1]] == 0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_v_all_ones_gives_all_ones(causal):
+    q, k, _ = _rand(1, 3, 3, 33, 45, 8, seed=4, scale_q=4.0)
+    v = np.ones_like(k)
+    o, _ = attention_fp64(q, k, v, 0.7, causal)
+    assert np.max(np.abs(o - 1.0)) <= 1e-14
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_v_identity_recovers_probabilities(causal):
+    D = 24
+    q, k, _ = _rand(1, 2, 1, 30, D, D, seed=8, scale_q=2.0)
+    v = np.broadcast_to(np.eye(D), (1, 1, D, D)).copy()
+    o, lse = attention_fp64(q, k, v, 0.3, causal)
+    s = _scores(q, k, float(np.float32(0.3)), causal)
+    P = softmax(s, axis=-1)
+    assert np.max(np.abs(o - P)) <= 1e-15
+    assert np.max(np.abs(lse - logsumexp(s, axis=-1))) <= 1e-13
+
+
+# ---- T6: pure-Python brute force on tiny inputs ----------------------------
+
+@pytest.mark.parametrize("shape,causal", [
+    ((1, 1, 1, 6, 6, 4), False), ((2, 2, 2, 9, 13, 5), False),
+    ((1, 7, 1, 11, 11, 3), True), ((1, 4, 2, 16, 5, 6), True),
+    ((2, 2, 1, 5, 16, 7), True), ((1, 1, 1, 1, 1, 1), False)])
+def test_matches_pure_python_bruteforce(shape, causal):
+    B, Hq, Hkv, Nq, Nkv, D = shape
+    q, k, v = _rand(B, Hq, Hkv, Nq, Nkv, D, seed=sum(shape), scale_q=1.5)
+    o_r, l_r = attention_bruteforce(q, k, v, 0.45, causal)
+    o, l = attention_fp64(q, k, v, 0.45, causal, row_chunk=4)
+    assert np.max(np.abs(o - o_r)) <= 1e-14
+    assert np.max(np.abs(l - l_r)) <= 1e-14
+
+
+# ---- T7: closed forms ------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_queries_give_means_of_allowed_values(causal):
+    _, k, v = _rand(1, 2, 2, 1, 40, 8, seed=9)
+    q = np.zeros((1, 2, 40, 8))
+    o, lse = attention_fp64(q, k, v, 0.35, causal)
+    for i in range(40):
+        n = i + 1 if causal else 40
+        assert np.allclose(o[:, :, i], v[:, :, :n].mean(axis=2), rtol=0, atol=1e-14)
+        assert np.allclose(lse[:, :, i], math.log(n), rtol=0, atol=1e-14)
+
+
+def test_single_key_returns_its_value_and_score():
+    q, k, v = _rand(2, 3, 1, 17, 1, 8, seed=10)
+    o, lse = attention_fp64(q, k, v, 0.5, False)
+    assert np.max(np.abs(o - v[:, [0, 0, 0]].repeat(17, axis=2))) <= 1e-15
+    s00 = 0.5 * np.einsum("bhid,bd->bhi", q, k[:, 0, 0])
+    assert np.max(np.abs(lse - s00)) <= 1e-14
+
+
+def test_causal_first_row_is_first_value():
+    q, k, v = _rand(1, 4, 2, 20, 20, 8, seed=12, scale_q=5.0)
+    o, lse = attention_fp64(q, k, v, 0.5, True)
+    for h in range(4):
+        g = kv_head_of(h, 4, 2)
+        assert np.array_equal(o[0, h, 0], v[0, g, 0])
+
+
+def test_dominant_key_without_overflow():
+    """Scores of +/-1e4 would overflow exp without the max subtraction."""
+    D = 8
+    k = np.zeros((1, 1, 5, D))
+    k[0, 0, :, 0] = [-1.0, 0.5, 1.0, 0.25, -0.5]
+    q = np.zeros((1, 1, 3, D))
+    q[0, 0, :, 0] = [2e4, -2e4, 1e4]
+    v = np.arange(5 * D, dtype=np.float64).reshape(1, 1, 5, D)
+    o, lse = attention_fp64(q, k, v, 1.0, False)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    assert np.array_equal(o[0, 0, 0], v[0, 0, 2])      # q*k largest at key 2
+    assert np.array_equal(o[0, 0, 1], v[0, 0, 0])      # sign flips -> key 0
+    assert lse[0, 0, 0] == pytest.approx(2e4, abs=1e-9)
+    assert lse[0, 0, 1] == pytest.approx(2e4, abs=1e-9)
+
+
+# ---- T8: structural identities ---------------------------------------------
+
+def test_causal_row_equals_noncausal_prefix():
+    q, k, v = _rand(1, 2, 2, 30, 30, 8, seed=13)
+    o_c, l_c = attention_fp64(q, k, v, 0.3, True)
+    for i in (0, 1, 7, 29):
+        o_p, l_p = attention_fp64(q[:, :, i:i + 1], k[:, :, :i + 1], v[:, :, :i + 1], 0.3)
+        assert np.max(np.abs(o_c[:, :, i] - o_p[:, :, 0])) <= 1e-15
+        assert np.max(np.abs(l_c[:, :, i] - l_p[:, :, 0])) <= 1e-15
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_equals_mha_with_repeated_kv(causal):
+    q, k, v = _rand(2, 7, 1, 21, 25, 8, seed=14)
+    o_g, l_g = attention_fp64(q, k, v, 0.3, causal)
+    o_m, l_m = attention_fp64(q, np.repeat(k, 7, axis=1), np.repeat(v, 7, axis=1), 0.3, causal)
+    assert np.array_equal(o_g, o_m) and np.array_equal(l_g, l_m)
+    q, k, v = _rand(1, 6, 3, 9, 12, 4, seed=15)
+    o_g, _ = attention_fp64(q, k, v, 0.3, causal)
+    # head h reads kv head h // 2: heads (0,1)->0, (2,3)->1, (4,5)->2
+    o_m, _ = attention_fp64(q, k[:, [0, 0, 1, 1, 2, 2]], v[:, [0, 0, 1, 1, 2, 2]], 0.3, causal)
+    assert np.array_equal(o_g, o_m)
+
+
+def test_key_permutation_invariance_noncausal():
+    q, k, v = _rand(1, 2, 2, 15, 40, 8, seed=16)
+    perm = np.random.default_rng(0).permutation(40)
+    o1, l1 = attention_fp64(q, k, v, 0.3)
+    o2, l2 = attention_fp64(q, k[:, :, perm], v[:, :, perm], 0.3)
+    assert np.max(np.abs(o1 - o2)) <= 1e-14 and np.max(np.abs(l1 - l2)) <= 1e-14
+
+
+# ---- T9: library routine ---------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_matches_torch_sdpa_float64(causal):
+    q, k, v = _rand(2, 4, 4, 70, 70, 16, seed=17, scale_q=2.0)
+    o, _ = attention_fp64(q, k, v, 0.25, causal, row_chunk=32)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+        is_causal=causal, scale=0.25)
+    assert np.max(np.abs(o - ref.numpy())) <= 1e-12
+
+
+def test_threaded_equals_serial():
+    q, k, v = _rand(2, 3, 1, 300, 260, 16, seed=18)
+    a = attention_fp64(q, k, v, 0.3, True, row_chunk=64, threads=1)
+    b = attention_fp64(q, k, v, 0.3, True, row_chunk=64, threads=4)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ---- input generators ------------------------------------------------------
+
+def test_generator_is_deterministic_and_outliers_exact():
+    a = workloads.make_inputs(1, 2, 2, 40, 300, 8, "bf16", seed=3, sigma=0.5,
+                              outlier_frac=0.01, outlier_mult=8.0)
+    b = workloads.make_inputs(1, 2, 2, 40, 300, 8, "bf16", seed=3, sigma=0.5,
+                              outlier_frac=0.01, outlier_mult=8.0)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y) and x.dtype == torch.bfloat16 and x.is_contiguous()
+    plain = workloads.make_inputs(1, 2, 2, 40, 300, 8, "bf16", seed=3, sigma=0.5)
+    assert torch.equal(a[0], plain[0])
+    ratio = a[1].double() / plain[1].double()
+    scaled = (ratio == 8.0).all(dim=-1)
+    same = (ratio == 1.0).all(dim=-1)
+    assert torch.all(scaled | same)
+    assert scaled.sum(dim=-1).tolist() == [[3, 3]]
+
+
+def test_named_workloads_match_their_descriptions():
+    w = workloads.WORKLOADS
+    assert (w[3].B, w[3].Hq, w[3].Nq, w[3].D, w[3].causal) == (2, 32, 8192, 128, False)
+    assert w[3].flops() == pytest.approx(2.199023e12, rel=1e-6)
+    assert (w[5].Hq, w[5].Hkv, w[5].Nkv, w[5].causal) == (28, 4, 32768, True)
+    assert w[1].dtype == "f32" and w[1].scale == np.float32(0.125)

@@ -1,0 +1,114 @@
+"""Seeded synthetic inputs for the attention forward.
+
+This module only draws random tensors; it holds none of the attention
+arithmetic.  Both sides of every comparison take their inputs from here: the
+HIP library (through its Python binding) and the fp64 oracle (which widens the
+very same low-precision values exactly to float64).
+
+The five named workloads have the shapes of the pages' setting: the course
+lab of "FlashAttention: IO-aware attention kernel" (§5) uses random
+[B, H, S, D] bf16 tensors in a 7B decoder's attention shape (28 heads of 128)
+with a causal mask; the others are multi-head and long-sequence variants.
+No public dataset is involved; nothing is read from disk.
+
+Recipe (all workloads): ``numpy.random.default_rng(seed)`` (PCG64), draw Q,
+then K, then (for outlier workloads) the outlier rows of K, then V, each as
+``standard_normal(shape, float32) * sigma``; outlier rows are
+``round(frac * Nkv)`` row indices per (b, kv-head) chosen without
+replacement and multiplied by a power of two (exact, commutes with the cast);
+finally each tensor is cast to the workload dtype with torch's CPU
+round-to-nearest-even conversion.  ``scale`` is float32(1/sqrt(D)).
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, asdict
+
+import numpy as np
+import torch
+
+DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclass(frozen=True)
+class Workload:
+    index: int
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nkv: int
+    D: int
+    dtype: str
+    causal: bool
+    sigma: float = 1.0
+    outlier_frac: float = 0.0
+    outlier_mult: float = 8.0
+
+    @property
+    def seed(self) -> int:
+        return 1000 + self.index
+
+    @property
+    def scale(self) -> float:
+        return default_scale(self.D)
+
+    def flops(self) -> float:
+        """4*B*Hq*Nq*Nkv*D, halved for causal (the throughput metric's count)."""
+        f = 4.0 * self.B * self.Hq * self.Nq * self.Nkv * self.D
+        return f / 2.0 if self.causal else f
+
+    def as_dict(self) -> dict:
+        d = asdict(self)
+        d["seed"] = self.seed
+        return d
+
+
+WORKLOADS = {
+    1: Workload(1, "tiny_exact_f32", 1, 1, 1, 256, 256, 64, "f32", False),
+    2: Workload(2, "multihead_bf16_n1024_d64", 4, 16, 16, 1024, 1024, 64, "bf16", False),
+    3: Workload(3, "long_noncausal_bf16_n8192_d128", 2, 32, 32, 8192, 8192, 128, "bf16", False),
+    4: Workload(4, "causal_gqa_7b_prefill_n4096", 1, 28, 4, 4096, 4096, 128, "bf16", True),
+    5: Workload(5, "long_causal_gqa_n32768_outlier_keys", 1, 28, 4, 32768, 32768, 128, "bf16",
+                True, sigma=0.5, outlier_frac=0.01, outlier_mult=8.0),
+}
+
+
+def default_scale(D: int) -> float:
+    return float(np.float32(1.0 / math.sqrt(D)))
+
+
+def make_inputs(B, Hq, Hkv, Nq, Nkv, D, dtype="bf16", seed=0, sigma=1.0,
+                outlier_frac=0.0, outlier_mult=8.0):
+    """Draw (q, k, v) as contiguous CPU torch tensors of ``dtype``."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, Nq, D), dtype=np.float32)
+    k = rng.standard_normal((B, Hkv, Nkv, D), dtype=np.float32)
+    if sigma != 1.0:
+        q *= np.float32(sigma)
+        k *= np.float32(sigma)
+    if outlier_frac > 0.0:
+        n_out = int(round(outlier_frac * Nkv))
+        for b in range(B):
+            for g in range(Hkv):
+                rows = rng.choice(Nkv, size=n_out, replace=False)
+                k[b, g, rows, :] *= np.float32(outlier_mult)
+    v = rng.standard_normal((B, Hkv, Nkv, D), dtype=np.float32)
+    if sigma != 1.0:
+        v *= np.float32(sigma)
+    tdt = DTYPES[dtype]
+    return tuple(torch.from_numpy(x).to(tdt).contiguous() for x in (q, k, v))
+
+
+def workload_inputs(w: Workload):
+    """(q, k, v, scale) for a named workload."""
+    q, k, v = make_inputs(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, w.dtype, w.seed,
+                          w.sigma, w.outlier_frac, w.outlier_mult)
+    return q, k, v, w.scale
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    """Exact widening of a CPU tensor (f32/f16/bf16) to a float64 array."""
+    return t.detach().to("cpu").to(torch.float64).numpy()
