@@ -1,0 +1,172 @@
+"""Python binding of the exact attention forward library (libfa.so).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/fa.h.  The functions named like
+the C entry points take the same arguments (pointers may be given as ints or
+as torch tensors) and return the C status code.  ``attention`` is the
+convenience form: it checks the tensors, allocates O and lse with torch on
+the inputs' device and launches on torch's current stream.
+
+There is no fallback: if libfa.so is missing or fails to load, every call
+raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
+HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "fa.h")
+
+FA_OK = 0
+FA_ERR_NULL_PTR = 1
+FA_ERR_BAD_DIM = 2
+FA_ERR_HEAD_GROUP = 3
+FA_ERR_HEAD_DIM = 4
+FA_ERR_DTYPE = 5
+FA_ERR_SCALE = 6
+FA_ERR_ALIGN = 7
+FA_ERR_HIP = 8
+FA_ERR_ALIAS = 9
+
+FA_F32 = 0
+FA_F16 = 1
+FA_BF16 = 2
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"fa status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+
+_VP = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_FWD_ARGS = [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _F, _I, _I]
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfa.so once (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise FAError(-1, f"{path} is missing: build it with "
+                          "`python -m exact_io_aware_37_amd.build`")
+    lib = ctypes.CDLL(path)
+    lib.fa_fwd.argtypes = list(_FWD_ARGS)
+    lib.fa_fwd.restype = _I
+    lib.fa_fwd_stream.argtypes = list(_FWD_ARGS) + [_VP]
+    lib.fa_fwd_stream.restype = _I
+    lib.fa_check_args.argtypes = list(_FWD_ARGS)
+    lib.fa_check_args.restype = _I
+    lib.fa_status_string.argtypes = [_I]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_launch_info.argtypes = [_I] * 8 + [ctypes.POINTER(_I)] * 3 + \
+        [ctypes.POINTER(ctypes.c_longlong), ctypes.POINTER(_I)]
+    lib.fa_launch_info.restype = _I
+    _lib = lib
+    return lib
+
+
+def header_functions(path: str = HEADER_PATH) -> list[str]:
+    """Names of the functions include/fa.h declares."""
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+def _ptr(x) -> int | None:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N_q, N_kv, d, scale, causal, dtype) -> int:
+    return load_library().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv,
+                                 N_q, N_kv, d, scale, int(causal), dtype)
+
+
+def fa_fwd_stream(q, k, v, o, lse, B, Hq, Hkv, N_q, N_kv, d, scale, causal, dtype,
+                  stream) -> int:
+    s = stream if (stream is None or isinstance(stream, int)) else stream.cuda_stream
+    return load_library().fa_fwd_stream(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq,
+                                        Hkv, N_q, N_kv, d, scale, int(causal), dtype, s)
+
+
+def fa_check_args(q, k, v, o, lse, B, Hq, Hkv, N_q, N_kv, d, scale, causal, dtype) -> int:
+    return load_library().fa_check_args(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq,
+                                        Hkv, N_q, N_kv, d, scale, int(causal), dtype)
+
+
+def fa_status_string(status: int) -> str:
+    return load_library().fa_status_string(status).decode()
+
+
+def fa_launch_info(B, Hq, Hkv, N_q, N_kv, d, causal, dtype):
+    """(status, dict) with rows_per_block, keys_per_tile, threads, blocks, lds_bytes."""
+    r, kt, th, lds = _I(), _I(), _I(), _I()
+    nb = ctypes.c_longlong()
+    st = load_library().fa_launch_info(B, Hq, Hkv, N_q, N_kv, d, int(causal), dtype,
+                                       ctypes.byref(r), ctypes.byref(kt), ctypes.byref(th),
+                                       ctypes.byref(nb), ctypes.byref(lds))
+    return st, dict(rows_per_block=r.value, keys_per_tile=kt.value, threads=th.value,
+                    blocks=nb.value, lds_bytes=lds.value)
+
+
+def dtype_code(torch_dtype) -> int:
+    import torch
+    codes = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+    if torch_dtype not in codes:
+        raise FAError(FA_ERR_DTYPE, f"unsupported dtype {torch_dtype}")
+    return codes[torch_dtype]
+
+
+def attention(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
+              stream=None):
+    """O, lse = softmax(scale * q k^T) v on the GPU; q [B,Hq,Nq,d], k/v [B,Hkv,Nkv,d].
+
+    ``scale`` defaults to 1/sqrt(d).  ``out``/``lse`` may be given to reuse
+    buffers.  Launches on ``stream`` (default: torch's current stream of q's
+    device) and returns without synchronising.
+    """
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise FAError(FA_ERR_NULL_PTR, f"{name} must be a GPU tensor")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise FAError(FA_ERR_BAD_DIM, f"{name} must be a contiguous 4-D tensor")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise FAError(FA_ERR_DTYPE, "q, k and v must share one dtype")
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nkv, dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or dk != d:
+        raise FAError(FA_ERR_BAD_DIM, f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} "
+                                      f"v{tuple(v.shape)}")
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = fa_fwd_stream(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, d, float(scale), causal,
+                       dtype_code(q.dtype), stream)
+    if st != FA_OK:
+        raise FAError(st, fa_status_string(st))
+    return out, lse
+
+
+__all__ = ["fa_fwd", "fa_fwd_stream", "fa_check_args", "fa_status_string", "fa_launch_info",
+           "attention", "load_library", "header_functions", "FAError", "dtype_code",
+           "FA_F32", "FA_F16", "FA_BF16"]

@@ -1,0 +1,747 @@
+// Exact tiled attention forward for gfx950 (MI355X): kernels and C ABI.
+//
+// One workgroup owns BR consecutive query rows of one (batch, query head).
+// It keeps, per row, a running maximum m, a running exponential sum l and an
+// fp32 output accumulator in registers, streams the key/value sequence in
+// tiles of BC rows through double-buffered LDS, and after the last tile
+// divides by l once and writes O and lse.  This is the recurrence of the
+// course page "FlashAttention: IO-aware attention kernel" (section 3.2: new
+// max, rescale old sum and accumulator by exp(m_old - m_new), add the tile's
+// exponentials) inside the query-tile-outer / key-tile-inner loop of its
+// sections 2 and 3.3.  The omica exam notes (section 2.3, block merge rule)
+// state the same update for whole tiles.  Scores and probabilities exist only
+// in registers; nothing of size N_q x N_kv touches memory.
+//
+// Matrix-core mapping (wave64, 32 query rows per wave):
+//   S^T = K Q^T   v_mfma_f32_32x32x16_{bf16,f16}: A = K rows from LDS, B = Q^T
+//                 held in registers for the whole loop.  The accumulator puts
+//                 one query per lane (lane % 32) and 16 keys per lane in
+//                 registers, so the row max and row sum are in-lane except
+//                 for one exchange between the two half-waves.
+//   O^T += V^T P^T  same instruction: B = P^T straight from the S^T
+//                 accumulator (rounded to the input type), A = V^T read from
+//                 an LDS copy of V that is stored transposed, with keys
+//                 permuted inside each 16-key group so that one 16-byte read
+//                 gives a lane its 8 keys in the order the accumulator holds
+//                 them.  The output accumulator also has one query per lane,
+//                 so the rescale factor and the final 1/l are lane-local.
+// The fp32 variant uses v_mfma_f32_32x32x2_f32 with the same skeleton.
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "fa.h"
+
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
+
+// Launch-independent arguments shared by every kernel variant.
+struct Params {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, Nq, Nkv;
+  int group;      // Hq / Hkv: query heads per key/value head
+  int n_qtiles;   // ceil(Nq / BR)
+  int n_heads;    // B * Hq
+  float sl2;      // |scale| * log2(e), or 1 when scale == 0
+  int qmode;      // 0: Q as given, 1: negated (scale < 0), 2: zeroed (scale == 0)
+};
+
+// ---------------------------------------------------------------- helpers
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+
+__device__ __forceinline__ bool wave_any(bool c) { return __builtin_amdgcn_ballot_w64(c) != 0; }
+
+// Work item of this workgroup.  Non-causal grids are remapped so that the
+// hardware's round-robin dispatch over the 8 XCDs (block i runs on XCD i % 8)
+// hands each XCD a contiguous range of (head, query tile) items: the tiles
+// of one head, which read the same K/V, then share that XCD's L2.  Causal
+// grids keep the dispatch order and list the longest tiles (the last query
+// tiles) first, heads fastest, so that the triangular work drains evenly.
+__device__ __forceinline__ void map_block(const Params& p, bool causal, int& b, int& hq,
+                                          int& qt) {
+  const int bid = blockIdx.x;
+  const int nb = gridDim.x;
+  int hl;
+  if (!causal) {
+    const int xcd = bid & 7, slot = bid >> 3;
+    const int per = nb >> 3, rem = nb & 7;
+    const int logical = xcd * per + (xcd < rem ? xcd : rem) + slot;
+    hl = logical / p.n_qtiles;
+    qt = logical - hl * p.n_qtiles;
+  } else {
+    const int r = bid / p.n_heads;
+    hl = bid - r * p.n_heads;
+    qt = p.n_qtiles - 1 - r;
+  }
+  b = hl / p.Hq;
+  hq = hl - b * p.Hq;
+}
+
+// ----------------------------------------------- 16-bit (bf16 / f16) path
+
+template <typename T>
+struct Mma16;
+
+template <>
+struct Mma16<__bf16> {
+  __device__ static __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ uint32_t pack(float lo, float hi) {
+    bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+};
+
+template <>
+struct Mma16<_Float16> {
+  __device__ static __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ uint32_t pack(float lo, float hi) {
+    f16x2 v = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+};
+
+template <int D>
+struct Cfg16 {
+  static constexpr int NW = 4;             // waves per workgroup
+  static constexpr int NT = 64 * NW;       // threads per workgroup
+  static constexpr int BR = 32 * NW;       // query rows per workgroup
+  static constexpr int BC = 64;            // keys per K/V tile
+  static constexpr int KP = D + 8;         // K tile pitch (elements): 16 B pad per row
+  static constexpr int VP = BC + 8;        // V^T tile pitch (elements): 16 B pad per row
+  static constexpr int KTILE = BC * KP;    // elements
+  static constexpr int VTILE = D * VP;     // elements
+  static constexpr int BUF = KTILE + VTILE;
+  static constexpr int LDS_BYTES = 2 * BUF * 2;
+  static constexpr int KLOADS = BC * D / 8 / NT;      // 16-byte K chunks per thread
+  static constexpr int VITEMS = (BC / 4) * (D / 8);   // (4 keys x 8 dims) V items
+  static_assert(KLOADS >= 1 && BC * D / 8 == KLOADS * NT, "K tile split");
+  static_assert(VITEMS <= NT, "V tile split");
+};
+
+// Position, inside a V^T row, of the 4-key group kg (keys 4kg..4kg+3 of the
+// tile).  Within each 16-key group the S^T accumulator gives lane half 0 the
+// keys {0-3, 8-11} and lane half 1 the keys {4-7, 12-15}; storing the groups
+// in the order 0,2,1,3 makes each half's 8 keys one contiguous 16-byte run.
+__device__ __forceinline__ int vt_pos(int kg) {
+  const int q = kg & 3;
+  return (kg >> 2) * 16 + (((q & 1) << 1) | (q >> 1)) * 4;
+}
+
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(Cfg16<D>::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_fwd_mfma16(Params p) {
+  using C = Cfg16<D>;
+  using M = Mma16<T>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char fa_smem[];
+  uint16_t* smem = reinterpret_cast<uint16_t*>(fa_smem);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+
+  int b, hq, qt;
+  map_block(p, CAUSAL, b, hq, qt);
+  const int hkv = hq / p.group;
+  const int q0 = qt * C::BR;
+  const int qw0 = q0 + wave * 32;   // first query row of this wave
+  const int myq = qw0 + l32;        // query row this lane accumulates
+
+  const uint16_t* Qg = static_cast<const uint16_t*>(p.q) + (size_t)(b * p.Hq + hq) * p.Nq * D;
+  const uint16_t* Kg = static_cast<const uint16_t*>(p.k) + (size_t)(b * p.Hkv + hkv) * p.Nkv * D;
+  const uint16_t* Vg = static_cast<const uint16_t*>(p.v) + (size_t)(b * p.Hkv + hkv) * p.Nkv * D;
+
+  // Q^T operand: lane (l32, half) holds row myq, dims c*16 + half*8 .. +7.
+  u32x4 qreg[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (myq < p.Nq) x = *reinterpret_cast<const u32x4*>(Qg + (size_t)myq * D + c * 16 + half * 8);
+    if (p.qmode == 1) x ^= 0x80008000u;        // exact negation of both halves
+    else if (p.qmode == 2) x = 0u;
+    qreg[c] = x;
+  }
+
+  const int kv_end = CAUSAL ? min(p.Nkv, q0 + C::BR) : p.Nkv;
+  const int n_tiles = (kv_end + C::BC - 1) / C::BC;
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
+  float m_run = -INFINITY;   // running max of scaled scores, log2 units
+  float l_run = 0.f;         // this lane's share of the running sum
+
+  // Global -> register prefetch of one K/V tile.
+  u32x4 kpre[C::KLOADS];
+  u32x4 vpre[4];
+  const int v_dchunk = tid % (D / 8);
+  const int v_kg = tid / (D / 8);
+  const bool v_loader = tid < C::VITEMS;
+
+  auto load_tile = [&](int j) {
+    const int kv0 = j * C::BC;
+#pragma unroll
+    for (int i = 0; i < C::KLOADS; ++i) {
+      const int c = tid + i * C::NT;
+      const int row = c / (D / 8);
+      const int col = (c % (D / 8)) * 8;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (kv0 + row < p.Nkv) x = *reinterpret_cast<const u32x4*>(Kg + (size_t)(kv0 + row) * D + col);
+      kpre[i] = x;
+    }
+    if (v_loader) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = kv0 + v_kg * 4 + r;
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (row < p.Nkv) x = *reinterpret_cast<const u32x4*>(Vg + (size_t)row * D + v_dchunk * 8);
+        vpre[r] = x;
+      }
+    }
+  };
+
+  auto store_tile = [&](int buf) {
+    uint16_t* Ks = smem + buf * C::BUF;
+    uint16_t* Vt = Ks + C::KTILE;
+#pragma unroll
+    for (int i = 0; i < C::KLOADS; ++i) {
+      const int c = tid + i * C::NT;
+      const int row = c / (D / 8);
+      const int col = (c % (D / 8)) * 8;
+      *reinterpret_cast<u32x4*>(Ks + row * C::KP + col) = kpre[i];
+    }
+    if (v_loader) {
+      // vpre[r][e] holds dims (2e, 2e+1) of key r; emit, per dim, the four
+      // keys as one 8-byte V^T store.
+      const int pos = vt_pos(v_kg);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const uint32_t sel = s ? 0x07060302u : 0x05040100u;
+          u32x2 w;
+          w[0] = __builtin_amdgcn_perm(vpre[1][e], vpre[0][e], sel);
+          w[1] = __builtin_amdgcn_perm(vpre[3][e], vpre[2][e], sel);
+          const int d = v_dchunk * 8 + 2 * e + s;
+          *reinterpret_cast<u32x2*>(Vt + d * C::VP + pos) = w;
+        }
+      }
+    }
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int j = 0; j < n_tiles; ++j) {
+    const int kv0 = j * C::BC;
+    if (j + 1 < n_tiles) load_tile(j + 1);
+
+    const uint16_t* Ks = smem + (j & 1) * C::BUF;
+    const uint16_t* Vt = Ks + C::KTILE;
+    // A wave skips tiles that hold no allowed key for any of its rows.
+    const bool active = (qw0 < p.Nq) && (!CAUSAL || kv0 <= qw0 + 31);
+    if (active) {
+      f32x16 s[C::BC / 32];
+#pragma unroll
+      for (int kt = 0; kt < C::BC / 32; ++kt) s[kt] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+#pragma unroll
+        for (int kt = 0; kt < C::BC / 32; ++kt) {
+          const u32x4 a =
+              *reinterpret_cast<const u32x4*>(Ks + (kt * 32 + l32) * C::KP + c * 16 + half * 8);
+          s[kt] = M::mma(a, qreg[c], s[kt]);
+        }
+      }
+
+      // s[kt][r] is the raw score of query myq and key
+      // kv0 + kt*32 + (r/4)*8 + half*4 + r%4.
+      const bool need_mask = (kv0 + C::BC > p.Nkv) || (CAUSAL && kv0 + C::BC - 1 > qw0);
+      if (need_mask) {
+#pragma unroll
+        for (int kt = 0; kt < C::BC / 32; ++kt) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kv0 + kt * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+            const bool masked = (key >= p.Nkv) || (CAUSAL && key > myq);
+            if (masked) s[kt][r] = -INFINITY;
+          }
+        }
+      }
+
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < C::BC / 32; ++kt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+      }
+      mx = fmaxf(mx, xor32(mx));
+      const float m_new = fmaxf(m_run, mx * p.sl2);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);   // 0 while m_run is -inf
+      float ls = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < C::BC / 32; ++kt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = fast_exp2(fmaf(s[kt][r], p.sl2, -m_use));
+          s[kt][r] = e;
+          ls += e;
+        }
+      }
+      l_run = fmaf(l_run, alpha, ls);
+      m_run = m_new;
+      if (wave_any(alpha != 1.f)) {
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
+      }
+
+#pragma unroll
+      for (int kt = 0; kt < C::BC / 32; ++kt) {
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          u32x4 pk;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) pk[w] = M::pack(s[kt][cc * 8 + 2 * w], s[kt][cc * 8 + 2 * w + 1]);
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            const u32x4 a = *reinterpret_cast<const u32x4*>(
+                Vt + (db * 32 + l32) * C::VP + kt * 32 + cc * 16 + half * 8);
+            acc[db] = M::mma(a, pk, acc[db]);
+          }
+        }
+      }
+    }
+
+    if (j + 1 < n_tiles) store_tile((j + 1) & 1);
+    __syncthreads();
+  }
+
+  // Epilogue: combine the half-waves' sums, divide once, write O and lse.
+  const float l_tot = l_run + xor32(l_run);
+  if (myq < p.Nq) {
+    const float inv = 1.f / l_tot;
+    uint16_t* Og = static_cast<uint16_t*>(p.o) + ((size_t)(b * p.Hq + hq) * p.Nq + myq) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 w;
+        w[0] = M::pack(acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv);
+        w[1] = M::pack(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
+        *reinterpret_cast<u32x2*>(Og + db * 32 + g * 8 + half * 4) = w;
+      }
+    }
+    if (half == 0) p.lse[(size_t)(b * p.Hq + hq) * p.Nq + myq] = (m_run + fast_log2(l_tot)) * kLn2;
+  }
+}
+
+// ------------------------------------------------------------- fp32 path
+
+template <int D>
+struct CfgF32 {
+  static constexpr int NW = 4;
+  static constexpr int NT = 64 * NW;
+  static constexpr int BR = 32 * NW;
+  static constexpr int BC = 32;
+  static constexpr int KP = D + 4;    // floats; rows shift by 4 banks
+  static constexpr int VP = D + 8;    // floats; keys k and k+4 land 32 banks apart
+  static constexpr int KTILE = BC * KP;
+  static constexpr int VTILE = BC * VP;
+  static constexpr int BUF = KTILE + VTILE;
+  static constexpr int LDS_BYTES = 2 * BUF * 4;
+  static constexpr int LOADS = BC * D / 4 / NT;   // float4 chunks per thread, per tensor
+  static_assert(LOADS >= 1 && BC * D / 4 == LOADS * NT, "tile split");
+};
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(CfgF32<D>::NT)
+attn_fwd_mfma_f32(Params p) {
+  using C = CfgF32<D>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char fa_smem[];
+  float* smem = reinterpret_cast<float*>(fa_smem);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+
+  int b, hq, qt;
+  map_block(p, CAUSAL, b, hq, qt);
+  const int hkv = hq / p.group;
+  const int q0 = qt * C::BR;
+  const int qw0 = q0 + wave * 32;
+  const int myq = qw0 + l32;
+
+  const float* Qg = static_cast<const float*>(p.q) + (size_t)(b * p.Hq + hq) * p.Nq * D;
+  const float* Kg = static_cast<const float*>(p.k) + (size_t)(b * p.Hkv + hkv) * p.Nkv * D;
+  const float* Vg = static_cast<const float*>(p.v) + (size_t)(b * p.Hkv + hkv) * p.Nkv * D;
+
+  // Contraction slot `half` of MFMA step c covers dim half*(D/2) + c, so each
+  // lane's dims are contiguous: Q^T operand = Q[myq][half*D/2 .. +D/2).
+  float qreg[D / 2];
+#pragma unroll
+  for (int c = 0; c < D / 2; c += 4) {
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+    if (myq < p.Nq) x = *reinterpret_cast<const f32x4*>(Qg + (size_t)myq * D + half * (D / 2) + c);
+    if (p.qmode == 1) x = -x;
+    else if (p.qmode == 2) x = f32x4{0.f, 0.f, 0.f, 0.f};
+    qreg[c] = x[0];
+    qreg[c + 1] = x[1];
+    qreg[c + 2] = x[2];
+    qreg[c + 3] = x[3];
+  }
+
+  const int kv_end = CAUSAL ? min(p.Nkv, q0 + C::BR) : p.Nkv;
+  const int n_tiles = (kv_end + C::BC - 1) / C::BC;
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  f32x4 kpre[C::LOADS];
+  f32x4 vpre[C::LOADS];
+
+  auto load_tile = [&](int j) {
+    const int kv0 = j * C::BC;
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int c = tid + i * C::NT;
+      const int row = c / (D / 4);
+      const int col = (c % (D / 4)) * 4;
+      f32x4 kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
+      if (kv0 + row < p.Nkv) {
+        kx = *reinterpret_cast<const f32x4*>(Kg + (size_t)(kv0 + row) * D + col);
+        vx = *reinterpret_cast<const f32x4*>(Vg + (size_t)(kv0 + row) * D + col);
+      }
+      kpre[i] = kx;
+      vpre[i] = vx;
+    }
+  };
+  auto store_tile = [&](int buf) {
+    float* Ks = smem + buf * C::BUF;
+    float* Vs = Ks + C::KTILE;
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int c = tid + i * C::NT;
+      const int row = c / (D / 4);
+      const int col = (c % (D / 4)) * 4;
+      *reinterpret_cast<f32x4*>(Ks + row * C::KP + col) = kpre[i];
+      *reinterpret_cast<f32x4*>(Vs + row * C::VP + col) = vpre[i];
+    }
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int j = 0; j < n_tiles; ++j) {
+    const int kv0 = j * C::BC;
+    if (j + 1 < n_tiles) load_tile(j + 1);
+    const float* Ks = smem + (j & 1) * C::BUF;
+    const float* Vs = Ks + C::KTILE;
+    const bool active = (qw0 < p.Nq) && (!CAUSAL || kv0 <= qw0 + 31);
+    if (active) {
+      f32x16 s = f32x16{};
+#pragma unroll
+      for (int c = 0; c < D / 2; c += 4) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(Ks + l32 * C::KP + half * (D / 2) + c);
+        s = __builtin_amdgcn_mfma_f32_32x32x2f32(a[0], qreg[c], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x2f32(a[1], qreg[c + 1], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x2f32(a[2], qreg[c + 2], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x2f32(a[3], qreg[c + 3], s, 0, 0, 0);
+      }
+      const bool need_mask = (kv0 + C::BC > p.Nkv) || (CAUSAL && kv0 + C::BC - 1 > qw0);
+      if (need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + (r >> 2) * 8 + half * 4 + (r & 3);
+          if ((key >= p.Nkv) || (CAUSAL && key > myq)) s[r] = -INFINITY;
+        }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      mx = fmaxf(mx, xor32(mx));
+      const float m_new = fmaxf(m_run, mx * p.sl2);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      float ls = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = fast_exp2(fmaf(s[r], p.sl2, -m_use));
+        s[r] = e;
+        ls += e;
+      }
+      l_run = fmaf(l_run, alpha, ls);
+      m_run = m_new;
+      if (wave_any(alpha != 1.f)) {
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
+      }
+      // Register r of S^T holds key (r/4)*8 + half*4 + r%4 for query l32:
+      // contraction slot `half` of step r is that key, so the A operand is
+      // V[key][d] with d = db*32 + l32 (row-major V, no transpose needed).
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = (r >> 2) * 8 + half * 4 + (r & 3);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const float a = Vs[key * C::VP + db * 32 + l32];
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[r], acc[db], 0, 0, 0);
+        }
+      }
+    }
+    if (j + 1 < n_tiles) store_tile((j + 1) & 1);
+    __syncthreads();
+  }
+
+  const float l_tot = l_run + xor32(l_run);
+  if (myq < p.Nq) {
+    const float inv = 1.f / l_tot;
+    float* Og = static_cast<float*>(p.o) + ((size_t)(b * p.Hq + hq) * p.Nq + myq) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 w = {acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv, acc[db][4 * g + 2] * inv,
+                   acc[db][4 * g + 3] * inv};
+        *reinterpret_cast<f32x4*>(Og + db * 32 + g * 8 + half * 4) = w;
+      }
+    }
+    if (half == 0) p.lse[(size_t)(b * p.Hq + hq) * p.Nq + myq] = (m_run + fast_log2(l_tot)) * kLn2;
+  }
+}
+
+// ------------------------------------------------------------ host side
+
+thread_local char g_hip_error[256] = "";
+
+struct Geometry {
+  int rows_per_block;
+  int keys_per_tile;
+  int threads;
+  int lds_bytes;
+};
+
+Geometry geometry_for(int d, int dtype) {
+  if (dtype == FA_F32) {
+    if (d == 64) return {CfgF32<64>::BR, CfgF32<64>::BC, CfgF32<64>::NT, CfgF32<64>::LDS_BYTES};
+    return {CfgF32<128>::BR, CfgF32<128>::BC, CfgF32<128>::NT, CfgF32<128>::LDS_BYTES};
+  }
+  if (d == 64) return {Cfg16<64>::BR, Cfg16<64>::BC, Cfg16<64>::NT, Cfg16<64>::LDS_BYTES};
+  return {Cfg16<128>::BR, Cfg16<128>::BC, Cfg16<128>::NT, Cfg16<128>::LDS_BYTES};
+}
+
+size_t elem_size(int dtype) { return dtype == FA_F32 ? 4 : 2; }
+
+int check_dims(int B, int Hq, int Hkv, int N_q, int N_kv, int d, int dtype, long long* blocks) {
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (B < 1 || Hq < 1 || Hkv < 1 || N_q < 1 || N_kv < 1) return FA_ERR_BAD_DIM;
+  if (Hq % Hkv != 0) return FA_ERR_HEAD_GROUP;
+  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  const Geometry g = geometry_for(d, dtype);
+  const long long tiles = ((long long)N_q + g.rows_per_block - 1) / g.rows_per_block;
+  const long long nb = (long long)B * Hq * tiles;
+  if (nb > 0x7fffffffLL) return FA_ERR_BAD_DIM;
+  // Row offsets are 64-bit, but (b * H + h) and row indices are 32-bit ints.
+  if ((long long)B * Hq > 0x7fffffffLL || (long long)B * Hkv > 0x7fffffffLL) return FA_ERR_BAD_DIM;
+  if (blocks) *blocks = nb;
+  return FA_OK;
+}
+
+bool overlaps(uintptr_t a, size_t na, uintptr_t b, size_t nb) {
+  return a < b + nb && b < a + na;
+}
+
+template <typename Kernel>
+int launch(Kernel kern, int lds_bytes, const Params& p, long long blocks, int threads,
+           hipStream_t stream) {
+  (void)hipGetLastError();   // clear a stale error so the check below is ours
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(threads), lds_bytes, stream, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    snprintf(g_hip_error, sizeof g_hip_error, "HIP error: %s (%s)", hipGetErrorName(e),
+             hipGetErrorString(e));
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
+template <typename Kernel>
+int set_lds_limit(Kernel kern, int lds_bytes) {
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+  if (e != hipSuccess) {
+    snprintf(g_hip_error, sizeof g_hip_error, "HIP error: %s (%s)", hipGetErrorName(e),
+             hipGetErrorString(e));
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
+template <typename T, int D, bool CAUSAL>
+int run16(const Params& p, long long blocks, hipStream_t stream) {
+  using C = Cfg16<D>;
+  static const int attr = set_lds_limit(attn_fwd_mfma16<T, D, CAUSAL>, C::LDS_BYTES);
+  if (attr != FA_OK) return attr;
+  return launch(attn_fwd_mfma16<T, D, CAUSAL>, C::LDS_BYTES, p, blocks, C::NT, stream);
+}
+
+template <int D, bool CAUSAL>
+int run32(const Params& p, long long blocks, hipStream_t stream) {
+  using C = CfgF32<D>;
+  static const int attr = set_lds_limit(attn_fwd_mfma_f32<D, CAUSAL>, C::LDS_BYTES);
+  if (attr != FA_OK) return attr;
+  return launch(attn_fwd_mfma_f32<D, CAUSAL>, C::LDS_BYTES, p, blocks, C::NT, stream);
+}
+
+template <typename T>
+int dispatch16(const Params& p, int d, bool causal, long long blocks, hipStream_t s) {
+  if (d == 64) return causal ? run16<T, 64, true>(p, blocks, s) : run16<T, 64, false>(p, blocks, s);
+  return causal ? run16<T, 128, true>(p, blocks, s) : run16<T, 128, false>(p, blocks, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_check_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                  int B, int Hq, int Hkv, int N_q, int N_kv, int d, float scale, int causal,
+                  int dtype) {
+  (void)causal;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_PTR;
+  const int st = check_dims(B, Hq, Hkv, N_q, N_kv, d, dtype, nullptr);
+  if (st != FA_OK) return st;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  const uintptr_t pq = (uintptr_t)q, pk = (uintptr_t)k, pv = (uintptr_t)v, po = (uintptr_t)o,
+                  pl = (uintptr_t)lse;
+  if (((pq | pk | pv | po) & 15u) != 0 || (pl & 3u) != 0) return FA_ERR_ALIGN;
+  const size_t es = elem_size(dtype);
+  const size_t nq = (size_t)B * Hq * N_q * d * es;
+  const size_t nkv = (size_t)B * Hkv * N_kv * d * es;
+  const size_t nl = (size_t)B * Hq * N_q * sizeof(float);
+  if (overlaps(po, nq, pq, nq) || overlaps(po, nq, pk, nkv) || overlaps(po, nq, pv, nkv) ||
+      overlaps(pl, nl, pq, nq) || overlaps(pl, nl, pk, nkv) || overlaps(pl, nl, pv, nkv) ||
+      overlaps(po, nq, pl, nl))
+    return FA_ERR_ALIAS;
+  return FA_OK;
+}
+
+int fa_launch_info(int B, int Hq, int Hkv, int N_q, int N_kv, int d, int causal, int dtype,
+                   int* rows_per_block, int* keys_per_tile, int* threads_per_block,
+                   long long* blocks, int* lds_bytes) {
+  (void)causal;
+  long long nb = 0;
+  const int st = check_dims(B, Hq, Hkv, N_q, N_kv, d, dtype, &nb);
+  if (st != FA_OK) return st;
+  const Geometry g = geometry_for(d, dtype);
+  if (rows_per_block) *rows_per_block = g.rows_per_block;
+  if (keys_per_tile) *keys_per_tile = g.keys_per_tile;
+  if (threads_per_block) *threads_per_block = g.threads;
+  if (blocks) *blocks = nb;
+  if (lds_bytes) *lds_bytes = g.lds_bytes;
+  return FA_OK;
+}
+
+int fa_fwd_stream(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                  int Hq, int Hkv, int N_q, int N_kv, int d, float scale, int causal, int dtype,
+                  void* stream) {
+  const int st = fa_check_args(q, k, v, o, lse, B, Hq, Hkv, N_q, N_kv, d, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  long long blocks = 0;
+  check_dims(B, Hq, Hkv, N_q, N_kv, d, dtype, &blocks);
+  const Geometry g = geometry_for(d, dtype);
+
+  Params p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Nq = N_q;
+  p.Nkv = N_kv;
+  p.group = Hq / Hkv;
+  p.n_qtiles = (N_q + g.rows_per_block - 1) / g.rows_per_block;
+  p.n_heads = B * Hq;
+  if (scale > 0.f) {
+    p.sl2 = scale * kLog2e;
+    p.qmode = 0;
+  } else if (scale < 0.f) {
+    p.sl2 = -scale * kLog2e;
+    p.qmode = 1;
+  } else {
+    p.sl2 = 1.f;
+    p.qmode = 2;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool c = causal != 0;
+  switch (dtype) {
+    case FA_BF16: return dispatch16<__bf16>(p, d, c, blocks, s);
+    case FA_F16: return dispatch16<_Float16>(p, d, c, blocks, s);
+    default:
+      if (d == 64) return c ? run32<64, true>(p, blocks, s) : run32<64, false>(p, blocks, s);
+      return c ? run32<128, true>(p, blocks, s) : run32<128, false>(p, blocks, s);
+  }
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+           int Hkv, int N_q, int N_kv, int d, float scale, int causal, int dtype) {
+  return fa_fwd_stream(q, k, v, o, lse, B, Hq, Hkv, N_q, N_kv, d, scale, causal, dtype, nullptr);
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL_PTR: return "a required pointer is NULL";
+    case FA_ERR_BAD_DIM: return "a dimension is < 1 or the launch grid would be too large";
+    case FA_ERR_HEAD_GROUP: return "Hq is not a multiple of Hkv";
+    case FA_ERR_HEAD_DIM: return "head dimension d must be 64 or 128";
+    case FA_ERR_DTYPE: return "dtype must be FA_F32, FA_F16 or FA_BF16";
+    case FA_ERR_SCALE: return "scale must be finite";
+    case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
+    case FA_ERR_ALIAS: return "o or lse overlaps an input or each other";
+    case FA_ERR_HIP: return g_hip_error[0] ? g_hip_error : "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

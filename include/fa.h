@@ -1,0 +1,114 @@
+/*
+ * fa.h - C ABI of the exact attention forward for AMD MI355X (gfx950).
+ *
+ * Operation.  For every batch b, query head h and query row i:
+ *
+ *     O[b,h,i,:] = sum_j softmax_j(scale * Q[b,h,i,:] . K[b,g,j,:]) * V[b,g,j,:]
+ *     lse[b,h,i] = ln( sum_j exp(scale * Q[b,h,i,:] . K[b,g,j,:]) )
+ *
+ * over the allowed keys j, with g = h / (Hq / Hkv).  This is the attention
+ * formula of the course page "FlashAttention: IO-aware attention kernel"
+ * (section 3.1), computed the way its section 3.2 describes: each query tile
+ * keeps a running maximum, a running normaliser and an output accumulator
+ * on chip, streams K/V tiles and rescales by exp(m_old - m_new), dividing by
+ * the normaliser once at the end (section 2's two-loop picture).  No score
+ * or probability matrix is written to memory.  lse carries the row maximum
+ * and row sum that the kyonqi FlashAttention walkthrough ("Flash Attention
+ * Backward") keeps for a backward pass, folded into one number per row.
+ *
+ * Masking.  causal = 0: every key 0 <= j < N_kv is allowed.  causal != 0:
+ * key j is allowed for query i iff j <= i, with literal indices (top-left
+ * alignment when N_q != N_kv; key 0 is always allowed, so no row is empty).
+ *
+ * Layout.  All tensors dense, row-major, head dimension fastest:
+ *     q   [B, Hq,  N_q,  d]   dtype
+ *     k,v [B, Hkv, N_kv, d]   dtype
+ *     o   [B, Hq,  N_q,  d]   dtype (rounded to nearest even from fp32)
+ *     lse [B, Hq,  N_q]       float32
+ * q, k, v, o must be 16-byte aligned device pointers, lse 4-byte aligned.
+ * o and lse must not overlap q, k or v (or each other).
+ *
+ * Arithmetic.  dtype FA_BF16 / FA_F16: products on the bf16/f16 matrix
+ * cores with fp32 accumulation; probabilities are rounded to the input
+ * dtype (round to nearest even) before the P*V product, the normaliser is
+ * summed from the unrounded fp32 values.  dtype FA_F32: fp32 matrix cores,
+ * no intermediate rounding below fp32.
+ *
+ * Ownership.  The caller allocates and owns every buffer.  The library
+ * allocates no device or host memory, keeps no pointer after a call returns
+ * and holds no state besides per-kernel attributes set once.
+ *
+ * Errors.  Every entry point returns an fa_status.  All arguments are
+ * validated on the host before any HIP call; an invalid call returns its
+ * error code without touching the device.  FA_ERR_HIP reports a launch or
+ * runtime error; fa_status_string(FA_ERR_HIP) then names the HIP error of
+ * the calling thread's last failing call.  Launches are asynchronous: a
+ * fault inside the kernel surfaces at the caller's next synchronisation.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+    FA_OK = 0,
+    FA_ERR_NULL_PTR = 1,   /* a required pointer is NULL                        */
+    FA_ERR_BAD_DIM = 2,    /* B, Hq, Hkv, N_q or N_kv < 1, or the grid too large */
+    FA_ERR_HEAD_GROUP = 3, /* Hq is not a multiple of Hkv                        */
+    FA_ERR_HEAD_DIM = 4,   /* d is not 64 or 128                                 */
+    FA_ERR_DTYPE = 5,      /* dtype is not one of fa_dtype                       */
+    FA_ERR_SCALE = 6,      /* scale is NaN or infinite                           */
+    FA_ERR_ALIGN = 7,      /* a pointer is misaligned                            */
+    FA_ERR_HIP = 8,        /* the HIP runtime reported an error                  */
+    FA_ERR_ALIAS = 9       /* o or lse overlaps q, k, v or each other            */
+} fa_status;
+
+typedef enum fa_dtype {
+    FA_F32 = 0,
+    FA_F16 = 1,
+    FA_BF16 = 2
+} fa_dtype;
+
+/*
+ * Exact attention forward, launched on the null (default) stream.
+ * scale is applied as given (callers usually pass 1/sqrt(d)); any finite
+ * value is accepted, including 0 and negative values.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int Hq, int Hkv, int N_q, int N_kv, int d,
+           float scale, int causal, int dtype);
+
+/* Same as fa_fwd, launched on the given hipStream_t (NULL = null stream). */
+int fa_fwd_stream(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int Hq, int Hkv, int N_q, int N_kv, int d,
+                  float scale, int causal, int dtype, void* stream);
+
+/*
+ * Host-only argument check used by both entry points: returns the status
+ * fa_fwd would return for these arguments before launching (FA_OK when they
+ * are valid).  Makes no HIP call.
+ */
+int fa_check_args(const void* q, const void* k, const void* v, const void* o,
+                  const float* lse, int B, int Hq, int Hkv, int N_q, int N_kv,
+                  int d, float scale, int causal, int dtype);
+
+/* Static description of a status code (FA_ERR_HIP adds the HIP error text). */
+const char* fa_status_string(int status);
+
+/*
+ * Launch geometry the library uses for these arguments: query rows per
+ * workgroup, keys per K/V tile, threads per workgroup, workgroups in the
+ * grid and bytes of LDS per workgroup.  Returns an fa_status like
+ * fa_check_args (pointers are not inspected).  Makes no HIP call.
+ */
+int fa_launch_info(int B, int Hq, int Hkv, int N_q, int N_kv, int d, int causal,
+                   int dtype, int* rows_per_block, int* keys_per_tile,
+                   int* threads_per_block, long long* blocks, int* lds_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -82,7 +82,7 @@ def _default_threads() -> int:
 
 
 def attention_fp64(q, k, v, scale: float, causal: bool = False,
-                   row_chunk: int = 256, threads: int | None = None):
+                   row_chunk: int = 256, threads: int | None = None, rows=None):
     """Exact attention by definition, in float64, materialising full rows.
 
     For each (b, h) and a chunk of query rows it forms the whole score block
@@ -97,6 +97,11 @@ def attention_fp64(q, k, v, scale: float, causal: bool = False,
     keys beyond the chunk's last row are never allowed, so they are not
     formed at all; this drops only terms that are exactly zero.
 
+    ``rows`` (optional) lists absolute query indices to evaluate; the result
+    then has len(rows) rows in that order (causal masking still uses the
+    absolute index).  Used to check single rows of workloads too large to
+    evaluate whole.
+
     Returns (o, lse) as float64 arrays.  Work units (b, h, chunk) run on a
     thread pool (numpy releases the GIL); BLAS is held to one thread meanwhile.
     """
@@ -105,21 +110,24 @@ def attention_fp64(q, k, v, scale: float, causal: bool = False,
     v = np.asarray(v, dtype=np.float64)
     B, Hq, Hkv, Nq, Nkv, D = _check_shapes(q, k, v)
     sigma = _sigma(scale)
-    o = np.empty((B, Hq, Nq, D), dtype=np.float64)
-    lse = np.empty((B, Hq, Nq), dtype=np.float64)
+    idx_all = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64).reshape(-1)
+    if idx_all.size and (idx_all.min() < 0 or idx_all.max() >= Nq):
+        raise ValueError("rows out of range")
+    R = idx_all.size
+    o = np.empty((B, Hq, R, D), dtype=np.float64)
+    lse = np.empty((B, Hq, R), dtype=np.float64)
 
     def work(unit):
         b, h, r0 = unit
-        r1 = min(r0 + row_chunk, Nq)
+        r1 = min(r0 + row_chunk, R)
+        idx = idx_all[r0:r1]
         g = kv_head_of(h, Hq, Hkv)
-        kend = min(Nkv, r1) if causal else Nkv
+        kend = min(Nkv, int(idx.max()) + 1) if causal else Nkv
         kb = k[b, g, :kend]
         vb = v[b, g, :kend]
-        s = sigma * (q[b, h, r0:r1] @ kb.T)                  # [R, kend]
+        s = sigma * (q[b, h, idx] @ kb.T)                    # [R, kend]
         if causal:
-            rows = np.arange(r0, r1)[:, None]
-            cols = np.arange(kend)[None, :]
-            s = np.where(cols <= rows, s, -np.inf)
+            s = np.where(np.arange(kend)[None, :] <= idx[:, None], s, -np.inf)
         m = s.max(axis=1)                                    # row maximum
         e = np.exp(s - m[:, None])                           # masked -> 0
         l = e.sum(axis=1)                                    # row sum
@@ -128,7 +136,7 @@ def attention_fp64(q, k, v, scale: float, causal: bool = False,
         lse[b, h, r0:r1] = m + np.log(l)
 
     units = [(b, h, r0) for b in range(B) for h in range(Hq)
-             for r0 in range(0, Nq, row_chunk)]
+             for r0 in range(0, R, row_chunk)]
     nthr = threads or _default_threads()
     if nthr <= 1 or len(units) == 1:
         for u in units:

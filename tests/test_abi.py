@@ -1,0 +1,139 @@
+"""C-ABI checks that need no GPU: the library loads, exports what include/fa.h
+declares, and rejects every invalid call on the host before any HIP call."""
+
+import ctypes
+import math
+
+import pytest
+
+import exact_io_aware_37_amd as fa
+
+# Fake, 16-byte aligned, non-overlapping addresses: only fa_check_args and the
+# argument-check path of fa_fwd see them; no call here reaches a launch.
+Q, K, V, O, L = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+GOOD = dict(B=2, Hq=8, Hkv=2, N_q=100, N_kv=77, d=128, scale=0.125, causal=1, dtype=fa.FA_BF16)
+
+
+def args(**kw):
+    a = dict(GOOD)
+    a.update(kw)
+    return a
+
+
+def check(q=Q, k=K, v=V, o=O, lse=L, **kw):
+    a = args(**kw)
+    return fa.fa_check_args(q, k, v, o, lse, a["B"], a["Hq"], a["Hkv"], a["N_q"], a["N_kv"],
+                            a["d"], a["scale"], a["causal"], a["dtype"])
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fa.load_library()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = fa.header_functions()
+    assert set(names) == {"fa_fwd", "fa_fwd_stream", "fa_check_args", "fa_status_string",
+                          "fa_launch_info"}
+    for n in names:
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_valid_arguments_pass(lib):
+    assert check() == fa.FA_OK
+    for dt in (fa.FA_F32, fa.FA_F16, fa.FA_BF16):
+        for d in (64, 128):
+            assert check(dtype=dt, d=d) == fa.FA_OK
+    assert check(scale=0.0) == fa.FA_OK and check(scale=-2.0) == fa.FA_OK
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse"])
+def test_null_pointers(lib, which):
+    assert check(**{which: 0}) == fa.FA_ERR_NULL_PTR
+
+
+@pytest.mark.parametrize("field", ["B", "Hq", "Hkv", "N_q", "N_kv"])
+@pytest.mark.parametrize("value", [0, -1])
+def test_non_positive_dims(lib, field, value):
+    kw = {field: value}
+    if field == "Hkv" and value == 0:
+        kw["Hq"] = 8
+    assert check(**kw) == fa.FA_ERR_BAD_DIM
+
+
+def test_head_group(lib):
+    assert check(Hq=7, Hkv=2) == fa.FA_ERR_HEAD_GROUP
+    assert check(Hq=28, Hkv=4) == fa.FA_OK
+
+
+@pytest.mark.parametrize("d", [1, 32, 63, 96, 127, 256])
+def test_head_dim(lib, d):
+    assert check(d=d) == fa.FA_ERR_HEAD_DIM
+
+
+@pytest.mark.parametrize("dtype", [-1, 3, 99])
+def test_dtype(lib, dtype):
+    assert check(dtype=dtype) == fa.FA_ERR_DTYPE
+
+
+@pytest.mark.parametrize("scale", [math.nan, math.inf, -math.inf])
+def test_scale(lib, scale):
+    assert check(scale=scale) == fa.FA_ERR_SCALE
+
+
+def test_alignment(lib):
+    assert check(q=Q + 8) == fa.FA_ERR_ALIGN
+    assert check(o=O + 2) == fa.FA_ERR_ALIGN
+    assert check(lse=L + 2) == fa.FA_ERR_ALIGN
+    assert check(lse=L + 4) == fa.FA_OK
+
+
+def test_aliasing(lib):
+    assert check(o=Q) == fa.FA_ERR_ALIAS
+    assert check(lse=V + 64) == fa.FA_ERR_ALIAS
+    assert check(lse=O + 16) == fa.FA_ERR_ALIAS
+    # o = [B,Hq,N_q,d] bf16 = 409600 bytes: a buffer right after it is fine
+    assert check(lse=O + 2 * 8 * 100 * 128 * 2) == fa.FA_OK
+
+
+def test_grid_too_large(lib):
+    assert check(B=65536, Hq=65536, Hkv=1, N_q=128) == fa.FA_ERR_BAD_DIM
+
+
+def test_fwd_rejects_on_host_without_touching_hip(lib):
+    # Invalid calls return their code from fa_fwd and fa_fwd_stream too; with
+    # no GPU in this process a call that reached HIP would report FA_ERR_HIP.
+    a = args(d=96)
+    st = fa.fa_fwd(Q, K, V, O, L, a["B"], a["Hq"], a["Hkv"], a["N_q"], a["N_kv"], a["d"],
+                   a["scale"], a["causal"], a["dtype"])
+    assert st == fa.FA_ERR_HEAD_DIM
+    st = fa.fa_fwd_stream(0, K, V, O, L, 1, 1, 1, 1, 1, 64, 1.0, 0, fa.FA_BF16, None)
+    assert st == fa.FA_ERR_NULL_PTR
+    st = fa.fa_fwd_stream(Q, K, V, O, L, 1, 3, 2, 1, 1, 64, 1.0, 0, fa.FA_BF16, None)
+    assert st == fa.FA_ERR_HEAD_GROUP
+
+
+def test_status_strings(lib):
+    for st in range(0, 10):
+        s = fa.fa_status_string(st)
+        assert isinstance(s, str) and s
+    assert fa.fa_status_string(123) == "unknown status"
+
+
+def test_launch_info(lib):
+    st, info = fa.fa_launch_info(2, 32, 32, 8192, 8192, 128, 0, fa.FA_BF16)
+    assert st == fa.FA_OK
+    assert info["threads"] % 64 == 0 and info["rows_per_block"] % 32 == 0
+    assert info["blocks"] == 2 * 32 * math.ceil(8192 / info["rows_per_block"])
+    assert 0 < info["lds_bytes"] <= 160 * 1024
+    st, info = fa.fa_launch_info(1, 1, 1, 256, 256, 64, 0, fa.FA_F32)
+    assert st == fa.FA_OK and info["blocks"] == math.ceil(256 / info["rows_per_block"])
+    assert fa.fa_launch_info(1, 1, 1, 0, 1, 64, 0, fa.FA_F32)[0] == fa.FA_ERR_BAD_DIM
+
+
+def test_python_wrapper_rejects_cpu_tensors(lib):
+    import torch
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(fa.FAError):
+        fa.attention(q, q, q)

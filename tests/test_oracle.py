@@ -297,3 +297,13 @@ def test_named_workloads_match_their_descriptions():
     assert w[3].flops() == pytest.approx(2.199023e12, rel=1e-6)
     assert (w[5].Hq, w[5].Hkv, w[5].Nkv, w[5].causal) == (28, 4, 32768, True)
     assert w[1].dtype == "f32" and w[1].scale == np.float32(0.125)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_row_subset_matches_whole(causal):
+    q, k, v = _rand(1, 4, 2, 300, 280, 16, seed=19)
+    o, l = attention_fp64(q, k, v, 0.3, causal)
+    rows = np.array([299, 0, 5, 137, 256, 255, 1])
+    o_r, l_r = attention_fp64(q, k, v, 0.3, causal, rows=rows, row_chunk=3)
+    assert np.array_equal(o_r, o[:, :, rows]) or np.max(np.abs(o_r - o[:, :, rows])) <= 1e-15
+    assert np.max(np.abs(l_r - l[:, :, rows])) <= 1e-15
