@@ -33,7 +33,7 @@ def hipcc() -> str:
 def build(verbose: bool = False, extra_flags=()) -> str:
     """Compile the library; returns the path of the built shared object."""
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-shared",
            "-Wall", "-Wno-unused-result", f"-I{INCLUDE}",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            *extra_flags, SRC, "-o", tmp]

@@ -102,6 +102,62 @@ __device__ __forceinline__ void map_block(const Params& p, bool causal, int& b, 
 }
 
 // ----------------------------------------------- 16-bit (bf16 / f16) path
+//
+// Workgroup: 8 waves x 32 query rows = 256 rows.  K/V tiles of 64 keys move
+// global -> LDS by buffer DMA (buffer_load ... lds, 16 B per lane, no VGPR
+// staging; rows past N_kv come back as zeros) into a 4-stage ring, issued two
+// tiles ahead.  K is stored row-major with an XOR swizzle of its 16-byte
+// chunks (conflict-free 16-byte operand reads); V is stored row-major too,
+// with its own swizzle, and read transposed by ds_read_b64_tr_b16, which
+// hands each lane four keys of one head-dimension column: the V^T operand of
+// the P*V product without any transpose pass.
+//
+// Main loop (tiles that need no mask), software-pipelined per wave:
+//   phase A: MFMA S(j+1) = K(j+1) Q^T   ||  VALU exp(S(j)) -> P(j), row sums
+//   phase B: MFMA O += V(j) P(j)        ||  VALU row max of S(j+1), new reference
+// Diagonal (causal) and ragged-tail tiles run afterwards through a plain,
+// masked, non-pipelined step.
+//
+// The exponent reference is lazy: it moves to the new running max only when
+// that max exceeds it by more than 2^8 (then O and the sum are rescaled by
+// exp2(m_old - m_new)).  Otherwise probabilities are taken against the older,
+// smaller reference and stay below 2^8.  O / l and lse = ref + log2(l) are
+// the same whatever reference is used, so the result stays exact; only the
+// rescale work is skipped.
+
+typedef __attribute__((address_space(3))) unsigned char lds_t;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+constexpr float kLazy = 8.0f;   // log2 of the largest probability the lazy reference allows
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // Raw buffer (stride 0): loads past `bytes` return zero, stores past it are dropped.
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// and all its LDS operations completed (s_waitcnt vmcnt(N) lgkmcnt(0)).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+}
+
+// Combine the two half-waves' values of a lane pair (l, l ^ 32) with
+// v_permlane32_swap; both lanes of a pair get the same, bitwise-identical
+// result (max and + are commutative).
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 template <typename T>
 struct Mma16;
@@ -116,6 +172,11 @@ struct Mma16<__bf16> {
     bf16x2 v = {(__bf16)lo, (__bf16)hi};
     return __builtin_bit_cast(uint32_t, v);
   }
+  // acc + lo + hi of a packed pair, accumulated in fp32.
+  __device__ static __forceinline__ float sum2(uint32_t pair, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair),
+                                           __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
+  }
 };
 
 template <>
@@ -128,46 +189,75 @@ struct Mma16<_Float16> {
     f16x2 v = {(_Float16)lo, (_Float16)hi};
     return __builtin_bit_cast(uint32_t, v);
   }
+  __device__ static __forceinline__ float sum2(uint32_t pair, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair),
+                                  __builtin_bit_cast(f16x2, 0x3c003c00u), acc, false);
+  }
 };
 
 template <int D>
 struct Cfg16 {
-  static constexpr int NW = 4;             // waves per workgroup
-  static constexpr int NT = 64 * NW;       // threads per workgroup
-  static constexpr int BR = 32 * NW;       // query rows per workgroup
-  static constexpr int BC = 64;            // keys per K/V tile
-  static constexpr int KP = D + 8;         // K tile pitch (elements): 16 B pad per row
-  static constexpr int VP = BC + 8;        // V^T tile pitch (elements): 16 B pad per row
-  static constexpr int KTILE = BC * KP;    // elements
-  static constexpr int VTILE = D * VP;     // elements
-  static constexpr int BUF = KTILE + VTILE;
-  static constexpr int LDS_BYTES = 2 * BUF * 2;
-  static constexpr int KLOADS = BC * D / 8 / NT;      // 16-byte K chunks per thread
-  static constexpr int VITEMS = (BC / 4) * (D / 8);   // (4 keys x 8 dims) V items
-  static_assert(KLOADS >= 1 && BC * D / 8 == KLOADS * NT, "K tile split");
-  static_assert(VITEMS <= NT, "V tile split");
+  static constexpr int NW = 8;                  // waves per workgroup
+  static constexpr int NT = 64 * NW;            // threads per workgroup
+  static constexpr int BR = 32 * NW;            // query rows per workgroup
+  static constexpr int BC = 64;                 // keys per K/V tile
+  static constexpr int STAGES = 4;              // LDS ring depth (tiles)
+  static constexpr int ROWB = D * 2;            // bytes per K/V row
+  static constexpr int NCH = D / 8;             // 16-byte chunks per row
+  static constexpr int TILEB = BC * ROWB;       // bytes of one K (or V) tile
+  static constexpr int STAGEB = 2 * TILEB;      // K tile then V tile
+  static constexpr int LDS_BYTES = STAGES * STAGEB;
+  static constexpr int CHUNKS = STAGEB / 1024;  // 1 KiB DMA instructions per tile
+  static constexpr int DPW = CHUNKS / NW;       // ... per wave
+  static_assert(DPW * NW == CHUNKS && DPW >= 1, "DMA split");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
-// Position, inside a V^T row, of the 4-key group kg (keys 4kg..4kg+3 of the
-// tile).  Within each 16-key group the S^T accumulator gives lane half 0 the
-// keys {0-3, 8-11} and lane half 1 the keys {4-7, 12-15}; storing the groups
-// in the order 0,2,1,3 makes each half's 8 keys one contiguous 16-byte run.
-__device__ __forceinline__ int vt_pos(int kg) {
-  const int q = kg & 3;
-  return (kg >> 2) * 16 + (((q & 1) << 1) | (q >> 1)) * 4;
+// XOR swizzles of the 16-byte chunk index within a row (period 16 rows).
+// K: 16 consecutive rows read the same logical chunk -> 16 distinct chunks.
+// V: a transposed read touches 4 consecutive rows x 4 chunks -> 16 distinct.
+template <int D>
+__device__ __forceinline__ int swz_k(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int swz_v(int row) {
+  return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
 }
 
+// Body of the 16-bit kernel.  It lives in a device function because the
+// host compilation pass does not emit launch stubs for kernel templates whose
+// own body holds template lambdas.
 template <typename T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(Cfg16<D>::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
-attn_fwd_mfma16(Params p) {
+__device__ __forceinline__ void attn_fwd_mfma16_body(const Params& p) {
   using C = Cfg16<D>;
   using M = Mma16<T>;
-  extern __shared__ __attribute__((aligned(16))) unsigned char fa_smem[];
-  uint16_t* smem = reinterpret_cast<uint16_t*>(fa_smem);
+  // One LDS object per ring stage and operand: with compile-time stage
+  // indices the compiler can tell a read of one stage from a DMA into another
+  // and does not stall the read on the unrelated transfer; the K ring fills
+  // the first 64 KiB so every K stage offset fits a ds_read immediate.
+  __shared__ __attribute__((aligned(1024))) unsigned char k0[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char k1[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char k2[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char k3[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char v0[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char v1[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char v2[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char v3[C::TILEB];
+  auto kst = [&]<int S>() -> lds_t* {
+    if constexpr ((S & 3) == 0) return (lds_t*)k0;
+    else if constexpr ((S & 3) == 1) return (lds_t*)k1;
+    else if constexpr ((S & 3) == 2) return (lds_t*)k2;
+    else return (lds_t*)k3;
+  };
+  auto vst = [&]<int S>() -> lds_t* {
+    if constexpr ((S & 3) == 0) return (lds_t*)v0;
+    else if constexpr ((S & 3) == 1) return (lds_t*)v1;
+    else if constexpr ((S & 3) == 2) return (lds_t*)v2;
+    else return (lds_t*)v3;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
@@ -176,196 +266,269 @@ attn_fwd_mfma16(Params p) {
   const int hkv = hq / p.group;
   const int q0 = qt * C::BR;
   const int qw0 = q0 + wave * 32;   // first query row of this wave
-  const int myq = qw0 + l32;        // query row this lane accumulates
+  const int myq = qw0 + l32;        // query row whose O column and statistics this lane holds
 
-  const uint16_t* Qg = static_cast<const uint16_t*>(p.q) + (size_t)(b * p.Hq + hq) * p.Nq * D;
-  const uint16_t* Kg = static_cast<const uint16_t*>(p.k) + (size_t)(b * p.Hkv + hkv) * p.Nkv * D;
-  const uint16_t* Vg = static_cast<const uint16_t*>(p.v) + (size_t)(b * p.Hkv + hkv) * p.Nkv * D;
-
-  // Q^T operand: lane (l32, half) holds row myq, dims c*16 + half*8 .. +7.
-  u32x4 qreg[D / 16];
-#pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (myq < p.Nq) x = *reinterpret_cast<const u32x4*>(Qg + (size_t)myq * D + c * 16 + half * 8);
-    if (p.qmode == 1) x ^= 0x80008000u;        // exact negation of both halves
-    else if (p.qmode == 2) x = 0u;
-    qreg[c] = x;
-  }
+  const size_t qhead = (size_t)(b * p.Hq + hq) * p.Nq;
+  const size_t kvhead = (size_t)(b * p.Hkv + hkv) * p.Nkv;
+  const rsrc_t rq = make_rsrc(static_cast<const uint16_t*>(p.q) + qhead * D, (uint32_t)p.Nq * C::ROWB);
+  const rsrc_t rk = make_rsrc(static_cast<const uint16_t*>(p.k) + kvhead * D, (uint32_t)p.Nkv * C::ROWB);
+  const rsrc_t rv = make_rsrc(static_cast<const uint16_t*>(p.v) + kvhead * D, (uint32_t)p.Nkv * C::ROWB);
 
   const int kv_end = CAUSAL ? min(p.Nkv, q0 + C::BR) : p.Nkv;
   const int n_tiles = (kv_end + C::BC - 1) / C::BC;
+  // Tiles whose every key is allowed for every row of the workgroup.
+  const int n_main = CAUSAL ? min((q0 + 1) / C::BC, p.Nkv / C::BC) : p.Nkv / C::BC;
+
+  // DMA of tile t into ring stage S (= t mod 4).
+  auto issue = [&]<int S>(int t) {
+    const int kv0 = t * C::BC;
+#pragma unroll
+    for (int u = 0; u < C::DPW; ++u) {
+      const int i = wave * C::DPW + u;            // 1 KiB chunk of the stage (wave-uniform)
+      const bool isv = i >= C::CHUNKS / 2;
+      const int ci = isv ? i - C::CHUNKS / 2 : i;
+      const int slot = ci * 64 + lane;            // 16-byte slot within the tile
+      const int row = slot / C::NCH;
+      const int c = (slot % C::NCH) ^ (isv ? swz_v<D>(row) : swz_k<D>(row));
+      lds_t* dst = (isv ? vst.template operator()<S>() : kst.template operator()<S>()) + ci * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? rv : rk, (lds_t*)dst, 16,
+                                               (kv0 + row) * C::ROWB + c * 16, 0, 0, 0);
+    }
+  };
+
+  // Tile t has landed in LDS for every wave; tile t+2 (ring stage S) is issued.
+  auto advance = [&]<int S>(int t) {
+    if (t + 1 < n_tiles) wait_vm_lgkm<C::DPW>();
+    else wait_vm_lgkm<0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (t + 2 < n_tiles) issue.template operator()<S>(t + 2);
+  };
+
+  issue.template operator()<0>(0);
+  if (n_tiles > 1) issue.template operator()<1>(1);
+
+  // Q^T operand, held for the whole loop: lane (l32, half) has row myq, dims
+  // cd*16 + half*8 .. +7.  Rows past N_q read as zeros.  qmode 1 flips both
+  // halves' sign bits (exact negation), qmode 2 zeroes Q.
+  const uint32_t qxor = p.qmode == 1 ? 0x80008000u : 0u;
+  const uint32_t qand = p.qmode == 2 ? 0u : 0xffffffffu;
+  u32x4 qreg[D / 16];
+#pragma unroll
+  for (int cd = 0; cd < D / 16; ++cd) {
+    const u32x4 x = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, (myq * D + cd * 16 + half * 8) * 2, 0, 0));
+    qreg[cd] = (x ^ qxor) & qand;
+  }
+
+  // Per-lane LDS byte offsets of the operand reads.  The swizzles have a
+  // period of 16 rows and act on chunk-index bits that a loop index only
+  // XORs, so one base per operand suffices:
+  //   K, dims cd*16.. of row l32 (+32 kt):   kbase ^ (cd * 32)   (+ kt * 32 rows)
+  //   V^T, columns db*32.., keys as above:   vbase ^ (db * 64)   (+ row offsets)
+  const int kbase = l32 * C::ROWB + ((half ^ (swz_k<D>(l32) & 1)) * 16) + ((swz_k<D>(l32) >> 1) * 32);
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const int vrow = (g16 >> 1) * 4 + (s16 >> 2);
+  const int vbase = vrow * C::ROWB + (swz_v<D>(vrow) >> 2) * 64 + (g16 & 1) * 32 +
+                    ((s16 & 3) >> 1) * 16 + (s16 & 1) * 8;
 
   f32x16 acc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
-  float m_run = -INFINITY;   // running max of scaled scores, log2 units
-  float l_run = 0.f;         // this lane's share of the running sum
+  float m_run = -INFINITY;   // exponent reference (log2 units), shared by both half-waves
+  float l_run = 0.f;         // this lane's part of the row sum, against m_run
 
-  // Global -> register prefetch of one K/V tile.
-  u32x4 kpre[C::KLOADS];
-  u32x4 vpre[4];
-  const int v_dchunk = tid % (D / 8);
-  const int v_kg = tid / (D / 8);
-  const bool v_loader = tid < C::VITEMS;
-
-  auto load_tile = [&](int j) {
-    const int kv0 = j * C::BC;
+  // The lane bases pass through an empty asm in every call so that the
+  // compiler recomputes the few XORs per tile instead of hoisting one address
+  // register per (stage, chunk) pair out of the loop.
+  auto compute_s = [&](const lds_t* st, f32x16 (&s)[2]) {
+    int kb = kbase;
+    asm volatile("" : "+v"(kb));
+    s[0] = f32x16{};
+    s[1] = f32x16{};
 #pragma unroll
-    for (int i = 0; i < C::KLOADS; ++i) {
-      const int c = tid + i * C::NT;
-      const int row = c / (D / 8);
-      const int col = (c % (D / 8)) * 8;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (kv0 + row < p.Nkv) x = *reinterpret_cast<const u32x4*>(Kg + (size_t)(kv0 + row) * D + col);
-      kpre[i] = x;
-    }
-    if (v_loader) {
+    for (int cd = 0; cd < D / 16; ++cd) {
+      const lds_t* a = st + (kb ^ (cd * 32));
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = kv0 + v_kg * 4 + r;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (row < p.Nkv) x = *reinterpret_cast<const u32x4*>(Vg + (size_t)row * D + v_dchunk * 8);
-        vpre[r] = x;
+      for (int kt = 0; kt < 2; ++kt) {
+        const u32x4 x = *(const u32x4 __attribute__((address_space(3)))*)(a + kt * 32 * C::ROWB);
+        s[kt] = M::mma(x, qreg[cd], s[kt]);
       }
     }
   };
 
-  auto store_tile = [&](int buf) {
-    uint16_t* Ks = smem + buf * C::BUF;
-    uint16_t* Vt = Ks + C::KTILE;
+  auto compute_pv = [&](const lds_t* st, const u32x4 (&pk)[2][2]) {
+    int vb = vbase;
+    asm volatile("" : "+v"(vb));
 #pragma unroll
-    for (int i = 0; i < C::KLOADS; ++i) {
-      const int c = tid + i * C::NT;
-      const int row = c / (D / 8);
-      const int col = (c % (D / 8)) * 8;
-      *reinterpret_cast<u32x4*>(Ks + row * C::KP + col) = kpre[i];
-    }
-    if (v_loader) {
-      // vpre[r][e] holds dims (2e, 2e+1) of key r; emit, per dim, the four
-      // keys as one 8-byte V^T store.
-      const int pos = vt_pos(v_kg);
+    for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int cc = 0; cc < 2; ++cc) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const uint32_t sel = s ? 0x07060302u : 0x05040100u;
-          u32x2 w;
-          w[0] = __builtin_amdgcn_perm(vpre[1][e], vpre[0][e], sel);
-          w[1] = __builtin_amdgcn_perm(vpre[3][e], vpre[2][e], sel);
-          const int d = v_dchunk * 8 + 2 * e + s;
-          *reinterpret_cast<u32x2*>(Vt + d * C::VP + pos) = w;
+        for (int db = 0; db < D / 32; ++db) {
+          const lds_t* a0 = st + (vb ^ (db * 64)) + (kt * 32 + cc * 16) * C::ROWB;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)a0);
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(a0 + 8 * C::ROWB));
+          const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+          const u32x4 x = {l2[0], l2[1], h2[0], h2[1]};
+          acc[db] = M::mma(x, pk[kt][cc], acc[db]);
         }
       }
     }
   };
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  // New exponent reference from a tile of raw scores; returns the factor that
+  // moves earlier sums to it (1 when the reference stays, 0 the first time).
+  auto new_reference = [&](const f32x16 (&s)[2]) -> float {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+    mx = pair_max(mx);
+    const float mc = mx * p.sl2;
+    const float m_new = (mc > m_run + kLazy) ? mc : m_run;
+    const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+    m_run = m_new;
+    return alpha;
+  };
 
-  for (int j = 0; j < n_tiles; ++j) {
-    const int kv0 = j * C::BC;
-    if (j + 1 < n_tiles) load_tile(j + 1);
+  auto rescale = [&](float alpha) {
+    l_run *= alpha;
+    if (wave_any(alpha != 1.f)) {
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
+    }
+  };
 
-    const uint16_t* Ks = smem + (j & 1) * C::BUF;
-    const uint16_t* Vt = Ks + C::KTILE;
-    // A wave skips tiles that hold no allowed key for any of its rows.
+  // P = exp2(s * sl2 - ref), rounded to T and packed as the B operand of P*V;
+  // the row sum accumulates the rounded values in fp32.
+  auto exponentiate = [&](const f32x16 (&s)[2], u32x4 (&pk)[2][2]) {
+    const float mu = (m_run == -INFINITY) ? 0.f : m_run;
+    float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float e0 = fast_exp2(fmaf(s[kt][cc * 8 + 2 * w], p.sl2, -mu));
+          const float e1 = fast_exp2(fmaf(s[kt][cc * 8 + 2 * w + 1], p.sl2, -mu));
+          const uint32_t pr = M::pack(e0, e1);
+          pk[kt][cc][w] = pr;
+          if (w & 1) ls1 = M::sum2(pr, ls1);
+          else ls0 = M::sum2(pr, ls0);
+        }
+      }
+    }
+    l_run += ls0 + ls1;
+  };
+
+  f32x16 s_cur[2];
+  u32x4 pk[2][2];
+
+  // Steady iteration j (j % 4 == R): tile j+1 is unmasked too.
+  auto steady = [&]<int R>(int j) {
+    advance.template operator()<(R + 3) & 3>(j + 1);
+    f32x16 s_next[2];
+    exponentiate(s_cur, pk);                                      // VALU on S(j) ...
+    compute_s(kst.template operator()<(R + 1) & 3>(), s_next);    // ... under MFMA S(j+1)
+    compute_pv(vst.template operator()<R>(), pk);                 // MFMA O += V(j) P(j) ...
+    const float alpha = new_reference(s_next);                    // ... under the scan of S(j+1)
+    rescale(alpha);
+    s_cur[0] = s_next[0];
+    s_cur[1] = s_next[1];
+  };
+  // Last unmasked iteration j = n_main - 1 (j % 4 == R).
+  auto last_main = [&]<int R>(int j) {
+    if (j + 1 < n_tiles) advance.template operator()<(R + 3) & 3>(j + 1);
+    exponentiate(s_cur, pk);
+    compute_pv(vst.template operator()<R>(), pk);
+  };
+  // A tile that needs a mask (ragged tail; causal diagonal), t % 4 == R.
+  auto masked = [&]<int R>(int t) {
+    if (t > n_main || n_main == 0) advance.template operator()<(R + 2) & 3>(t);
+    const int kv0 = t * C::BC;
     const bool active = (qw0 < p.Nq) && (!CAUSAL || kv0 <= qw0 + 31);
     if (active) {
-      f32x16 s[C::BC / 32];
+      f32x16 s[2];
+      compute_s(kst.template operator()<R>(), s);
 #pragma unroll
-      for (int kt = 0; kt < C::BC / 32; ++kt) s[kt] = f32x16{};
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-#pragma unroll
-        for (int kt = 0; kt < C::BC / 32; ++kt) {
-          const u32x4 a =
-              *reinterpret_cast<const u32x4*>(Ks + (kt * 32 + l32) * C::KP + c * 16 + half * 8);
-          s[kt] = M::mma(a, qreg[c], s[kt]);
-        }
-      }
-
-      // s[kt][r] is the raw score of query myq and key
-      // kv0 + kt*32 + (r/4)*8 + half*4 + r%4.
-      const bool need_mask = (kv0 + C::BC > p.Nkv) || (CAUSAL && kv0 + C::BC - 1 > qw0);
-      if (need_mask) {
-#pragma unroll
-        for (int kt = 0; kt < C::BC / 32; ++kt) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + kt * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-            const bool masked = (key >= p.Nkv) || (CAUSAL && key > myq);
-            if (masked) s[kt][r] = -INFINITY;
-          }
-        }
-      }
-
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < C::BC / 32; ++kt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-      }
-      mx = fmaxf(mx, xor32(mx));
-      const float m_new = fmaxf(m_run, mx * p.sl2);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);   // 0 while m_run is -inf
-      float ls = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < C::BC / 32; ++kt) {
+      for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float e = fast_exp2(fmaf(s[kt][r], p.sl2, -m_use));
-          s[kt][r] = e;
-          ls += e;
+          const int key = kv0 + kt * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+          if ((key >= p.Nkv) || (CAUSAL && key > myq)) s[kt][r] = -INFINITY;
         }
       }
-      l_run = fmaf(l_run, alpha, ls);
-      m_run = m_new;
-      if (wave_any(alpha != 1.f)) {
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
-      }
+      rescale(new_reference(s));
+      exponentiate(s, pk);
+      compute_pv(vst.template operator()<R>(), pk);
+    }
+  };
 
-#pragma unroll
-      for (int kt = 0; kt < C::BC / 32; ++kt) {
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          u32x4 pk;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) pk[w] = M::pack(s[kt][cc * 8 + 2 * w], s[kt][cc * 8 + 2 * w + 1]);
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            const u32x4 a = *reinterpret_cast<const u32x4*>(
-                Vt + (db * 32 + l32) * C::VP + kt * 32 + cc * 16 + half * 8);
-            acc[db] = M::mma(a, pk, acc[db]);
-          }
-        }
+  if (n_main > 0) {
+    advance.template operator()<2>(0);
+    compute_s(kst.template operator()<0>(), s_cur);
+    rescale(new_reference(s_cur));
+    int j = 0;
+    for (; j + 4 < n_main; j += 4) {
+      steady.template operator()<0>(j);
+      steady.template operator()<1>(j + 1);
+      steady.template operator()<2>(j + 2);
+      steady.template operator()<3>(j + 3);
+    }
+    for (; j + 1 < n_main; ++j) {
+      switch (j & 3) {
+        case 0: steady.template operator()<0>(j); break;
+        case 1: steady.template operator()<1>(j); break;
+        case 2: steady.template operator()<2>(j); break;
+        default: steady.template operator()<3>(j); break;
       }
     }
-
-    if (j + 1 < n_tiles) store_tile((j + 1) & 1);
-    __syncthreads();
+    switch (j & 3) {
+      case 0: last_main.template operator()<0>(j); break;
+      case 1: last_main.template operator()<1>(j); break;
+      case 2: last_main.template operator()<2>(j); break;
+      default: last_main.template operator()<3>(j); break;
+    }
+  }
+  for (int t = n_main; t < n_tiles; ++t) {
+    switch (t & 3) {
+      case 0: masked.template operator()<0>(t); break;
+      case 1: masked.template operator()<1>(t); break;
+      case 2: masked.template operator()<2>(t); break;
+      default: masked.template operator()<3>(t); break;
+    }
   }
 
   // Epilogue: combine the half-waves' sums, divide once, write O and lse.
-  const float l_tot = l_run + xor32(l_run);
-  if (myq < p.Nq) {
-    const float inv = 1.f / l_tot;
-    uint16_t* Og = static_cast<uint16_t*>(p.o) + ((size_t)(b * p.Hq + hq) * p.Nq + myq) * D;
+  // Rows past N_q fall outside the buffer ranges and are dropped.
+  const float l_tot = pair_sum(l_run);
+  const float inv = 1.f / l_tot;
+  const rsrc_t ro = make_rsrc(static_cast<uint16_t*>(p.o) + qhead * D, (uint32_t)p.Nq * C::ROWB);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
+  for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 w;
-        w[0] = M::pack(acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv);
-        w[1] = M::pack(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
-        *reinterpret_cast<u32x2*>(Og + db * 32 + g * 8 + half * 4) = w;
-      }
+    for (int g = 0; g < 4; ++g) {
+      u32x2 w;
+      w[0] = M::pack(acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv);
+      w[1] = M::pack(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, w), ro,
+                                            (myq * D + db * 32 + g * 8 + half * 4) * 2, 0, 0);
     }
-    if (half == 0) p.lse[(size_t)(b * p.Hq + hq) * p.Nq + myq] = (m_run + fast_log2(l_tot)) * kLn2;
   }
+  if (half == 0) {
+    const rsrc_t rl = make_rsrc(p.lse + qhead, (uint32_t)p.Nq * 4u);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((m_run + fast_log2(l_tot)) * kLn2), rl,
+                                          myq * 4, 0, 0);
+  }
+}
+
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(Cfg16<D>::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_fwd_mfma16(Params p) {
+  attn_fwd_mfma16_body<T, D, CAUSAL>(p);
 }
 
 // ------------------------------------------------------------- fp32 path
@@ -579,8 +742,11 @@ int check_dims(int B, int Hq, int Hkv, int N_q, int N_kv, int d, int dtype, long
   const long long tiles = ((long long)N_q + g.rows_per_block - 1) / g.rows_per_block;
   const long long nb = (long long)B * Hq * tiles;
   if (nb > 0x7fffffffLL) return FA_ERR_BAD_DIM;
-  // Row offsets are 64-bit, but (b * H + h) and row indices are 32-bit ints.
+  // Head offsets are 64-bit, but (b * H + h), row indices and the byte
+  // offsets inside one head (buffer descriptors, 32-bit) are not.
   if ((long long)B * Hq > 0x7fffffffLL || (long long)B * Hkv > 0x7fffffffLL) return FA_ERR_BAD_DIM;
+  const long long nmax = (N_q > N_kv ? N_q : N_kv) + 256LL;
+  if (nmax * d * (long long)elem_size(dtype) > 0x7fffffffLL) return FA_ERR_BAD_DIM;
   if (blocks) *blocks = nb;
   return FA_OK;
 }
@@ -617,10 +783,8 @@ int set_lds_limit(Kernel kern, int lds_bytes) {
 
 template <typename T, int D, bool CAUSAL>
 int run16(const Params& p, long long blocks, hipStream_t stream) {
-  using C = Cfg16<D>;
-  static const int attr = set_lds_limit(attn_fwd_mfma16<T, D, CAUSAL>, C::LDS_BYTES);
-  if (attr != FA_OK) return attr;
-  return launch(attn_fwd_mfma16<T, D, CAUSAL>, C::LDS_BYTES, p, blocks, C::NT, stream);
+  // All LDS of this kernel is static (one object per ring stage).
+  return launch(attn_fwd_mfma16<T, D, CAUSAL>, 0, p, blocks, Cfg16<D>::NT, stream);
 }
 
 template <int D, bool CAUSAL>

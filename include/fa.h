@@ -55,7 +55,7 @@ extern "C" {
 typedef enum fa_status {
     FA_OK = 0,
     FA_ERR_NULL_PTR = 1,   /* a required pointer is NULL                        */
-    FA_ERR_BAD_DIM = 2,    /* B, Hq, Hkv, N_q or N_kv < 1, or the grid too large */
+    FA_ERR_BAD_DIM = 2,    /* a dimension < 1, or too large (see fa_fwd)         */
     FA_ERR_HEAD_GROUP = 3, /* Hq is not a multiple of Hkv                        */
     FA_ERR_HEAD_DIM = 4,   /* d is not 64 or 128                                 */
     FA_ERR_DTYPE = 5,      /* dtype is not one of fa_dtype                       */
@@ -75,6 +75,9 @@ typedef enum fa_dtype {
  * Exact attention forward, launched on the null (default) stream.
  * scale is applied as given (callers usually pass 1/sqrt(d)); any finite
  * value is accepted, including 0 and negative values.
+ * Size limits (FA_ERR_BAD_DIM beyond them): one head of q or k/v, plus 256
+ * rows, must stay below 2 GiB ((max(N_q, N_kv) + 256) * d * elem_size <
+ * 2^31), B*Hq and B*Hkv below 2^31, and the grid below 2^31 workgroups.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int Hq, int Hkv, int N_q, int N_kv, int d,

@@ -137,3 +137,11 @@ def test_python_wrapper_rejects_cpu_tensors(lib):
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(fa.FAError):
         fa.attention(q, q, q)
+
+
+def test_sequence_length_limit(lib):
+    # one head of k/v (+256 rows) must stay below 2 GiB
+    n_ok = (1 << 31) // (128 * 2) - 257
+    far = dict(q=1 << 40, k=2 << 40, v=3 << 40, o=4 << 40, lse=5 << 40)
+    assert check(N_q=16, N_kv=n_ok, B=1, Hq=1, Hkv=1, **far) == fa.FA_OK
+    assert check(N_q=16, N_kv=n_ok + 2, B=1, Hq=1, Hkv=1, **far) == fa.FA_ERR_BAD_DIM
