@@ -1,16 +1,16 @@
 // Exact tiled attention forward for gfx950 (MI355X): kernels and C ABI.
 //
 // One workgroup owns BR consecutive query rows of one (batch, query head).
-// It keeps, per row, a running maximum m, a running exponential sum l and an
-// fp32 output accumulator in registers, streams the key/value sequence in
-// tiles of BC rows through double-buffered LDS, and after the last tile
-// divides by l once and writes O and lse.  This is the recurrence of the
-// course page "FlashAttention: IO-aware attention kernel" (section 3.2: new
-// max, rescale old sum and accumulator by exp(m_old - m_new), add the tile's
-// exponentials) inside the query-tile-outer / key-tile-inner loop of its
-// sections 2 and 3.3.  The omica exam notes (section 2.3, block merge rule)
-// state the same update for whole tiles.  Scores and probabilities exist only
-// in registers; nothing of size N_q x N_kv touches memory.
+// It keeps, per row, an exponent reference m, a running exponential sum l and
+// an fp32 output accumulator in registers, streams the key/value sequence in
+// tiles through LDS, and after the last tile divides by l once and writes O
+// and lse.  This is the recurrence of the course page "FlashAttention:
+// IO-aware attention kernel" (section 3.2: new max, rescale the old sum and
+// accumulator by exp(m_old - m_new), add the tile's exponentials) inside the
+// query-tile-outer / key-tile-inner loop of its sections 2 and 3.3.  The
+// omica exam notes (section 2.3, block merge rule) state the same update for
+// whole tiles.  Scores and probabilities exist only in registers; nothing of
+// size N_q x N_kv touches memory.
 //
 // Matrix-core mapping (wave64, 32 query rows per wave):
 //   S^T = K Q^T   v_mfma_f32_32x32x16_{bf16,f16}: A = K rows from LDS, B = Q^T
@@ -20,12 +20,12 @@
 //                 for one exchange between the two half-waves.
 //   O^T += V^T P^T  same instruction: B = P^T straight from the S^T
 //                 accumulator (rounded to the input type), A = V^T read from
-//                 an LDS copy of V that is stored transposed, with keys
-//                 permuted inside each 16-key group so that one 16-byte read
-//                 gives a lane its 8 keys in the order the accumulator holds
-//                 them.  The output accumulator also has one query per lane,
+//                 row-major V in LDS by ds_read_b64_tr_b16, which hands each
+//                 lane 4 keys of one head-dimension column; the key order of
+//                 the accumulator is matched by the choice of rows each lane
+//                 reads.  The output accumulator also has one query per lane,
 //                 so the rescale factor and the final 1/l are lane-local.
-// The fp32 variant uses v_mfma_f32_32x32x2_f32 with the same skeleton.
+// The fp32 variant uses v_mfma_f32_32x32x2_f32 with a simpler skeleton.
 
 #include <hip/hip_runtime.h>
 
@@ -197,10 +197,13 @@ struct Mma16<_Float16> {
 
 template <int D>
 struct Cfg16 {
+  static constexpr int QH = 1;                  // 32-row query halves per wave
   static constexpr int NW = 8;                  // waves per workgroup
   static constexpr int NT = 64 * NW;            // threads per workgroup
-  static constexpr int BR = 32 * NW;            // query rows per workgroup
+  static constexpr int BR = 32 * QH * NW;       // query rows per workgroup
   static constexpr int BC = 64;                 // keys per K/V tile
+  static constexpr int KT = BC / 32;            // 32-key blocks per tile
+  static constexpr int WAVES_PER_EU = QH == 1 ? 2 : 1;
   static constexpr int STAGES = 4;              // LDS ring depth (tiles)
   static constexpr int ROWB = D * 2;            // bytes per K/V row
   static constexpr int NCH = D / 8;             // 16-byte chunks per row
@@ -229,6 +232,8 @@ __device__ __forceinline__ int swz_v(int row) {
 template <typename T, int D, bool CAUSAL>
 __device__ __forceinline__ void attn_fwd_mfma16_body(const Params& p) {
   using C = Cfg16<D>;
+  constexpr int KT = C::KT;
+  constexpr int QH = C::QH;
   using M = Mma16<T>;
   // One LDS object per ring stage and operand: with compile-time stage
   // indices the compiler can tell a read of one stage from a DMA into another
@@ -265,8 +270,9 @@ __device__ __forceinline__ void attn_fwd_mfma16_body(const Params& p) {
   map_block(p, CAUSAL, b, hq, qt);
   const int hkv = hq / p.group;
   const int q0 = qt * C::BR;
-  const int qw0 = q0 + wave * 32;   // first query row of this wave
-  const int myq = qw0 + l32;        // query row whose O column and statistics this lane holds
+  const int qw0 = q0 + wave * 32 * QH;   // first query row of this wave
+  // Query half h of the wave holds rows qw0 + 32h .. +31; lane l32 of it
+  // holds row qw0 + 32h + l32 (its O column and its row statistics).
 
   const size_t qhead = (size_t)(b * p.Hq + hq) * p.Nq;
   const size_t kvhead = (size_t)(b * p.Hkv + hkv) * p.Nkv;
@@ -313,12 +319,16 @@ __device__ __forceinline__ void attn_fwd_mfma16_body(const Params& p) {
   // halves' sign bits (exact negation), qmode 2 zeroes Q.
   const uint32_t qxor = p.qmode == 1 ? 0x80008000u : 0u;
   const uint32_t qand = p.qmode == 2 ? 0u : 0xffffffffu;
-  u32x4 qreg[D / 16];
+  u32x4 qreg[QH][D / 16];
 #pragma unroll
-  for (int cd = 0; cd < D / 16; ++cd) {
-    const u32x4 x = __builtin_bit_cast(
-        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, (myq * D + cd * 16 + half * 8) * 2, 0, 0));
-    qreg[cd] = (x ^ qxor) & qand;
+  for (int h = 0; h < QH; ++h) {
+#pragma unroll
+    for (int cd = 0; cd < D / 16; ++cd) {
+      const int row = qw0 + 32 * h + l32;
+      const u32x4 x = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, (row * D + cd * 16 + half * 8) * 2, 0, 0));
+      qreg[h][cd] = (x ^ qxor) & qand;
+    }
   }
 
   // Per-lane LDS byte offsets of the operand reads.  The swizzles have a
@@ -332,36 +342,46 @@ __device__ __forceinline__ void attn_fwd_mfma16_body(const Params& p) {
   const int vbase = vrow * C::ROWB + (swz_v<D>(vrow) >> 2) * 64 + (g16 & 1) * 32 +
                     ((s16 & 3) >> 1) * 16 + (s16 & 1) * 8;
 
-  f32x16 acc[D / 32];
+  f32x16 acc[QH][D / 32];
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
-  float m_run = -INFINITY;   // exponent reference (log2 units), shared by both half-waves
-  float l_run = 0.f;         // this lane's part of the row sum, against m_run
+  for (int h = 0; h < QH; ++h)
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) acc[h][i] = f32x16{};
+  float m_run[QH];   // exponent reference (log2 units), shared by both half-waves
+  float l_run[QH];   // this lane's part of the row sum, against m_run
+#pragma unroll
+  for (int h = 0; h < QH; ++h) {
+    m_run[h] = -INFINITY;
+    l_run[h] = 0.f;
+  }
 
   // The lane bases pass through an empty asm in every call so that the
   // compiler recomputes the few XORs per tile instead of hoisting one address
   // register per (stage, chunk) pair out of the loop.
-  auto compute_s = [&](const lds_t* st, f32x16 (&s)[2]) {
+  auto compute_s = [&](const lds_t* st, f32x16 (&s)[QH][KT]) {
     int kb = kbase;
     asm volatile("" : "+v"(kb));
-    s[0] = f32x16{};
-    s[1] = f32x16{};
+#pragma unroll
+    for (int h = 0; h < QH; ++h)
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) s[h][kt] = f32x16{};
 #pragma unroll
     for (int cd = 0; cd < D / 16; ++cd) {
       const lds_t* a = st + (kb ^ (cd * 32));
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+      for (int kt = 0; kt < KT; ++kt) {
         const u32x4 x = *(const u32x4 __attribute__((address_space(3)))*)(a + kt * 32 * C::ROWB);
-        s[kt] = M::mma(x, qreg[cd], s[kt]);
+#pragma unroll
+        for (int h = 0; h < QH; ++h) s[h][kt] = M::mma(x, qreg[h][cd], s[h][kt]);
       }
     }
   };
 
-  auto compute_pv = [&](const lds_t* st, const u32x4 (&pk)[2][2]) {
+  auto compute_pv = [&](const lds_t* st, const u32x4 (&pk)[QH][KT][2]) {
     int vb = vbase;
     asm volatile("" : "+v"(vb));
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
 #pragma unroll
@@ -371,43 +391,52 @@ __device__ __forceinline__ void attn_fwd_mfma16_body(const Params& p) {
           const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(a0 + 8 * C::ROWB));
           const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
           const u32x4 x = {l2[0], l2[1], h2[0], h2[1]};
-          acc[db] = M::mma(x, pk[kt][cc], acc[db]);
+#pragma unroll
+          for (int h = 0; h < QH; ++h) acc[h][db] = M::mma(x, pk[h][kt][cc], acc[h][db]);
         }
       }
     }
   };
 
-  // New exponent reference from a tile of raw scores; returns the factor that
-  // moves earlier sums to it (1 when the reference stays, 0 the first time).
-  auto new_reference = [&](const f32x16 (&s)[2]) -> float {
+  // New exponent reference of query half h from a tile of raw scores;
+  // returns the factor that moves earlier sums to it (1 when the reference
+  // stays, 0 the first time).
+  auto new_reference = [&](const f32x16 (&s)[KT], int h) -> float {
     float mx = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
     mx = pair_max(mx);
     const float mc = mx * p.sl2;
-    const float m_new = (mc > m_run + kLazy) ? mc : m_run;
-    const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
-    m_run = m_new;
+    const float m_new = (mc > m_run[h] + kLazy) ? mc : m_run[h];
+    const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run[h] - m_new);
+    m_run[h] = m_new;
     return alpha;
   };
 
-  auto rescale = [&](float alpha) {
-    l_run *= alpha;
-    if (wave_any(alpha != 1.f)) {
+  auto rescale = [&](const float (&alpha)[QH]) {
+    bool any = false;
 #pragma unroll
-      for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
+    for (int h = 0; h < QH; ++h) {
+      l_run[h] *= alpha[h];
+      any = any || (alpha[h] != 1.f);
+    }
+    if (wave_any(any)) {
+#pragma unroll
+      for (int h = 0; h < QH; ++h)
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) acc[h][i] *= alpha[h];
     }
   };
 
   // P = exp2(s * sl2 - ref), rounded to T and packed as the B operand of P*V;
   // the row sum accumulates the rounded values in fp32.
-  auto exponentiate = [&](const f32x16 (&s)[2], u32x4 (&pk)[2][2]) {
-    const float mu = (m_run == -INFINITY) ? 0.f : m_run;
+  auto exponentiate = [&](const f32x16 (&s)[KT], u32x4 (&pk)[KT][2], int h) {
+    const float mu = (m_run[h] == -INFINITY) ? 0.f : m_run[h];
     float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
 #pragma unroll
@@ -421,48 +450,62 @@ __device__ __forceinline__ void attn_fwd_mfma16_body(const Params& p) {
         }
       }
     }
-    l_run += ls0 + ls1;
+    l_run[h] += ls0 + ls1;
   };
 
-  f32x16 s_cur[2];
-  u32x4 pk[2][2];
+  f32x16 s_cur[QH][KT];
+  u32x4 pk[QH][KT][2];
 
   // Steady iteration j (j % 4 == R): tile j+1 is unmasked too.
   auto steady = [&]<int R>(int j) {
     advance.template operator()<(R + 3) & 3>(j + 1);
-    f32x16 s_next[2];
-    exponentiate(s_cur, pk);                                      // VALU on S(j) ...
-    compute_s(kst.template operator()<(R + 1) & 3>(), s_next);    // ... under MFMA S(j+1)
-    compute_pv(vst.template operator()<R>(), pk);                 // MFMA O += V(j) P(j) ...
-    const float alpha = new_reference(s_next);                    // ... under the scan of S(j+1)
+    f32x16 s_next[QH][KT];
+#pragma unroll
+    for (int h = 0; h < QH; ++h) exponentiate(s_cur[h], pk[h], h);   // VALU on S(j) ...
+    compute_s(kst.template operator()<(R + 1) & 3>(), s_next);       // ... under MFMA S(j+1)
+    compute_pv(vst.template operator()<R>(), pk);                    // MFMA O += V(j) P(j) ...
+    float alpha[QH];
+#pragma unroll
+    for (int h = 0; h < QH; ++h) alpha[h] = new_reference(s_next[h], h);   // ... under the scan of S(j+1)
     rescale(alpha);
-    s_cur[0] = s_next[0];
-    s_cur[1] = s_next[1];
+#pragma unroll
+    for (int h = 0; h < QH; ++h)
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) s_cur[h][kt] = s_next[h][kt];
   };
   // Last unmasked iteration j = n_main - 1 (j % 4 == R).
   auto last_main = [&]<int R>(int j) {
     if (j + 1 < n_tiles) advance.template operator()<(R + 3) & 3>(j + 1);
-    exponentiate(s_cur, pk);
+#pragma unroll
+    for (int h = 0; h < QH; ++h) exponentiate(s_cur[h], pk[h], h);
     compute_pv(vst.template operator()<R>(), pk);
   };
   // A tile that needs a mask (ragged tail; causal diagonal), t % 4 == R.
+  // Rows with no allowed key in it get p = 0 exactly.
   auto masked = [&]<int R>(int t) {
     if (t > n_main || n_main == 0) advance.template operator()<(R + 2) & 3>(t);
     const int kv0 = t * C::BC;
-    const bool active = (qw0 < p.Nq) && (!CAUSAL || kv0 <= qw0 + 31);
+    const bool active = (qw0 < p.Nq) && (!CAUSAL || kv0 <= qw0 + 32 * QH - 1);
     if (active) {
-      f32x16 s[2];
+      f32x16 s[QH][KT];
       compute_s(kst.template operator()<R>(), s);
+      float alpha[QH];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+      for (int h = 0; h < QH; ++h) {
+        const int myq = qw0 + 32 * h + l32;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + kt * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-          if ((key >= p.Nkv) || (CAUSAL && key > myq)) s[kt][r] = -INFINITY;
+        for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kv0 + kt * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+            if ((key >= p.Nkv) || (CAUSAL && key > myq)) s[h][kt][r] = -INFINITY;
+          }
         }
+        alpha[h] = new_reference(s[h], h);
       }
-      rescale(new_reference(s));
-      exponentiate(s, pk);
+      rescale(alpha);
+#pragma unroll
+      for (int h = 0; h < QH; ++h) exponentiate(s[h], pk[h], h);
       compute_pv(vst.template operator()<R>(), pk);
     }
   };
@@ -470,7 +513,10 @@ __device__ __forceinline__ void attn_fwd_mfma16_body(const Params& p) {
   if (n_main > 0) {
     advance.template operator()<2>(0);
     compute_s(kst.template operator()<0>(), s_cur);
-    rescale(new_reference(s_cur));
+    float alpha[QH];
+#pragma unroll
+    for (int h = 0; h < QH; ++h) alpha[h] = new_reference(s_cur[h], h);
+    rescale(alpha);
     int j = 0;
     for (; j + 4 < n_main; j += 4) {
       steady.template operator()<0>(j);
@@ -504,29 +550,38 @@ __device__ __forceinline__ void attn_fwd_mfma16_body(const Params& p) {
 
   // Epilogue: combine the half-waves' sums, divide once, write O and lse.
   // Rows past N_q fall outside the buffer ranges and are dropped.
-  const float l_tot = pair_sum(l_run);
-  const float inv = 1.f / l_tot;
   const rsrc_t ro = make_rsrc(static_cast<uint16_t*>(p.o) + qhead * D, (uint32_t)p.Nq * C::ROWB);
+  const rsrc_t rl = make_rsrc(p.lse + qhead, (uint32_t)p.Nq * 4u);
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
+  for (int h = 0; h < QH; ++h) {
+    const int myq = qw0 + 32 * h + l32;
+    const float l_tot = pair_sum(l_run[h]);
+    const float inv = 1.f / l_tot;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      u32x2 w;
-      w[0] = M::pack(acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv);
-      w[1] = M::pack(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
-      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, w), ro,
-                                            (myq * D + db * 32 + g * 8 + half * 4) * 2, 0, 0);
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 w;
+        w[0] = M::pack(acc[h][db][4 * g] * inv, acc[h][db][4 * g + 1] * inv);
+        w[1] = M::pack(acc[h][db][4 * g + 2] * inv, acc[h][db][4 * g + 3] * inv);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, w), ro,
+                                              (myq * D + db * 32 + g * 8 + half * 4) * 2, 0, 0);
+      }
     }
-  }
-  if (half == 0) {
-    const rsrc_t rl = make_rsrc(p.lse + qhead, (uint32_t)p.Nq * 4u);
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((m_run + fast_log2(l_tot)) * kLn2), rl,
-                                          myq * 4, 0, 0);
+    if (half == 0)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((m_run[h] + fast_log2(l_tot)) * kLn2), rl,
+                                            myq * 4, 0, 0);
   }
 }
 
+template <int D>
+constexpr int kNT16 = Cfg16<D>::NT;
+template <int D>
+constexpr int kWavesPerEU16 = Cfg16<D>::WAVES_PER_EU;
+
 template <typename T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(Cfg16<D>::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(kNT16<D>)
+    __attribute__((amdgpu_waves_per_eu(kWavesPerEU16<D>, kWavesPerEU16<D>)))
 attn_fwd_mfma16(Params p) {
   attn_fwd_mfma16_body<T, D, CAUSAL>(p);
 }
