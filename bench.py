@@ -42,6 +42,8 @@ def parse():
                     help="approximate CPU time budget of the oracle baseline (0 disables)")
     ap.add_argument("--check-rows", type=int, default=64,
                     help="rows per sampled head checked against the oracle after timing")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the context measurements (library GEMM and zero-input run)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of attention, run 3 plain device-to-device copies of this "
                          "many MiB (calibrates the HBM byte counters of a profiler)")
@@ -83,6 +85,56 @@ def measured_traffic(workload_name: str):
     if fields.get("traffic_kernel_source_sha256") != sha:
         return None
     return float(fields["traffic_bytes_per_launch"])
+
+
+def power_context(fa, w, qd, kd, vd, o, lse, scale, stream, dcode):
+    """Context for the roofline fraction, measured on the same GPU in the same process.
+
+    MI355X lowers its clock under sustained dense MFMA load on random operands, so the
+    published peak is not reachable with such data.  Two reference points show by how
+    much: a library bf16 GEMM (torch.mm, 8192^3, the same N(0,1) values as the workload)
+    and the attention kernel itself on all-zero inputs (same instructions, little
+    switching activity), each next to its own zero/random counterpart.
+    """
+    import torch
+
+    def timed(fn, n):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    g = torch.Generator(device="cpu").manual_seed(7)
+    a = torch.randn(8192, 8192, generator=g).to(device=qd.device, dtype=torch.bfloat16)
+    b = torch.randn(8192, 8192, generator=g).to(device=qd.device, dtype=torch.bfloat16)
+    c = torch.empty_like(a)
+    gemm_flops = 2.0 * 8192 ** 3
+    with torch.cuda.stream(stream):
+        ms_rand = timed(lambda: torch.mm(a, b, out=c), 40)
+        a.zero_()
+        b.zero_()
+        ms_zero = timed(lambda: torch.mm(a, b, out=c), 40)
+    del a, b, c
+    zq, zk, zv = torch.zeros_like(qd), torch.zeros_like(kd), torch.zeros_like(vd)
+
+    def attn_zero():
+        st = fa.fa_fwd_stream(zq, zk, zv, o, lse, w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, scale,
+                              w.causal, dcode, stream)
+        if st != 0:
+            raise RuntimeError(fa.fa_status_string(st))
+    ms_attn_zero = timed(attn_zero, 20)
+    return {
+        "library_gemm_bf16_8192_random_tflops": round(gemm_flops / ms_rand / 1e9, 1),
+        "library_gemm_bf16_8192_zero_tflops": round(gemm_flops / ms_zero / 1e9, 1),
+        "this_kernel_zero_inputs_tflops": round(w.flops() / ms_attn_zero / 1e9, 1),
+        "note": "same GPU, same process; random operands draw more power and lower the clock",
+    }
 
 
 def cpu_baseline(w, q, k, v, budget_s):
@@ -153,17 +205,20 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    # One event before every launch and one after the last: the launches stay
+    # back to back, and each launch's duration is the gap between its events.
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        evs[i].record(stream)
         step()
-    ev1.record(stream)
+    evs[-1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    per_launch = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    kernel_ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    median_ms = per_launch[len(per_launch) // 2]
     wall_ms = wall * 1e3 / args.steps
 
     flops = w.flops()
@@ -196,6 +251,10 @@ def main():
                  "max_abs_err_lse": max(e[1] for e in errs),
                  "rows_checked": int(len(rows)) * len(errs)}
 
+    context = None
+    if not args.no_context and w.dtype != "f32":
+        context = power_context(fa, w, qd, kd, vd, o, lse, scale, stream, dcode)
+
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(w, q, k, v, args.cpu_seconds)
@@ -220,7 +279,10 @@ def main():
         "pct_of_peak": round(100 * value / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": measured_traffic(w.name), "kernel_ms": round(kernel_ms, 5)},
+                     "traffic": measured_traffic(w.name), "kernel_ms": round(kernel_ms, 5),
+                     "kernel_ms_median": round(median_ms, 5),
+                     "kernel_ms_min": round(per_launch[0], 5)},
+        "context": context,
         "cpu_baseline": None if cpu is None else {k_: cpu[k_] for k_ in
                                                   ("value", "unit", "cores", "kind", "sample")},
         "parity_sample": check,
