@@ -31,6 +31,8 @@ FA_ERR_SCALE = 6
 FA_ERR_ALIGN = 7
 FA_ERR_HIP = 8
 FA_ERR_ALIAS = 9
+FA_ERR_WORKSPACE = 10
+FA_SPLITKV_MAX_SPLITS = 256
 
 FA_F32 = 0
 FA_F16 = 1
@@ -71,6 +73,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_launch_info.argtypes = [_I] * 8 + [ctypes.POINTER(_I)] * 3 + \
         [ctypes.POINTER(ctypes.c_longlong), ctypes.POINTER(_I)]
     lib.fa_launch_info.restype = _I
+    lib.fa_splitkv_workspace_bytes.argtypes = [_I] * 5
+    lib.fa_splitkv_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_splitkv_default_splits.argtypes = [_I] * 7
+    lib.fa_splitkv_default_splits.restype = _I
+    lib.fa_fwd_splitkv.argtypes = list(_FWD_ARGS) + [_I, _VP, ctypes.c_size_t, _VP]
+    lib.fa_fwd_splitkv.restype = _I
     _lib = lib
     return lib
 
@@ -123,6 +131,22 @@ def fa_launch_info(B, Hq, Hkv, N_q, N_kv, d, causal, dtype):
                     blocks=nb.value, lds_bytes=lds.value)
 
 
+def fa_splitkv_workspace_bytes(B, Hq, N_q, d, num_splits) -> int:
+    return load_library().fa_splitkv_workspace_bytes(B, Hq, N_q, d, num_splits)
+
+
+def fa_splitkv_default_splits(B, Hq, Hkv, N_q, N_kv, d, dtype) -> int:
+    return load_library().fa_splitkv_default_splits(B, Hq, Hkv, N_q, N_kv, d, dtype)
+
+
+def fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, N_q, N_kv, d, scale, causal, dtype, num_splits,
+                   workspace, workspace_bytes, stream) -> int:
+    s = stream if (stream is None or isinstance(stream, int)) else stream.cuda_stream
+    return load_library().fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq,
+                                         Hkv, N_q, N_kv, d, scale, int(causal), dtype,
+                                         num_splits, _ptr(workspace), workspace_bytes, s)
+
+
 def dtype_code(torch_dtype) -> int:
     import torch
     codes = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
@@ -140,18 +164,7 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None, out=Non
     device) and returns without synchronising.
     """
     import torch
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_cuda:
-            raise FAError(FA_ERR_NULL_PTR, f"{name} must be a GPU tensor")
-        if t.dim() != 4 or not t.is_contiguous():
-            raise FAError(FA_ERR_BAD_DIM, f"{name} must be a contiguous 4-D tensor")
-    if not (q.dtype == k.dtype == v.dtype):
-        raise FAError(FA_ERR_DTYPE, "q, k and v must share one dtype")
-    B, Hq, Nq, d = q.shape
-    Bk, Hkv, Nkv, dk = k.shape
-    if tuple(v.shape) != tuple(k.shape) or Bk != B or dk != d:
-        raise FAError(FA_ERR_BAD_DIM, f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} "
-                                      f"v{tuple(v.shape)}")
+    B, Hq, Hkv, Nq, Nkv, d = _check_tensors(q, k, v)
     if scale is None:
         scale = 1.0 / float(d) ** 0.5
     if out is None:
@@ -167,6 +180,58 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None, out=Non
     return out, lse
 
 
+def _check_tensors(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise FAError(FA_ERR_NULL_PTR, f"{name} must be a GPU tensor")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise FAError(FA_ERR_BAD_DIM, f"{name} must be a contiguous 4-D tensor")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise FAError(FA_ERR_DTYPE, "q, k and v must share one dtype")
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nkv, dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or dk != d:
+        raise FAError(FA_ERR_BAD_DIM, f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} "
+                                      f"v{tuple(v.shape)}")
+    return B, Hq, Hkv, Nq, Nkv, d
+
+
+def attention_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
+                      num_splits: int | None = None, workspace=None, out=None, lse=None,
+                      stream=None):
+    """Split-KV (FlashDecoding) form of ``attention``: same result, for few query rows.
+
+    ``num_splits`` defaults to fa_splitkv_default_splits.  ``workspace`` (a
+    CUDA tensor of at least fa_splitkv_workspace_bytes bytes) may be given to
+    reuse memory; otherwise torch allocates one.  Returns (out, lse).
+    """
+    import torch
+    B, Hq, Hkv, Nq, Nkv, d = _check_tensors(q, k, v)
+    dt = dtype_code(q.dtype)
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    if num_splits is None:
+        num_splits = fa_splitkv_default_splits(B, Hq, Hkv, Nq, Nkv, d, dt)
+        if num_splits < 1:
+            raise FAError(FA_ERR_BAD_DIM, "no valid split count for these sizes")
+    need = fa_splitkv_workspace_bytes(B, Hq, Nq, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = fa_fwd_splitkv(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, d, float(scale), causal, dt,
+                        num_splits, workspace, ws_bytes, stream)
+    if st != FA_OK:
+        raise FAError(st, fa_status_string(st))
+    return out, lse
+
+
 __all__ = ["fa_fwd", "fa_fwd_stream", "fa_check_args", "fa_status_string", "fa_launch_info",
-           "attention", "load_library", "header_functions", "FAError", "dtype_code",
+           "fa_splitkv_workspace_bytes", "fa_splitkv_default_splits", "fa_fwd_splitkv",
+           "attention", "attention_splitkv", "load_library", "header_functions", "FAError", "dtype_code",
            "FA_F32", "FA_F16", "FA_BF16"]

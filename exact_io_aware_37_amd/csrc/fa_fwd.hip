@@ -586,6 +586,296 @@ attn_fwd_mfma16(Params p) {
   attn_fwd_mfma16_body<T, D, CAUSAL>(p);
 }
 
+// --------------------------------------------------- split-KV (16-bit) path
+//
+// For shapes with few query rows per key/value head (decoding: N_q = 1), the
+// 256-row workgroup above would leave almost every MFMA row empty and the GPU
+// mostly idle.  The course page "FlashAttention: IO-aware attention kernel"
+// (section 3, where the method helps and where it does not) names the decode
+// variant, FlashDecoding, that parallelises over the key/value length
+// instead.  This path cuts the key sequence of every (batch, key/value head)
+// into num_splits chunks and gives each (row block, chunk) pair to one wave.  A row block is 32 consecutive "packed" rows of one key/value head:
+// packed row r stands for query head g*G + r / N_q and query row r % N_q
+// (G = Hq / Hkv), so the query heads that share a K/V head share its
+// stream, and a decode step of a 7:1 group fills 7 MFMA rows instead of 1.
+// Each wave keeps its own running reference, sum and accumulator over its
+// chunk (the same recurrence and lazy reference as the main path), and
+// writes the chunk's normalised output and its lse in fp32 to a workspace.
+// A second kernel merges the chunks of every row with the block merge rule
+// of the omica exam notes (section 2.3), in its form for normalised
+// partials: each chunk weighted by exp(lse_s - lse).
+//
+// Waves are independent (no barrier).  Each streams its chunk in tiles of
+// 32 keys: the K fragments go straight from global memory into registers
+// (each lane reads its own key row), double-buffered one tile ahead; V goes
+// by DMA into a private two-stage LDS ring, one tile ahead, and is read
+// transposed like in the main path.  Eight waves per workgroup (two per
+// SIMD) keep every MFMA within 256 registers in its VGPR form.
+
+template <int D>
+struct CfgSplit {
+  static constexpr int NW = 8;                  // waves (work items) per workgroup
+  static constexpr int NT = 64 * NW;
+  static constexpr int BC = 32;                 // keys per tile
+  static constexpr int ROWB = D * 2;            // bytes per K/V row
+  static constexpr int NCH = D / 8;             // 16-byte chunks per row
+  static constexpr int TILEB = BC * ROWB;       // one V tile of one wave
+  static constexpr int VPT = TILEB / 1024;      // 1 KiB DMA instructions per V tile
+  static constexpr int KPT = D / 16;            // K fragment loads per tile
+  static constexpr int LDS_BYTES = 2 * NW * TILEB;
+  static_assert(VPT >= 1, "DMA split");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+struct SplitParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* ows;       // [S][B*Hq*N_q][d] chunk outputs, normalised
+  float* lws;       // [S][B*Hq*N_q]    chunk lse (natural log), -inf when empty
+  int B, Hq, Hkv, Nq, Nkv;
+  int group;        // G = Hq / Hkv
+  int R;            // packed rows per (b, kv head) = G * N_q
+  int nrb;          // row blocks per (b, kv head) = ceil(R / 32)
+  int S;            // chunks per row block
+  int tps;          // 32-key tiles per chunk
+  long long items;  // B * Hkv * nrb * S
+  long long rows;   // B * Hq * N_q
+  float sl2;
+  int qmode;
+};
+
+template <typename T, int D, bool CAUSAL>
+__device__ __forceinline__ void attn_splitkv_body(const SplitParams& p) {
+  using C = CfgSplit<D>;
+  using M = Mma16<T>;
+  __shared__ __attribute__((aligned(1024))) unsigned char v0[C::NW * C::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char v1[C::NW * C::TILEB];
+  auto vst = [&]<int S>() -> lds_t* { if constexpr ((S & 1) == 0) return (lds_t*)v0; else return (lds_t*)v1; };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+
+  const long long item = (long long)blockIdx.x * C::NW + wave;
+  if (item >= p.items) return;   // no barrier in this kernel: idle waves may leave
+  const int s = (int)(item % p.S);
+  long long rest = item / p.S;
+  const int rb = (int)(rest % p.nrb);
+  rest /= p.nrb;
+  const int g = (int)(rest % p.Hkv);
+  const int b = (int)(rest / p.Hkv);
+
+  // This lane's packed row, its query head and query index.
+  const int r = rb * 32 + l32;
+  const bool row_ok = r < p.R;
+  const int rr = row_ok ? r : p.R - 1;
+  const int hq = g * p.group + rr / p.Nq;
+  const int qi = rr - (rr / p.Nq) * p.Nq;
+  // Largest and smallest query index among the block's rows (causal limits).
+  const int r_lo = rb * 32, r_hi = min(rb * 32 + 31, p.R - 1);
+  const bool one_head = (r_lo / p.Nq) == (r_hi / p.Nq);
+  const int qi_max = one_head ? r_hi % p.Nq : p.Nq - 1;
+  const int qi_min = one_head ? r_lo % p.Nq : 0;
+
+  const int c0 = s * p.tps * C::BC;                              // first key of the chunk
+  int c1 = min(p.Nkv, c0 + p.tps * C::BC);                       // one past its last key
+  if (CAUSAL) c1 = min(c1, qi_max + 1);
+  const int n_tiles = c1 > c0 ? (c1 - c0 + C::BC - 1) / C::BC : 0;
+
+  const size_t kvhead = (size_t)(b * p.Hkv + g) * p.Nkv;
+  const rsrc_t rk = make_rsrc(static_cast<const uint16_t*>(p.k) + kvhead * D, (uint32_t)p.Nkv * C::ROWB);
+  const rsrc_t rv = make_rsrc(static_cast<const uint16_t*>(p.v) + kvhead * D, (uint32_t)p.Nkv * C::ROWB);
+
+  // K fragments of tile t: lane (l32, half) holds key c0 + 32t + l32, dims
+  // cd*16 + half*8 .. +7 (rows past N_kv read as zeros).
+  auto load_k = [&](int t, u32x4 (&kr)[C::KPT]) {
+    const int off = (c0 + t * C::BC + l32) * C::ROWB + half * 16;
+#pragma unroll
+    for (int cd = 0; cd < C::KPT; ++cd)
+      kr[cd] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, off + cd * 32, 0, 0));
+  };
+  // DMA of the V rows of tile t into this wave's part of ring stage S.
+  auto issue_v = [&]<int S>(int t) {
+    const int kv0 = c0 + t * C::BC;
+#pragma unroll
+    for (int u = 0; u < C::VPT; ++u) {
+      const int slot = u * 64 + lane;
+      const int row = slot / C::NCH;
+      const int c = (slot % C::NCH) ^ swz_v<D>(row);
+      lds_t* dst = vst.template operator()<S>() + wave * C::TILEB + u * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst, 16, (kv0 + row) * C::ROWB + c * 16, 0, 0, 0);
+    }
+  };
+
+  u32x4 ka[C::KPT], kb[C::KPT];
+  if (n_tiles > 0) {
+    load_k(0, ka);
+    issue_v.template operator()<0>(0);
+  }
+
+  // Q^T operand of the wave's 32 packed rows (zeros past R).
+  const uint32_t qxor = p.qmode == 1 ? 0x80008000u : 0u;
+  const uint32_t qand = p.qmode == 2 ? 0u : 0xffffffffu;
+  const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + ((size_t)(b * p.Hq + hq) * p.Nq + qi) * D;
+  u32x4 qreg[D / 16];
+#pragma unroll
+  for (int cd = 0; cd < D / 16; ++cd) {
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (row_ok) x = *reinterpret_cast<const u32x4*>(qrow + cd * 16 + half * 8);
+    qreg[cd] = (x ^ qxor) & qand;
+  }
+
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const int vrow = (g16 >> 1) * 4 + (s16 >> 2);
+  const int vbase = vrow * C::ROWB + (swz_v<D>(vrow) >> 2) * 64 + (g16 & 1) * 32 +
+                    ((s16 & 3) >> 1) * 16 + (s16 & 1) * 8;
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // Tile t from K registers kc and V stage S.  Inside the loop every step
+  // prefetches tile t+1 into kn and stage S^1; the last tile of the loop
+  // "prefetches" itself again (a cached re-read), so the loop body has no
+  // branch around its memory operations and the wait count is exact.  The
+  // peeled final step (LAST) prefetches nothing and waits for everything: a
+  // prefetch there would load registers nobody reads, which the compiler may
+  // drop, and a fixed wait count would then be wrong.
+  auto step = [&]<int S, bool LAST>(int t, u32x4 (&kc)[C::KPT], u32x4 (&kn)[C::KPT]) {
+    if constexpr (LAST) {
+      (void)kn;
+      wait_vm_lgkm<0>();
+    } else {
+      const int tn = min(t + 1, n_tiles - 1);
+      load_k(tn, kn);
+      issue_v.template operator()<S ^ 1>(tn);
+      wait_vm_lgkm<C::KPT + C::VPT>();
+    }
+    f32x16 sc = f32x16{};
+#pragma unroll
+    for (int cd = 0; cd < D / 16; ++cd) sc = M::mma(kc[cd], qreg[cd], sc);
+    const int kv0 = c0 + t * C::BC;
+    const bool need_mask = (kv0 + C::BC > c1) || (CAUSAL && kv0 + C::BC - 1 > qi_min);
+    if (need_mask) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = kv0 + (e >> 2) * 8 + half * 4 + (e & 3);
+        if (key >= c1 || (CAUSAL && key > qi)) sc[e] = -INFINITY;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[e]);
+    mx = pair_max(mx);
+    const float mc = mx * p.sl2;
+    const float m_new = (mc > m_run + kLazy) ? mc : m_run;
+    const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
+    if (wave_any(alpha != 1.f)) {
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
+    }
+    const float mu = (m_run == -INFINITY) ? 0.f : m_run;
+    u32x4 pk[2];
+    float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float e0 = fast_exp2(fmaf(sc[cc * 8 + 2 * w], p.sl2, -mu));
+        const float e1 = fast_exp2(fmaf(sc[cc * 8 + 2 * w + 1], p.sl2, -mu));
+        const uint32_t pr = M::pack(e0, e1);
+        pk[cc][w] = pr;
+        if (w & 1) ls1 = M::sum2(pr, ls1);
+        else ls0 = M::sum2(pr, ls0);
+      }
+    }
+    l_run += ls0 + ls1;
+    // The empty asm makes the compiler recompute the few XORs below every
+    // tile instead of keeping one address register per (stage, fragment).
+    int vb = wave * C::TILEB + vbase;
+    asm volatile("" : "+v"(vb));
+    const lds_t* vs = vst.template operator()<S>();
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const lds_t* a0 = vs + (vb ^ (db * 64)) + (cc * 16) * C::ROWB;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)a0);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(a0 + 8 * C::ROWB));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        const u32x4 x = {l2[0], l2[1], h2[0], h2[1]};
+        acc[db] = M::mma(x, pk[cc], acc[db]);
+      }
+    }
+  };
+  int t = 0;
+  for (; t + 1 < n_tiles; t += 2) {
+    step.template operator()<0, false>(t, ka, kb);
+    step.template operator()<1, false>(t + 1, kb, ka);
+  }
+  if (t < n_tiles) step.template operator()<0, true>(t, ka, kb);
+
+  // Chunk result: normalised output and lse, or (0, -inf) for an empty chunk.
+  const float l_tot = pair_sum(l_run);
+  const bool has = l_tot > 0.f;
+  const float inv = has ? 1.f / l_tot : 0.f;
+  if (row_ok) {
+    const size_t row = (size_t)(b * p.Hq + hq) * p.Nq + qi;
+    float* dst = p.ows + ((size_t)s * p.rows + row) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const f32x4 w = {acc[db][4 * gq] * inv, acc[db][4 * gq + 1] * inv, acc[db][4 * gq + 2] * inv,
+                         acc[db][4 * gq + 3] * inv};
+        *reinterpret_cast<f32x4*>(dst + db * 32 + gq * 8 + half * 4) = w;
+      }
+    }
+    if (half == 0) p.lws[(size_t)s * p.rows + row] = has ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(CfgSplit<D>::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_splitkv_mfma16(SplitParams p) {
+  attn_splitkv_body<T, D, CAUSAL>(p);
+}
+
+// Merge of the chunk results of every row: lse = ln sum_s exp(lse_s) and
+// O = sum_s exp(lse_s - lse) O_s, rounded once to the output type.  D/4
+// lanes share a row, each with 4 consecutive head dimensions.
+template <typename T, int D>
+__global__ void __launch_bounds__(256) attn_splitkv_combine(const float* __restrict__ ows,
+                                                             const float* __restrict__ lws,
+                                                             T* __restrict__ o, float* __restrict__ lse,
+                                                             long long rows, int S) {
+  constexpr int LPR = D / 4;             // lanes per row
+  const long long row = ((long long)blockIdx.x * 256 + threadIdx.x) / LPR;
+  const int part = threadIdx.x % LPR;
+  if (row >= rows) return;
+  float mx = -INFINITY;
+  for (int s = 0; s < S; ++s) mx = fmaxf(mx, lws[(size_t)s * rows + row]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float ls = lws[(size_t)s * rows + row];
+    if (ls == -INFINITY) continue;
+    const float w = fast_exp2((ls - mx) * kLog2e);
+    wsum += w;
+    acc += w * *reinterpret_cast<const f32x4*>(ows + ((size_t)s * rows + row) * D + part * 4);
+  }
+  const float inv = 1.f / wsum;
+  T out4[4] = {(T)(acc[0] * inv), (T)(acc[1] * inv), (T)(acc[2] * inv), (T)(acc[3] * inv)};
+  *reinterpret_cast<u32x2*>(o + row * D + part * 4) = __builtin_bit_cast(u32x2, out4);
+  if (part == 0) lse[row] = mx + fast_log2(wsum) * kLn2;
+}
+
 // ------------------------------------------------------------- fp32 path
 
 template <int D>
@@ -856,6 +1146,59 @@ int dispatch16(const Params& p, int d, bool causal, long long blocks, hipStream_
   return causal ? run16<T, 128, true>(p, blocks, s) : run16<T, 128, false>(p, blocks, s);
 }
 
+// Split-KV geometry for valid dimensions (d, dtype already checked).
+struct SplitGeometry {
+  int R, nrb, n_tiles;   // packed rows per kv head, row blocks, 32-key tiles of N_kv
+};
+
+SplitGeometry split_geometry(int Hq, int Hkv, int N_q, int N_kv) {
+  SplitGeometry g;
+  g.R = (Hq / Hkv) * N_q;
+  g.nrb = (g.R + 31) / 32;
+  g.n_tiles = (N_kv + 31) / 32;
+  return g;
+}
+
+int check_split_dims(int B, int Hq, int Hkv, int N_q, int N_kv, int d, int dtype, int num_splits) {
+  if (dtype == FA_F32) return FA_ERR_DTYPE;
+  const int st = check_dims(B, Hq, Hkv, N_q, N_kv, d, dtype, nullptr);
+  if (st != FA_OK) return st;
+  if ((long long)(Hq / Hkv) * N_q > 0x7fffffffLL - 32) return FA_ERR_BAD_DIM;
+  const SplitGeometry g = split_geometry(Hq, Hkv, N_q, N_kv);
+  if (num_splits < 1 || num_splits > g.n_tiles || num_splits > FA_SPLITKV_MAX_SPLITS)
+    return FA_ERR_BAD_DIM;
+  const long long items = (long long)B * Hkv * g.nrb * num_splits;
+  if ((items + 3) / 4 > 0x7fffffffLL) return FA_ERR_BAD_DIM;
+  return FA_OK;
+}
+
+template <typename T, int D, bool CAUSAL>
+int run_split(const SplitParams& sp, T* o, float* lse, hipStream_t stream) {
+  using C = CfgSplit<D>;
+  (void)hipGetLastError();
+  const long long blocks = (sp.items + C::NW - 1) / C::NW;
+  hipLaunchKernelGGL((attn_splitkv_mfma16<T, D, CAUSAL>), dim3((unsigned)blocks), dim3(C::NT), 0,
+                     stream, sp);
+  const long long cblocks = (sp.rows * (D / 4) + 255) / 256;
+  hipLaunchKernelGGL((attn_splitkv_combine<T, D>), dim3((unsigned)cblocks), dim3(256), 0, stream,
+                     sp.ows, sp.lws, o, lse, sp.rows, sp.S);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    snprintf(g_hip_error, sizeof g_hip_error, "HIP error: %s (%s)", hipGetErrorName(e),
+             hipGetErrorString(e));
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
+template <typename T>
+int dispatch_split(const SplitParams& sp, void* o, float* lse, int d, bool causal, hipStream_t s) {
+  T* ot = static_cast<T*>(o);
+  if (d == 64)
+    return causal ? run_split<T, 64, true>(sp, ot, lse, s) : run_split<T, 64, false>(sp, ot, lse, s);
+  return causal ? run_split<T, 128, true>(sp, ot, lse, s) : run_split<T, 128, false>(sp, ot, lse, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -947,6 +1290,84 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   return fa_fwd_stream(q, k, v, o, lse, B, Hq, Hkv, N_q, N_kv, d, scale, causal, dtype, nullptr);
 }
 
+size_t fa_splitkv_workspace_bytes(int B, int Hq, int N_q, int d, int num_splits) {
+  if (B < 1 || Hq < 1 || N_q < 1 || (d != 64 && d != 128) || num_splits < 1 ||
+      num_splits > FA_SPLITKV_MAX_SPLITS)
+    return 0;
+  const unsigned long long rows = (unsigned long long)B * Hq * N_q;
+  return (size_t)(rows * (unsigned long long)num_splits * (d + 1) * sizeof(float));
+}
+
+int fa_splitkv_default_splits(int B, int Hq, int Hkv, int N_q, int N_kv, int d, int dtype) {
+  const int st = check_split_dims(B, Hq, Hkv, N_q, N_kv, d, dtype, 1);
+  if (st != FA_OK) return 0;
+  const SplitGeometry g = split_geometry(Hq, Hkv, N_q, N_kv);
+  // About 2048 waves (two rounds of 4 waves on each of the 256 CUs), and at
+  // least 4 tiles (128 keys) per chunk so the merge stays cheap.
+  const long long base = (long long)B * Hkv * g.nrb;
+  long long s = (2048 + base - 1) / base;
+  const long long cap = (g.n_tiles + 3) / 4;
+  if (s > cap) s = cap;
+  if (s > FA_SPLITKV_MAX_SPLITS) s = FA_SPLITKV_MAX_SPLITS;
+  return s < 1 ? 1 : (int)s;
+}
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                   int Hq, int Hkv, int N_q, int N_kv, int d, float scale, int causal, int dtype,
+                   int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace) return FA_ERR_NULL_PTR;
+  int st = fa_check_args(q, k, v, o, lse, B, Hq, Hkv, N_q, N_kv, d, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  st = check_split_dims(B, Hq, Hkv, N_q, N_kv, d, dtype, num_splits);
+  if (st != FA_OK) return st;
+  const size_t need = fa_splitkv_workspace_bytes(B, Hq, N_q, d, num_splits);
+  if (workspace_bytes < need) return FA_ERR_WORKSPACE;
+  const uintptr_t pw = (uintptr_t)workspace;
+  if ((pw & 15u) != 0) return FA_ERR_ALIGN;
+  const size_t es = elem_size(dtype);
+  const size_t nq = (size_t)B * Hq * N_q * d * es;
+  const size_t nkv = (size_t)B * Hkv * N_kv * d * es;
+  const size_t nl = (size_t)B * Hq * N_q * sizeof(float);
+  if (overlaps(pw, need, (uintptr_t)q, nq) || overlaps(pw, need, (uintptr_t)k, nkv) ||
+      overlaps(pw, need, (uintptr_t)v, nkv) || overlaps(pw, need, (uintptr_t)o, nq) ||
+      overlaps(pw, need, (uintptr_t)lse, nl))
+    return FA_ERR_ALIAS;
+
+  const SplitGeometry g = split_geometry(Hq, Hkv, N_q, N_kv);
+  SplitParams sp;
+  sp.q = q;
+  sp.k = k;
+  sp.v = v;
+  sp.rows = (long long)B * Hq * N_q;
+  sp.ows = static_cast<float*>(workspace);
+  sp.lws = sp.ows + (size_t)num_splits * sp.rows * d;
+  sp.B = B;
+  sp.Hq = Hq;
+  sp.Hkv = Hkv;
+  sp.Nq = N_q;
+  sp.Nkv = N_kv;
+  sp.group = Hq / Hkv;
+  sp.R = g.R;
+  sp.nrb = g.nrb;
+  sp.S = num_splits;
+  sp.tps = (g.n_tiles + num_splits - 1) / num_splits;
+  sp.items = (long long)B * Hkv * g.nrb * num_splits;
+  if (scale > 0.f) {
+    sp.sl2 = scale * kLog2e;
+    sp.qmode = 0;
+  } else if (scale < 0.f) {
+    sp.sl2 = -scale * kLog2e;
+    sp.qmode = 1;
+  } else {
+    sp.sl2 = 1.f;
+    sp.qmode = 2;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool c = causal != 0;
+  if (dtype == FA_BF16) return dispatch_split<__bf16>(sp, o, lse, d, c, s);
+  return dispatch_split<_Float16>(sp, o, lse, d, c, s);
+}
+
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
@@ -957,7 +1378,8 @@ const char* fa_status_string(int status) {
     case FA_ERR_DTYPE: return "dtype must be FA_F32, FA_F16 or FA_BF16";
     case FA_ERR_SCALE: return "scale must be finite";
     case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
-    case FA_ERR_ALIAS: return "o or lse overlaps an input or each other";
+    case FA_ERR_ALIAS: return "o, lse or the workspace overlaps an input or each other";
+    case FA_ERR_WORKSPACE: return "workspace smaller than fa_splitkv_workspace_bytes";
     case FA_ERR_HIP: return g_hip_error[0] ? g_hip_error : "HIP runtime error";
     default: return "unknown status";
   }

@@ -48,6 +48,8 @@
 #ifndef FA_H_
 #define FA_H_
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -62,7 +64,8 @@ typedef enum fa_status {
     FA_ERR_SCALE = 6,      /* scale is NaN or infinite                           */
     FA_ERR_ALIGN = 7,      /* a pointer is misaligned                            */
     FA_ERR_HIP = 8,        /* the HIP runtime reported an error                  */
-    FA_ERR_ALIAS = 9       /* o or lse overlaps q, k, v or each other            */
+    FA_ERR_ALIAS = 9,      /* o, lse or a workspace overlaps an input or another */
+    FA_ERR_WORKSPACE = 10  /* workspace smaller than fa_splitkv_workspace_bytes  */
 } fa_status;
 
 typedef enum fa_dtype {
@@ -109,6 +112,56 @@ const char* fa_status_string(int status);
 int fa_launch_info(int B, int Hq, int Hkv, int N_q, int N_kv, int d, int causal,
                    int dtype, int* rows_per_block, int* keys_per_tile,
                    int* threads_per_block, long long* blocks, int* lds_bytes);
+
+/*
+ * Split-KV forward (FlashDecoding).  Same operation, arguments, layouts,
+ * masking and rounding as fa_fwd, for shapes with few query rows per
+ * key/value head, above all decoding (N_q = 1).  The course page
+ * "FlashAttention: IO-aware attention kernel" (section 3, where the method
+ * helps and where it does not; sections 8 and 9) names this decode variant,
+ * FlashDecoding: it parallelises over the key/value length to fill the GPU.
+ * Here the keys of every (batch, key/value head) are cut into num_splits chunks of
+ * ceil(ceil(N_kv / 32) / num_splits) tiles of 32 keys; each chunk yields
+ * the exact attention of its rows over that chunk alone (output O_s and
+ * lse_s); a second launch merges them with the block merge rule of the
+ * omica exam notes (section 2.3), written for normalised partials:
+ *
+ *     lse = ln sum_s exp(lse_s),   O = sum_s exp(lse_s - lse) * O_s
+ *
+ * which equals attention over all keys.  For a decoding step pass causal = 0
+ * (the new query sees every cached key; causal masking keeps the literal
+ * j <= i convention of fa_fwd).  Chunks with no allowed key of a
+ * row contribute nothing (lse_s = -inf).  The query heads that share a
+ * key/value head are processed together: rows (h, i) of one group form one
+ * sequence of Hq/Hkv * N_q "packed" rows, 32 per wave.
+ *
+ * dtype FA_BF16 or FA_F16 only (FA_ERR_DTYPE for FA_F32); d 64 or 128.
+ * 1 <= num_splits <= min(ceil(N_kv / 32), FA_SPLITKV_MAX_SPLITS), else
+ * FA_ERR_BAD_DIM.
+ *
+ * workspace: caller-owned device memory of at least
+ * fa_splitkv_workspace_bytes(B, Hq, N_q, d, num_splits) bytes (FA_ERR_WORKSPACE
+ * otherwise), 16-byte aligned (FA_ERR_ALIGN), not overlapping q, k, v, o or
+ * lse (FA_ERR_ALIAS).  It holds the chunk results in fp32,
+ *     O_s   [num_splits][B*Hq*N_q][d]   then
+ *     lse_s [num_splits][B*Hq*N_q],
+ * row index (b*Hq + h)*N_q + i, and is fully rewritten by every call; its
+ * previous contents do not matter.  Both launches go to `stream` (NULL = null
+ * stream); calls that share a workspace must be ordered on one stream.
+ * The library itself still allocates nothing.
+ */
+#define FA_SPLITKV_MAX_SPLITS 256
+
+size_t fa_splitkv_workspace_bytes(int B, int Hq, int N_q, int d, int num_splits);
+
+/* A split count for these sizes that fills the GPU (about 2048 waves), with
+ * at least 4 tiles per chunk; 0 when the sizes are invalid for fa_fwd_splitkv. */
+int fa_splitkv_default_splits(int B, int Hq, int Hkv, int N_q, int N_kv, int d, int dtype);
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int Hq, int Hkv, int N_q, int N_kv, int d,
+                   float scale, int causal, int dtype, int num_splits,
+                   void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

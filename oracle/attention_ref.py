@@ -148,6 +148,45 @@ def attention_fp64(q, k, v, scale: float, causal: bool = False,
     return o, lse
 
 
+def attention_fp64_key_range(q, k, v, scale: float, causal: bool, lo: int, hi: int):
+    """Exact attention of every row over its allowed keys that lie in [lo, hi).
+
+    The same definition as ``attention_fp64`` with the key set J_i replaced by
+    J_i intersected with [lo, hi) (causal masking keeps absolute indices).  A
+    row whose restricted key set is empty has no softmax; it gets O = 0 and
+    lse = -inf, the values that contribute nothing to the block merge rule
+    ([P2] §二.3).  This is the partial result one split-KV chunk stands for.
+    Plain and unthreaded: meant for small cases.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, Hkv, Nq, Nkv, D = _check_shapes(q, k, v)
+    sigma = _sigma(scale)
+    lo, hi = max(0, int(lo)), min(Nkv, int(hi))
+    o = np.zeros((B, Hq, Nq, D), dtype=np.float64)
+    lse = np.full((B, Hq, Nq), -np.inf, dtype=np.float64)
+    if hi <= lo:
+        return o, lse
+    keys = np.arange(lo, hi)
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            s = sigma * (q[b, h] @ k[b, g, lo:hi].T)          # [Nq, hi - lo]
+            if causal:
+                s = np.where(keys[None, :] <= np.arange(Nq)[:, None], s, -np.inf)
+            for i in range(Nq):
+                row = s[i]
+                if not np.any(np.isfinite(row)):
+                    continue                                   # empty: (0, -inf)
+                m = row.max()
+                e = np.exp(row - m)
+                l = e.sum()
+                o[b, h, i] = (e / l) @ v[b, g, lo:hi]
+                lse[b, h, i] = m + np.log(l)
+    return o, lse
+
+
 def probabilities_fp64(q, k, scale: float, causal: bool = False):
     """Full probability tensor P [B, Hq, Nq, Nkv] (masked entries are 0).
 

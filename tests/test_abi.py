@@ -34,7 +34,8 @@ def lib():
 def test_library_exports_every_declared_symbol(lib):
     names = fa.header_functions()
     assert set(names) == {"fa_fwd", "fa_fwd_stream", "fa_check_args", "fa_status_string",
-                          "fa_launch_info"}
+                          "fa_launch_info", "fa_splitkv_workspace_bytes",
+                          "fa_splitkv_default_splits", "fa_fwd_splitkv"}
     for n in names:
         assert hasattr(lib, n), n
         assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
@@ -115,7 +116,7 @@ def test_fwd_rejects_on_host_without_touching_hip(lib):
 
 
 def test_status_strings(lib):
-    for st in range(0, 10):
+    for st in range(0, 11):
         s = fa.fa_status_string(st)
         assert isinstance(s, str) and s
     assert fa.fa_status_string(123) == "unknown status"
@@ -145,3 +146,55 @@ def test_sequence_length_limit(lib):
     far = dict(q=1 << 40, k=2 << 40, v=3 << 40, o=4 << 40, lse=5 << 40)
     assert check(N_q=16, N_kv=n_ok, B=1, Hq=1, Hkv=1, **far) == fa.FA_OK
     assert check(N_q=16, N_kv=n_ok + 2, B=1, Hq=1, Hkv=1, **far) == fa.FA_ERR_BAD_DIM
+
+
+# ---- split-KV entry points ------------------------------------------------
+
+W = 0x60000000   # fake workspace, clear of Q, K, V, O, L above
+
+
+def split(q=Q, k=K, v=V, o=O, lse=L, ws=W, ws_bytes=None, S=2, **kw):
+    a = args(**kw)
+    if ws_bytes is None:
+        ws_bytes = fa.fa_splitkv_workspace_bytes(a["B"], a["Hq"], a["N_q"], a["d"], S)
+    # Every case below fails its host checks, so no call reaches HIP.
+    return fa.fa_fwd_splitkv(q, k, v, o, lse, a["B"], a["Hq"], a["Hkv"], a["N_q"], a["N_kv"],
+                             a["d"], a["scale"], a["causal"], a["dtype"], S, ws, ws_bytes, None)
+
+
+def test_splitkv_workspace_bytes(lib):
+    # O_s in fp32 for every (split, row, dim) plus one fp32 lse per (split, row)
+    assert fa.fa_splitkv_workspace_bytes(8, 28, 1, 128, 64) == 64 * 8 * 28 * (128 + 1) * 4
+    assert fa.fa_splitkv_workspace_bytes(2, 3, 5, 64, 1) == 2 * 3 * 5 * 65 * 4
+    for bad in [(0, 1, 1, 64, 1), (1, 0, 1, 64, 1), (1, 1, 0, 64, 1), (1, 1, 1, 96, 1),
+                (1, 1, 1, 64, 0), (1, 1, 1, 64, fa.FA_SPLITKV_MAX_SPLITS + 1)]:
+        assert fa.fa_splitkv_workspace_bytes(*bad) == 0
+
+
+def test_splitkv_default_splits(lib):
+    # decode, 8 x 4 kv heads x 1 row block: 2048 waves / 32 items = 64 splits
+    assert fa.fa_splitkv_default_splits(8, 28, 4, 1, 32768, 128, fa.FA_BF16) == 64
+    # short keys: at least 4 tiles of 32 keys per split
+    assert fa.fa_splitkv_default_splits(1, 8, 1, 1, 256, 64, fa.FA_F16) == 2
+    # plenty of row blocks already: no split
+    assert fa.fa_splitkv_default_splits(4, 32, 32, 2048, 2048, 128, fa.FA_BF16) == 1
+    # never above the cap, invalid sizes give 0
+    assert fa.fa_splitkv_default_splits(1, 1, 1, 1, 1 << 20, 64, fa.FA_BF16) == \
+        fa.FA_SPLITKV_MAX_SPLITS
+    assert fa.fa_splitkv_default_splits(1, 1, 1, 1, 64, 64, fa.FA_F32) == 0
+    assert fa.fa_splitkv_default_splits(1, 3, 2, 1, 64, 64, fa.FA_BF16) == 0
+
+
+def test_splitkv_rejects_on_host(lib):
+    good = dict(N_q=1, N_kv=1000)
+    assert split(ws=0, **good) == fa.FA_ERR_NULL_PTR
+    assert split(dtype=fa.FA_F32, **good) == fa.FA_ERR_DTYPE
+    assert split(S=0, **good) == fa.FA_ERR_BAD_DIM
+    assert split(S=33, **good) == fa.FA_ERR_BAD_DIM          # 1000 keys = 32 tiles: S <= 32
+    assert split(ws_bytes=16, **good) == fa.FA_ERR_WORKSPACE
+    assert split(ws=W + 4, **good) == fa.FA_ERR_ALIGN
+    assert split(ws=O, **good) == fa.FA_ERR_ALIAS
+    assert split(ws=Q - 64, **good) == fa.FA_ERR_ALIAS
+    assert split(d=96, **good) == fa.FA_ERR_HEAD_DIM
+    assert split(Hq=7, **good) == fa.FA_ERR_HEAD_GROUP
+    assert split(q=0, **good) == fa.FA_ERR_NULL_PTR

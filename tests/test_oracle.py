@@ -18,8 +18,8 @@ import pytest
 import torch
 from scipy.special import logsumexp, softmax
 
-from oracle import (attention_bruteforce, attention_fp64, attention_online_blocked,
-                    probabilities_fp64, kv_head_of)
+from oracle import (attention_bruteforce, attention_fp64, attention_fp64_key_range,
+                    attention_online_blocked, probabilities_fp64, kv_head_of)
 import workloads
 
 pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
@@ -307,3 +307,42 @@ def test_row_subset_matches_whole(causal):
     o_r, l_r = attention_fp64(q, k, v, 0.3, causal, rows=rows, row_chunk=3)
     assert np.array_equal(o_r, o[:, :, rows]) or np.max(np.abs(o_r - o[:, :, rows])) <= 1e-15
     assert np.max(np.abs(l_r - l[:, :, rows])) <= 1e-15
+
+
+# ---- key-range partials (the chunk results of the split-KV form) ----------
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("cuts", [(0, 100), (0, 1, 100), (0, 37, 64, 65, 100), (0, 50, 50, 100)])
+def test_key_range_chunks_merge_to_full(causal, cuts):
+    """Chunk results over a partition of the keys, merged by the [P2] §二.3 rule
+    (new max, every part rescaled to it, sums added), give the full result."""
+    q, k, v = _rand(2, 6, 2, 40, 100, 16, seed=23)
+    full_o, full_l = attention_fp64(q, k, v, 0.4, causal)
+    parts = [attention_fp64_key_range(q, k, v, 0.4, causal, a, b)
+             for a, b in zip(cuts[:-1], cuts[1:])]
+    m = np.max(np.stack([pl for _, pl in parts]), axis=0)
+    w = [np.exp(pl - m) for _, pl in parts]            # exp(-inf) = 0 for empty parts
+    l_sum = sum(w)
+    o = sum(wi[..., None] * po for wi, (po, _) in zip(w, parts)) / l_sum[..., None]
+    assert np.max(np.abs(o - full_o)) <= 1e-13
+    assert np.max(np.abs(m + np.log(l_sum) - full_l)) <= 1e-13
+
+
+def test_key_range_whole_range_equals_full():
+    q, k, v = _rand(1, 3, 3, 20, 33, 8, seed=29)
+    for causal in (False, True):
+        o, l = attention_fp64_key_range(q, k, v, 0.7, causal, 0, 33)
+        fo, fl = attention_fp64(q, k, v, 0.7, causal)
+        assert np.max(np.abs(o - fo)) <= 1e-14 and np.max(np.abs(l - fl)) <= 1e-14
+
+
+def test_key_range_empty_rows_and_single_key():
+    q, k, v = _rand(1, 1, 1, 10, 10, 4, seed=31)
+    # causal rows i < 6 have no key in [6, 10): O = 0, lse = -inf
+    o, l = attention_fp64_key_range(q, k, v, 1.0, True, 6, 10)
+    assert np.all(o[0, 0, :6] == 0) and np.all(np.isneginf(l[0, 0, :6]))
+    assert np.all(np.isfinite(l[0, 0, 6:]))
+    # one key: O is that value row, lse its score
+    o, l = attention_fp64_key_range(q, k, v, 0.5, False, 3, 4)
+    assert np.allclose(o[0, 0], np.broadcast_to(v[0, 0, 3], (10, 4)), rtol=0, atol=1e-15)
+    assert np.allclose(l[0, 0], 0.5 * q[0, 0] @ k[0, 0, 3], rtol=0, atol=1e-14)

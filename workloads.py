@@ -9,7 +9,11 @@ The five named workloads have the shapes of the pages' setting: the course
 lab of "FlashAttention: IO-aware attention kernel" (§5) uses random
 [B, H, S, D] bf16 tensors in a 7B decoder's attention shape (28 heads of 128)
 with a causal mask; the others are multi-head and long-sequence variants.
-No public dataset is involved; nothing is read from disk.
+Workload 6 is one decoding step of that 7B shape (one new query row per
+sequence against a 32768-key cache, batch 8), the case the same page (§3,
+where the method helps and where it does not) sends to the split-KV
+FlashDecoding variant.  No public dataset is involved; nothing is read from
+disk.
 
 Recipe (all workloads): ``numpy.random.default_rng(seed)`` (PCG64), draw Q,
 then K, then (for outlier workloads) the outlier rows of K, then V, each as
@@ -60,6 +64,13 @@ class Workload:
         f = 4.0 * self.B * self.Hq * self.Nq * self.Nkv * self.D
         return f / 2.0 if self.causal else f
 
+    def io_bytes(self) -> float:
+        """Compulsory HBM bytes of one forward: Q, K, V read once, O and lse written once."""
+        es = 4 if self.dtype == "f32" else 2
+        q = self.B * self.Hq * self.Nq * self.D
+        kv = self.B * self.Hkv * self.Nkv * self.D
+        return float(es * (2 * q + 2 * kv) + 4 * self.B * self.Hq * self.Nq)
+
     def as_dict(self) -> dict:
         d = asdict(self)
         d["seed"] = self.seed
@@ -73,6 +84,7 @@ WORKLOADS = {
     4: Workload(4, "causal_gqa_7b_prefill_n4096", 1, 28, 4, 4096, 4096, 128, "bf16", True),
     5: Workload(5, "long_causal_gqa_n32768_outlier_keys", 1, 28, 4, 32768, 32768, 128, "bf16",
                 True, sigma=0.5, outlier_frac=0.01, outlier_mult=8.0),
+    6: Workload(6, "decode_gqa_7b_b8_n32768", 8, 28, 4, 1, 32768, 128, "bf16", False),
 }
 
 
