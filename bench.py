@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
 METRIC = "attn fwd TFLOP/s and % of MI355X bf16 MFMA peak (N=8k/32k, d=128)"
 
 
@@ -42,6 +43,11 @@ def parse():
                     help="approximate CPU time budget of the oracle baseline (0 disables)")
     ap.add_argument("--check-rows", type=int, default=64,
                     help="rows per sampled head checked against the oracle after timing")
+    ap.add_argument("--path", choices=["auto", "fwd", "splitkv"], default="auto",
+                    help="entry point to time: fa_fwd_stream, or fa_fwd_splitkv (auto: split-KV "
+                         "for the decoding workload 6, fa_fwd otherwise)")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="split count for the split-KV path (0: fa_splitkv_default_splits)")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the context measurements (library GEMM and zero-input run)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -137,8 +143,12 @@ def power_context(fa, w, qd, kd, vd, o, lse, scale, stream, dcode):
     }
 
 
-def cpu_baseline(w, q, k, v, budget_s):
-    """Time the oracle on whole (b, h) heads until ~budget_s of wall time."""
+def cpu_baseline(w, q, k, v, budget_s, hbm_bound=False):
+    """Time the oracle on whole (b, h) heads until ~budget_s of wall time.
+
+    The rate is in the benchmark's unit: FLOPs of the heads done (TFLOP/s), or
+    for the HBM-bound decoding workload their share of the compulsory bytes
+    (GB/s)."""
     import numpy as np
     import workloads
     from oracle import attention_fp64
@@ -149,7 +159,7 @@ def cpu_baseline(w, q, k, v, budget_s):
     order = rng.permutation(len(heads))
     g = w.Hq // w.Hkv
     done, t_total, flops = 0, 0.0, 0.0
-    per_head = w.flops() / (w.B * w.Hq)
+    per_head = (w.io_bytes() if hbm_bound else w.flops()) / (w.B * w.Hq)
     for i in order:
         b, h = heads[i]
         qh = workloads.to_f64(q[b:b + 1, h:h + 1])
@@ -162,7 +172,8 @@ def cpu_baseline(w, q, k, v, budget_s):
         done += 1
         if t_total >= budget_s:
             break
-    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": cores,
+    scale, unit = (1e9, "GB/s") if hbm_bound else (1e12, "TFLOP/s")
+    return {"value": flops / t_total / scale, "unit": unit, "cores": cores,
             "kind": "oracle",
             "sample": f"{done} of {len(heads)} (b,h) heads of the same workload, all "
                       f"{w.Nq} rows each, fp64 numpy, {t_total:.2f} s",
@@ -195,11 +206,25 @@ def main():
     dcode = fa.dtype_code(qd.dtype)
     fa.load_library()
 
-    def step():
-        st = fa.fa_fwd_stream(qd, kd, vd, o, lse, w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, scale,
-                              w.causal, dcode, stream)
-        if st != 0:
-            raise RuntimeError(fa.fa_status_string(st))
+    path = args.path if args.path != "auto" else ("splitkv" if w.index == 6 else "fwd")
+    splits = None
+    if path == "splitkv":
+        splits = args.splits or fa.fa_splitkv_default_splits(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D,
+                                                              dcode)
+        ws_bytes = fa.fa_splitkv_workspace_bytes(w.B, w.Hq, w.Nq, w.D, splits)
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+        def step():
+            st = fa.fa_fwd_splitkv(qd, kd, vd, o, lse, w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, scale,
+                                   w.causal, dcode, splits, workspace, ws_bytes, stream)
+            if st != 0:
+                raise RuntimeError(fa.fa_status_string(st))
+    else:
+        def step():
+            st = fa.fa_fwd_stream(qd, kd, vd, o, lse, w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, scale,
+                                  w.causal, dcode, stream)
+            if st != 0:
+                raise RuntimeError(fa.fa_status_string(st))
 
     for _ in range(args.warmup):
         step()
@@ -222,19 +247,27 @@ def main():
     wall_ms = wall * 1e3 / args.steps
 
     flops = w.flops()
-    value = flops / (wall_ms * 1e-3) / 1e12
-    achieved = flops / (kernel_ms * 1e-3) / 1e12
-    peak = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
-    print(f"[bench] {w.name}: kernel {kernel_ms:.4f} ms/launch (events), wall {wall_ms:.4f} "
-          f"ms/step -> {achieved:.1f} TFLOP/s = {100 * achieved / peak:.1f}% of {peak} peak",
-          file=sys.stderr, flush=True)
+    hbm_bound = path == "splitkv"
+    if hbm_bound:
+        # Decoding reads the whole K/V cache for one query row per head: HBM-bound.
+        work, unit, peak, bound = w.io_bytes() / 1e9, "GB/s", PEAK_HBM_GBS, "hbm"
+        metric = "decode attention HBM GB/s (split-KV, compulsory bytes)"
+    else:
+        work, unit, bound = flops / 1e12, "TFLOP/s", "mfma"
+        peak = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
+        metric = METRIC
+    value = work / (wall_ms * 1e-3)
+    achieved = work / (kernel_ms * 1e-3)
+    print(f"[bench] {w.name} ({path}): kernel {kernel_ms:.4f} ms/step (events), wall "
+          f"{wall_ms:.4f} ms/step -> {achieved:.1f} {unit} = {100 * achieved / peak:.1f}% of "
+          f"{peak} peak", file=sys.stderr, flush=True)
 
     # Sampled parity of the benchmarked output (a few heads, a few rows each).
     check = None
     if args.check_rows > 0:
         from oracle import attention_fp64
         rng = np.random.default_rng(1)
-        rows = np.unique(np.concatenate([rng.choice(w.Nq, args.check_rows, replace=False),
+        rows = np.unique(np.concatenate([rng.choice(w.Nq, min(args.check_rows, w.Nq), replace=False),
                                          [0, w.Nq - 1]]))
         g = w.Hq // w.Hkv
         errs = []
@@ -252,18 +285,23 @@ def main():
                  "rows_checked": int(len(rows)) * len(errs)}
 
     context = None
-    if not args.no_context and w.dtype != "f32":
+    if not args.no_context and w.dtype != "f32" and not hbm_bound:
         context = power_context(fa, w, qd, kd, vd, o, lse, scale, stream, dcode)
 
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(w, q, k, v, args.cpu_seconds)
+        cpu = cpu_baseline(w, q, k, v, args.cpu_seconds, hbm_bound)
 
-    launch = fa.fa_launch_info(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, w.causal, dcode)[1]
+    if path == "splitkv":
+        launch = {"entry": "fa_fwd_splitkv", "num_splits": splits, "keys_per_tile": 32,
+                  "rows_per_wave": 32, "waves_per_block": 8,
+                  "note": "two launches per step: chunk kernel, then combine"}
+    else:
+        launch = fa.fa_launch_info(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, w.causal, dcode)[1]
     line = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(value, 3),
-        "unit": "TFLOP/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -277,8 +315,8 @@ def main():
                    "N_kv": w.Nkv, "d": w.D, "causal": w.causal, "seed": w.seed,
                    "flops_per_step": flops, "launch": launch},
         "pct_of_peak": round(100 * value / peak, 2),
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+        "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak,
+                     "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(w.name), "kernel_ms": round(kernel_ms, 5),
                      "kernel_ms_median": round(median_ms, 5),
                      "kernel_ms_min": round(per_launch[0], 5)},

@@ -637,8 +637,7 @@ struct SplitParams {
   int group;        // G = Hq / Hkv
   int R;            // packed rows per (b, kv head) = G * N_q
   int nrb;          // row blocks per (b, kv head) = ceil(R / 32)
-  int S;            // chunks per row block
-  int tps;          // 32-key tiles per chunk
+  int S;            // chunks per row block (chunk s: tiles s, s+S, s+2S, ...)
   long long items;  // B * Hkv * nrb * S
   long long rows;   // B * Hq * N_q
   float sl2;
@@ -680,26 +679,33 @@ __device__ __forceinline__ void attn_splitkv_body(const SplitParams& p) {
   const int qi_max = one_head ? r_hi % p.Nq : p.Nq - 1;
   const int qi_min = one_head ? r_lo % p.Nq : 0;
 
-  const int c0 = s * p.tps * C::BC;                              // first key of the chunk
-  int c1 = min(p.Nkv, c0 + p.tps * C::BC);                       // one past its last key
+  // Chunk s owns the 32-key tiles s, s + S, s + 2S, ... of the keys any row
+  // of the block may see.  Interleaving (rather than one contiguous range
+  // per chunk) makes the S waves of one head read neighbouring tiles at the
+  // same time, so the memory traffic of all waves stays close to a few
+  // sequential streams instead of thousands of streams with equal address
+  // strides, which collide in the same memory channels.
+  int c1 = p.Nkv;                                                // one past the last key used
   if (CAUSAL) c1 = min(c1, qi_max + 1);
-  const int n_tiles = c1 > c0 ? (c1 - c0 + C::BC - 1) / C::BC : 0;
+  const int t_all = (c1 + C::BC - 1) / C::BC;
+  const int n_tiles = s < t_all ? (t_all - s + p.S - 1) / p.S : 0;
+  auto tile_key0 = [&](int t) { return (s + t * p.S) * C::BC; };
 
   const size_t kvhead = (size_t)(b * p.Hkv + g) * p.Nkv;
   const rsrc_t rk = make_rsrc(static_cast<const uint16_t*>(p.k) + kvhead * D, (uint32_t)p.Nkv * C::ROWB);
   const rsrc_t rv = make_rsrc(static_cast<const uint16_t*>(p.v) + kvhead * D, (uint32_t)p.Nkv * C::ROWB);
 
-  // K fragments of tile t: lane (l32, half) holds key c0 + 32t + l32, dims
+  // K fragments of tile t: lane (l32, half) holds key tile_key0(t) + l32, dims
   // cd*16 + half*8 .. +7 (rows past N_kv read as zeros).
   auto load_k = [&](int t, u32x4 (&kr)[C::KPT]) {
-    const int off = (c0 + t * C::BC + l32) * C::ROWB + half * 16;
+    const int off = (tile_key0(t) + l32) * C::ROWB + half * 16;
 #pragma unroll
     for (int cd = 0; cd < C::KPT; ++cd)
       kr[cd] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, off + cd * 32, 0, 0));
   };
   // DMA of the V rows of tile t into this wave's part of ring stage S.
   auto issue_v = [&]<int S>(int t) {
-    const int kv0 = c0 + t * C::BC;
+    const int kv0 = tile_key0(t);
 #pragma unroll
     for (int u = 0; u < C::VPT; ++u) {
       const int slot = u * 64 + lane;
@@ -758,7 +764,7 @@ __device__ __forceinline__ void attn_splitkv_body(const SplitParams& p) {
     f32x16 sc = f32x16{};
 #pragma unroll
     for (int cd = 0; cd < D / 16; ++cd) sc = M::mma(kc[cd], qreg[cd], sc);
-    const int kv0 = c0 + t * C::BC;
+    const int kv0 = tile_key0(t);
     const bool need_mask = (kv0 + C::BC > c1) || (CAUSAL && kv0 + C::BC - 1 > qi_min);
     if (need_mask) {
 #pragma unroll
@@ -848,32 +854,62 @@ attn_splitkv_mfma16(SplitParams p) {
 }
 
 // Merge of the chunk results of every row: lse = ln sum_s exp(lse_s) and
-// O = sum_s exp(lse_s - lse) O_s, rounded once to the output type.  D/4
-// lanes share a row, each with 4 consecutive head dimensions.
+// O = sum_s exp(lse_s - lse) O_s, rounded once to the output type.  One
+// workgroup per row: the chunk weights are formed in parallel, then G groups
+// of D/4 threads (4 head dimensions each) sum a strided subset of the chunks
+// with independent loads, and LDS adds the G partial sums.
 template <typename T, int D>
 __global__ void __launch_bounds__(256) attn_splitkv_combine(const float* __restrict__ ows,
                                                              const float* __restrict__ lws,
                                                              T* __restrict__ o, float* __restrict__ lse,
                                                              long long rows, int S) {
-  constexpr int LPR = D / 4;             // lanes per row
-  const long long row = ((long long)blockIdx.x * 256 + threadIdx.x) / LPR;
-  const int part = threadIdx.x % LPR;
-  if (row >= rows) return;
-  float mx = -INFINITY;
-  for (int s = 0; s < S; ++s) mx = fmaxf(mx, lws[(size_t)s * rows + row]);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float ls = lws[(size_t)s * rows + row];
-    if (ls == -INFINITY) continue;
-    const float w = fast_exp2((ls - mx) * kLog2e);
-    wsum += w;
-    acc += w * *reinterpret_cast<const f32x4*>(ows + ((size_t)s * rows + row) * D + part * 4);
+  constexpr int LPR = D / 4;            // threads per dimension sweep
+  constexpr int G = 256 / LPR;          // chunk groups
+  __shared__ float w_s[FA_SPLITKV_MAX_SPLITS];
+  __shared__ float red[256];
+  __shared__ f32x4 part[G][LPR];
+  const long long row = blockIdx.x;
+  const int tid = threadIdx.x;
+
+  // Largest chunk lse (S <= 256: one value per thread).
+  const float lv = tid < S ? lws[(size_t)tid * rows + row] : -INFINITY;
+  red[tid] = lv;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+    __syncthreads();
   }
-  const float inv = 1.f / wsum;
-  T out4[4] = {(T)(acc[0] * inv), (T)(acc[1] * inv), (T)(acc[2] * inv), (T)(acc[3] * inv)};
-  *reinterpret_cast<u32x2*>(o + row * D + part * 4) = __builtin_bit_cast(u32x2, out4);
-  if (part == 0) lse[row] = mx + fast_log2(wsum) * kLn2;
+  const float mx = red[0];
+  __syncthreads();
+  // Weights exp(lse_s - max); empty chunks (lse_s = -inf) get 0.
+  const float wv = (tid < S && lv != -INFINITY) ? fast_exp2((lv - mx) * kLog2e) : 0.f;
+  if (tid < S) w_s[tid] = wv;
+  red[tid] = wv;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
+  }
+  const float wsum = red[0];
+
+  const int c = tid % LPR, grp = tid / LPR;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int s = grp; s < S; s += G) {
+    const float w = w_s[s];
+    if (w != 0.f) acc += w * *reinterpret_cast<const f32x4*>(ows + ((size_t)s * rows + row) * D + c * 4);
+  }
+  part[grp][c] = acc;
+  __syncthreads();
+  if (tid < LPR) {
+    f32x4 t = part[0][tid];
+#pragma unroll
+    for (int g2 = 1; g2 < G; ++g2) t += part[g2][tid];
+    const float inv = 1.f / wsum;
+    T out4[4] = {(T)(t[0] * inv), (T)(t[1] * inv), (T)(t[2] * inv), (T)(t[3] * inv)};
+    *reinterpret_cast<u32x2*>(o + row * D + tid * 4) = __builtin_bit_cast(u32x2, out4);
+    if (tid == 0) lse[row] = mx + fast_log2(wsum) * kLn2;
+  }
 }
 
 // ------------------------------------------------------------- fp32 path
@@ -1168,7 +1204,8 @@ int check_split_dims(int B, int Hq, int Hkv, int N_q, int N_kv, int d, int dtype
   if (num_splits < 1 || num_splits > g.n_tiles || num_splits > FA_SPLITKV_MAX_SPLITS)
     return FA_ERR_BAD_DIM;
   const long long items = (long long)B * Hkv * g.nrb * num_splits;
-  if ((items + 3) / 4 > 0x7fffffffLL) return FA_ERR_BAD_DIM;
+  if ((items + 7) / 8 > 0x7fffffffLL) return FA_ERR_BAD_DIM;
+  if ((long long)B * Hq * N_q > 0x7fffffffLL) return FA_ERR_BAD_DIM;   // one combine block per row
   return FA_OK;
 }
 
@@ -1179,8 +1216,7 @@ int run_split(const SplitParams& sp, T* o, float* lse, hipStream_t stream) {
   const long long blocks = (sp.items + C::NW - 1) / C::NW;
   hipLaunchKernelGGL((attn_splitkv_mfma16<T, D, CAUSAL>), dim3((unsigned)blocks), dim3(C::NT), 0,
                      stream, sp);
-  const long long cblocks = (sp.rows * (D / 4) + 255) / 256;
-  hipLaunchKernelGGL((attn_splitkv_combine<T, D>), dim3((unsigned)cblocks), dim3(256), 0, stream,
+  hipLaunchKernelGGL((attn_splitkv_combine<T, D>), dim3((unsigned)sp.rows), dim3(256), 0, stream,
                      sp.ows, sp.lws, o, lse, sp.rows, sp.S);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
@@ -1350,7 +1386,6 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
   sp.R = g.R;
   sp.nrb = g.nrb;
   sp.S = num_splits;
-  sp.tps = (g.n_tiles + num_splits - 1) / num_splits;
   sp.items = (long long)B * Hkv * g.nrb * num_splits;
   if (scale > 0.f) {
     sp.sl2 = scale * kLog2e;

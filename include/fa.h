@@ -120,8 +120,10 @@ int fa_launch_info(int B, int Hq, int Hkv, int N_q, int N_kv, int d, int causal,
  * "FlashAttention: IO-aware attention kernel" (section 3, where the method
  * helps and where it does not; sections 8 and 9) names this decode variant,
  * FlashDecoding: it parallelises over the key/value length to fill the GPU.
- * Here the keys of every (batch, key/value head) are cut into num_splits chunks of
- * ceil(ceil(N_kv / 32) / num_splits) tiles of 32 keys; each chunk yields
+ * Here the keys of every (batch, key/value head) are dealt into num_splits
+ * chunks: with tiles of 32 keys, chunk s holds tiles s, s + num_splits,
+ * s + 2*num_splits, ... (interleaved, so that concurrent chunks read
+ * neighbouring memory); each chunk yields
  * the exact attention of its rows over that chunk alone (output O_s and
  * lse_s); a second launch merges them with the block merge rule of the
  * omica exam notes (section 2.3), written for normalised partials:

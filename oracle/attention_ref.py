@@ -148,31 +148,31 @@ def attention_fp64(q, k, v, scale: float, causal: bool = False,
     return o, lse
 
 
-def attention_fp64_key_range(q, k, v, scale: float, causal: bool, lo: int, hi: int):
-    """Exact attention of every row over its allowed keys that lie in [lo, hi).
+def attention_fp64_keys(q, k, v, scale: float, causal: bool, keys):
+    """Exact attention of every row over its allowed keys that belong to ``keys``.
 
     The same definition as ``attention_fp64`` with the key set J_i replaced by
-    J_i intersected with [lo, hi) (causal masking keeps absolute indices).  A
-    row whose restricted key set is empty has no softmax; it gets O = 0 and
-    lse = -inf, the values that contribute nothing to the block merge rule
-    ([P2] §二.3).  This is the partial result one split-KV chunk stands for.
-    Plain and unthreaded: meant for small cases.
+    J_i intersected with the given key indices (causal masking keeps absolute
+    indices).  A row whose restricted key set is empty has no softmax; it gets
+    O = 0 and lse = -inf, the values that contribute nothing to the block
+    merge rule ([P2] §二.3).  This is the partial result one split-KV chunk
+    stands for.  Plain and unthreaded: meant for small cases.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     B, Hq, Hkv, Nq, Nkv, D = _check_shapes(q, k, v)
     sigma = _sigma(scale)
-    lo, hi = max(0, int(lo)), min(Nkv, int(hi))
+    keys = np.unique(np.asarray(keys, dtype=np.int64).reshape(-1))
+    keys = keys[(keys >= 0) & (keys < Nkv)]
     o = np.zeros((B, Hq, Nq, D), dtype=np.float64)
     lse = np.full((B, Hq, Nq), -np.inf, dtype=np.float64)
-    if hi <= lo:
+    if keys.size == 0:
         return o, lse
-    keys = np.arange(lo, hi)
     for b in range(B):
         for h in range(Hq):
             g = kv_head_of(h, Hq, Hkv)
-            s = sigma * (q[b, h] @ k[b, g, lo:hi].T)          # [Nq, hi - lo]
+            s = sigma * (q[b, h] @ k[b, g, keys].T)           # [Nq, len(keys)]
             if causal:
                 s = np.where(keys[None, :] <= np.arange(Nq)[:, None], s, -np.inf)
             for i in range(Nq):
@@ -182,9 +182,14 @@ def attention_fp64_key_range(q, k, v, scale: float, causal: bool, lo: int, hi: i
                 m = row.max()
                 e = np.exp(row - m)
                 l = e.sum()
-                o[b, h, i] = (e / l) @ v[b, g, lo:hi]
+                o[b, h, i] = (e / l) @ v[b, g, keys]
                 lse[b, h, i] = m + np.log(l)
     return o, lse
+
+
+def attention_fp64_key_range(q, k, v, scale: float, causal: bool, lo: int, hi: int):
+    """``attention_fp64_keys`` over the contiguous key range [lo, hi)."""
+    return attention_fp64_keys(q, k, v, scale, causal, np.arange(max(0, int(lo)), int(hi)))
 
 
 def probabilities_fp64(q, k, scale: float, causal: bool = False):

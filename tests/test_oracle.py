@@ -19,7 +19,8 @@ import torch
 from scipy.special import logsumexp, softmax
 
 from oracle import (attention_bruteforce, attention_fp64, attention_fp64_key_range,
-                    attention_online_blocked, probabilities_fp64, kv_head_of)
+                    attention_fp64_keys, attention_online_blocked, probabilities_fp64,
+                    kv_head_of)
 import workloads
 
 pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
@@ -326,6 +327,30 @@ def test_key_range_chunks_merge_to_full(causal, cuts):
     o = sum(wi[..., None] * po for wi, (po, _) in zip(w, parts)) / l_sum[..., None]
     assert np.max(np.abs(o - full_o)) <= 1e-13
     assert np.max(np.abs(m + np.log(l_sum) - full_l)) <= 1e-13
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("S", [1, 3, 4])
+def test_interleaved_tile_chunks_merge_to_full(causal, S):
+    """Chunks dealt tile by tile (chunk s: tiles s, s+S, ... of 8 keys) merge to the full result."""
+    q, k, v = _rand(1, 4, 2, 30, 75, 8, seed=37)
+    full_o, full_l = attention_fp64(q, k, v, 0.6, causal)
+    tiles = np.arange(75) // 8
+    parts = [attention_fp64_keys(q, k, v, 0.6, causal, np.nonzero(tiles % S == s)[0])
+             for s in range(S)]
+    m = np.max(np.stack([pl for _, pl in parts]), axis=0)
+    w = [np.exp(pl - m) for _, pl in parts]
+    l_sum = sum(w)
+    o = sum(wi[..., None] * po for wi, (po, _) in zip(w, parts)) / l_sum[..., None]
+    assert np.max(np.abs(o - full_o)) <= 1e-13
+    assert np.max(np.abs(m + np.log(l_sum) - full_l)) <= 1e-13
+
+
+def test_key_set_order_and_duplicates_do_not_matter():
+    q, k, v = _rand(1, 2, 1, 6, 20, 4, seed=41)
+    a = attention_fp64_keys(q, k, v, 0.9, True, [3, 1, 7, 7, 12])
+    b = attention_fp64_keys(q, k, v, 0.9, True, [1, 3, 7, 12])
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
 def test_key_range_whole_range_equals_full():
