@@ -14,6 +14,7 @@ routine and pure-Python brute force (tests/test_oracle.py).
 from .attention_ref import (  # noqa: F401
     attention_fp64,
     attention_fp64_keys,
+    attention_bwd_fp64,
     attention_fp64_key_range,
     attention_bruteforce,
     attention_online_blocked,

@@ -192,6 +192,50 @@ def attention_fp64_key_range(q, k, v, scale: float, causal: bool, lo: int, hi: i
     return attention_fp64_keys(q, k, v, scale, causal, np.arange(max(0, int(lo)), int(hi)))
 
 
+def attention_bwd_fp64(q, k, v, do, scale: float, causal: bool = False):
+    """Gradients of the attention output, by definition, in float64.
+
+    The pages give the backward pass as recomputation: the forward keeps O
+    and the row statistics, and the backward forms S and P again from Q, K
+    and those statistics instead of storing them ([P3] "Flash Attention
+    Backward"; [P2] §二.5, §四.4).  The gradients themselves are the plain
+    calculus of O = softmax(S) V with S = sigma Q K^T (masked keys have
+    P = 0), for the scalar L = sum(O * dO):
+
+        dV = P^T dO,   dP = dO V^T,   dS = P * (dP - rowsum(P * dP)),
+        dQ = sigma dS K,   dK = sigma dS^T Q.
+
+    Here P is formed whole from S (safe softmax), not from saved statistics.
+    With grouped heads, dK and dV of a key/value head sum the contributions
+    of every query head that reads it.  Returns (dq, dk, dv) in float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, Hq, Hkv, Nq, Nkv, D = _check_shapes(q, k, v)
+    if do.shape != q.shape:
+        raise ValueError("dO must have the shape of Q")
+    sigma = _sigma(scale)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            s = sigma * (q[b, h] @ k[b, g].T)                  # [Nq, Nkv]
+            if causal:
+                s = np.where(np.arange(Nkv)[None, :] <= np.arange(Nq)[:, None], s, -np.inf)
+            e = np.exp(s - s.max(axis=1, keepdims=True))
+            p = e / e.sum(axis=1, keepdims=True)               # P
+            dv[b, g] += p.T @ do[b, h]                         # dV = P^T dO
+            dp = do[b, h] @ v[b, g].T                          # dP = dO V^T
+            ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+            dq[b, h] = sigma * (ds @ k[b, g])                  # dQ = sigma dS K
+            dk[b, g] += sigma * (ds.T @ q[b, h])               # dK = sigma dS^T Q
+    return dq, dk, dv
+
+
 def probabilities_fp64(q, k, scale: float, causal: bool = False):
     """Full probability tensor P [B, Hq, Nq, Nkv] (masked entries are 0).
 

@@ -18,9 +18,9 @@ import pytest
 import torch
 from scipy.special import logsumexp, softmax
 
-from oracle import (attention_bruteforce, attention_fp64, attention_fp64_key_range,
-                    attention_fp64_keys, attention_online_blocked, probabilities_fp64,
-                    kv_head_of)
+from oracle import (attention_bruteforce, attention_bwd_fp64, attention_fp64,
+                    attention_fp64_key_range, attention_fp64_keys, attention_online_blocked,
+                    probabilities_fp64, kv_head_of)
 import workloads
 
 pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
@@ -371,3 +371,68 @@ def test_key_range_empty_rows_and_single_key():
     o, l = attention_fp64_key_range(q, k, v, 0.5, False, 3, 4)
     assert np.allclose(o[0, 0], np.broadcast_to(v[0, 0, 3], (10, 4)), rtol=0, atol=1e-15)
     assert np.allclose(l[0, 0], 0.5 * q[0, 0] @ k[0, 0, 3], rtol=0, atol=1e-14)
+
+
+# ---- backward (gradients of L = sum(O * dO)) --------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_matches_central_differences(causal):
+    """Every entry of dQ, dK, dV against a central difference of L = sum(O * dO)."""
+    q, k, v = _rand(1, 2, 1, 5, 7, 3, seed=43)
+    do = np.random.default_rng(44).standard_normal(q.shape)
+    scale = 0.7
+    dq, dk, dv = attention_bwd_fp64(q, k, v, do, scale, causal)
+
+    def loss(q_, k_, v_):
+        return float(np.sum(attention_fp64(q_, k_, v_, scale, causal)[0] * do))
+
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = {"q": q, "k": k, "v": v}
+            args_m = dict(args_p)
+            args_p[name], args_m[name] = xp, xm
+            num[idx] = (loss(**{a + "_": b for a, b in args_p.items()}) -
+                        loss(**{a + "_": b for a, b in args_m.items()})) / (2 * h)
+        assert np.max(np.abs(num - g)) <= 1e-7 * max(1.0, np.max(np.abs(g))), name
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_matches_torch_autograd_float64(causal):
+    """dQ, dK, dV against torch's float64 autograd of its own attention routine
+    (K/V repeated over the query heads of a group, gradients summed back)."""
+    B, Hq, Hkv, N, D = 2, 6, 2, 17, 8
+    q, k, v = _rand(B, Hq, Hkv, N, N, D, seed=47)
+    do = np.random.default_rng(48).standard_normal(q.shape)
+    scale = float(np.float32(0.35))          # the fp32 value both sides use
+    dq, dk, dv = attention_bwd_fp64(q, k, v, do, scale, causal)
+    tq = torch.tensor(q, requires_grad=True)
+    tk = torch.tensor(k, requires_grad=True)
+    tv = torch.tensor(v, requires_grad=True)
+    g = Hq // Hkv
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk.repeat_interleave(g, dim=1), tv.repeat_interleave(g, dim=1),
+        is_causal=causal, scale=scale)
+    o.backward(torch.tensor(do))
+    assert np.max(np.abs(tq.grad.numpy() - dq)) <= 1e-12
+    assert np.max(np.abs(tk.grad.numpy() - dk)) <= 1e-12
+    assert np.max(np.abs(tv.grad.numpy() - dv)) <= 1e-12
+
+
+def test_backward_closed_forms():
+    """One key: O = v0 for every row, so dV0 = sum of dO rows and dQ = dK = 0."""
+    q, k, v = _rand(1, 1, 1, 4, 1, 5, seed=53)
+    do = np.random.default_rng(54).standard_normal(q.shape)
+    dq, dk, dv = attention_bwd_fp64(q, k, v, do, 0.9, False)
+    assert np.allclose(dv[0, 0, 0], do[0, 0].sum(axis=0), rtol=0, atol=1e-14)
+    assert np.max(np.abs(dq)) <= 1e-15 and np.max(np.abs(dk)) <= 1e-15
+    # scale 0: P uniform, dV = (1/N) * column sums of dO for every key, dQ = dK = 0
+    q, k, v = _rand(1, 1, 1, 3, 4, 2, seed=55)
+    do = np.random.default_rng(56).standard_normal(q.shape)
+    dq, dk, dv = attention_bwd_fp64(q, k, v, do, 0.0, False)
+    assert np.allclose(dv[0, 0], np.broadcast_to(do[0, 0].sum(axis=0) / 4, (4, 2)), atol=1e-14)
+    assert np.max(np.abs(dq)) == 0 and np.max(np.abs(dk)) == 0
