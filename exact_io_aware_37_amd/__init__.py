@@ -79,6 +79,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_splitkv_default_splits.restype = _I
     lib.fa_fwd_splitkv.argtypes = list(_FWD_ARGS) + [_I, _VP, ctypes.c_size_t, _VP]
     lib.fa_fwd_splitkv.restype = _I
+    lib.fa_bwd_workspace_bytes.argtypes = [_I] * 3
+    lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_bwd.argtypes = [_VP] * 9 + [_I] * 6 + [_F, _I, _I, _VP, ctypes.c_size_t, _VP]
+    lib.fa_bwd.restype = _I
     _lib = lib
     return lib
 
@@ -145,6 +149,18 @@ def fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, N_q, N_kv, d, scale, causal, dty
     return load_library().fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq,
                                          Hkv, N_q, N_kv, d, scale, int(causal), dtype,
                                          num_splits, _ptr(workspace), workspace_bytes, s)
+
+
+def fa_bwd_workspace_bytes(B, Hq, N_q) -> int:
+    return load_library().fa_bwd_workspace_bytes(B, Hq, N_q)
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N_q, N_kv, d, scale, causal, dtype,
+           workspace, workspace_bytes, stream) -> int:
+    s = stream if (stream is None or isinstance(stream, int)) else stream.cuda_stream
+    return load_library().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                 _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, N_q, N_kv, d, scale,
+                                 int(causal), dtype, _ptr(workspace), workspace_bytes, s)
 
 
 def dtype_code(torch_dtype) -> int:
@@ -231,7 +247,38 @@ def attention_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
     return out, lse
 
 
+def attention_backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
+                       workspace=None, dq=None, dk=None, dv=None, stream=None):
+    """(dq, dk, dv): gradients of sum(o * dout) for o, lse = attention(q, k, v, causal, scale).
+
+    ``o`` and ``lse`` are the forward's outputs.  ``workspace`` (at least
+    fa_bwd_workspace_bytes bytes) may be given to reuse memory.
+    """
+    import torch
+    B, Hq, Hkv, Nq, Nkv, d = _check_tensors(q, k, v)
+    for name, t in (("o", o), ("dout", dout)):
+        if not t.is_cuda or tuple(t.shape) != tuple(q.shape) or t.dtype != q.dtype or \
+                not t.is_contiguous():
+            raise FAError(FA_ERR_BAD_DIM, f"{name} must be a contiguous GPU tensor like q")
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    need = fa_bwd_workspace_bytes(B, Hq, Nq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, d, float(scale), causal,
+                dtype_code(q.dtype), workspace, workspace.numel() * workspace.element_size(), stream)
+    if st != FA_OK:
+        raise FAError(st, fa_status_string(st))
+    return dq, dk, dv
+
+
 __all__ = ["fa_fwd", "fa_fwd_stream", "fa_check_args", "fa_status_string", "fa_launch_info",
            "fa_splitkv_workspace_bytes", "fa_splitkv_default_splits", "fa_fwd_splitkv",
-           "attention", "attention_splitkv", "load_library", "header_functions", "FAError", "dtype_code",
+           "fa_bwd_workspace_bytes", "fa_bwd",
+           "attention", "attention_splitkv", "attention_backward", "load_library", "header_functions", "FAError", "dtype_code",
            "FA_F32", "FA_F16", "FA_BF16"]

@@ -177,6 +177,11 @@ struct Mma16<__bf16> {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair),
                                            __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
   }
+  // acc + a.lo * b.lo + a.hi * b.hi of two packed pairs, in fp32.
+  __device__ static __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), acc, false);
+  }
 };
 
 template <>
@@ -192,6 +197,10 @@ struct Mma16<_Float16> {
   __device__ static __forceinline__ float sum2(uint32_t pair, float acc) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair),
                                   __builtin_bit_cast(f16x2, 0x3c003c00u), acc, false);
+  }
+  __device__ static __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), acc,
+                                  false);
   }
 };
 
@@ -912,6 +921,486 @@ __global__ void __launch_bounds__(256) attn_splitkv_combine(const float* __restr
   }
 }
 
+// ------------------------------------------------------ backward (16-bit)
+//
+// Recomputation, as the kyonqi walkthrough ("Flash Attention Backward") and
+// the omica exam notes (section 2.5) describe it: the forward keeps O and one
+// statistic per row (lse), and the backward forms S and P again tile by tile
+// from Q, K and lse, P = exp(scale * q.k - lse), never storing either.  The
+// gradients are those of O = softmax(S) V for the scalar sum(O * dO):
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  D = rowsum(dO * O),
+//   dQ = scale dS K,  dK = scale dS^T Q,
+// with dK, dV of a key/value head summed over its query heads.  Three
+// launches: a row pass writing (lse * log2 e, D) per query row to the
+// workspace, a key-stationary pass for dK and dV, and a query-stationary pass
+// for dQ.  Every output element is written once by one wave (no atomics), so
+// the result is deterministic.
+//
+// Tiles live in LDS with the K swizzle (16-byte chunk index XOR a row
+// function); the same layout serves both operand reads, the 16-byte row
+// reads and the transposed ds_read_b64_tr_b16 reads.
+
+// Transposed-read lane base for rows vrow and vrow + 8 of a 16-row group
+// stored with swz_k; the head-dimension block db is applied as "^ (db * 64)".
+template <int D>
+__device__ __forceinline__ int tr_base_k(int lane, int hi) {
+  constexpr int ROWB = D * 2;
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const int row = (g16 >> 1) * 4 + (s16 >> 2) + 8 * hi;
+  const int c = (g16 & 1) * 2 + ((s16 & 3) >> 1);
+  return row * ROWB + ((c ^ swz_k<D>(row)) * 16) + (s16 & 1) * 8;
+}
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float2* stats;    // [B*Hq*N_q]: (lse * log2 e, rowsum(dO * O))
+  int B, Hq, Hkv, Nq, Nkv;
+  int group;
+  float scale;      // as given (any finite value)
+  float sl2;        // scale * log2 e (sign kept)
+  int n_tiles;      // workgroup tiles along the stationary axis
+};
+
+// Row pass: stats[row] = (lse * log2 e, sum_d dO[row][d] * O[row][d]).
+template <typename T, int D>
+__global__ void __launch_bounds__(256) attn_bwd_prep(BwdParams p, long long rows) {
+  constexpr int LPR = D / 8;               // lanes per row, 8 elements each
+  const long long row = ((long long)blockIdx.x * 256 + threadIdx.x) / LPR;
+  const int part = threadIdx.x % LPR;
+  const bool ok = row < rows;
+  const long long r = ok ? row : 0;
+  float acc = 0.f;
+  if (ok) {
+    const u32x4 a = *(reinterpret_cast<const u32x4*>(static_cast<const T*>(p.dout) + r * D) + part);
+    const u32x4 b = *(reinterpret_cast<const u32x4*>(static_cast<const T*>(p.o) + r * D) + part);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = Mma16<T>::dot2(a[i], b[i], acc);
+  }
+#pragma unroll
+  for (int w = LPR / 2; w > 0; w >>= 1) acc += __shfl_xor(acc, w);
+  if (ok && part == 0) p.stats[r] = make_float2(p.lse[r] * kLog2e, acc);
+}
+
+template <int D>
+struct CfgBwdKV {
+  static constexpr int NW = 8;                  // waves; 32 keys each
+  static constexpr int NT = 64 * NW;
+  static constexpr int BKV = 32 * NW;           // keys per workgroup
+  static constexpr int BQ = 32;                 // query rows per step
+  static constexpr int ROWB = D * 2;
+  static constexpr int NCH = D / 8;
+  static constexpr int QTB = BQ * ROWB;         // one Q (or dO) step tile
+  static constexpr int CH = QTB / 1024;         // 1 KiB DMA chunks per step tile
+  static constexpr int DPW = 2 * CH / NW;       // Q + dO chunks per wave per step
+  static constexpr int VCH = BKV * ROWB / 1024; // V chunks (once)
+  static_assert(DPW >= 1 && DPW * NW == 2 * CH, "DMA split");
+};
+
+template <typename T, int D, bool CAUSAL>
+__device__ __forceinline__ void attn_bwd_dkdv_body(const BwdParams& p) {
+  using C = CfgBwdKV<D>;
+  using M = Mma16<T>;
+  __shared__ __attribute__((aligned(1024))) unsigned char q0s[C::QTB];
+  __shared__ __attribute__((aligned(1024))) unsigned char q1s[C::QTB];
+  __shared__ __attribute__((aligned(1024))) unsigned char o0s[C::QTB];
+  __shared__ __attribute__((aligned(1024))) unsigned char o1s[C::QTB];
+  __shared__ __attribute__((aligned(256))) unsigned char st0[C::BQ * 8];
+  __shared__ __attribute__((aligned(256))) unsigned char st1[C::BQ * 8];
+  __shared__ __attribute__((aligned(1024))) unsigned char vall[C::BKV * C::ROWB];
+  auto qst = [&]<int S>() -> lds_t* { if constexpr ((S & 1) == 0) return (lds_t*)q0s; else return (lds_t*)q1s; };
+  auto ost = [&]<int S>() -> lds_t* { if constexpr ((S & 1) == 0) return (lds_t*)o0s; else return (lds_t*)o1s; };
+  auto sst = [&]<int S>() -> lds_t* { if constexpr ((S & 1) == 0) return (lds_t*)st0; else return (lds_t*)st1; };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+
+  // Work item: (b, kv head, key tile), key tiles fastest.
+  const int kt = blockIdx.x % p.n_tiles;
+  const int bg = blockIdx.x / p.n_tiles;
+  const int g = bg % p.Hkv;
+  const int b = bg / p.Hkv;
+  const int k0 = kt * C::BKV;
+  const int kw0 = k0 + wave * 32;               // this wave's first key
+  const int key = kw0 + l32;                    // this lane's key (column of S)
+
+  const size_t kvhead = (size_t)(b * p.Hkv + g) * p.Nkv;
+  const rsrc_t rk = make_rsrc(static_cast<const uint16_t*>(p.k) + kvhead * D, (uint32_t)p.Nkv * C::ROWB);
+  const rsrc_t rv = make_rsrc(static_cast<const uint16_t*>(p.v) + kvhead * D, (uint32_t)p.Nkv * C::ROWB);
+
+  // V rows of the whole key tile into LDS, once.
+#pragma unroll
+  for (int u = 0; u < C::VCH / C::NW; ++u) {
+    const int ci = wave * (C::VCH / C::NW) + u;
+    const int slot = ci * 64 + lane;
+    const int row = slot / C::NCH;
+    const int c = (slot % C::NCH) ^ swz_k<D>(row);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_t*)vall + ci * 1024, 16,
+                                             (k0 + row) * C::ROWB + c * 16, 0, 0, 0);
+  }
+  // K^T operand of the wave's 32 keys, in registers for the whole pass.
+  u32x4 kreg[D / 16];
+#pragma unroll
+  for (int cd = 0; cd < D / 16; ++cd)
+    kreg[cd] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             rk, key * C::ROWB + cd * 32 + half * 16, 0, 0));
+
+  // Query steps: every query head of the group, query rows from the first
+  // one that can see this key tile (causal) to N_q.
+  const int qs0 = CAUSAL ? k0 / C::BQ : 0;
+  const int nqs = (p.Nq + C::BQ - 1) / C::BQ;
+  const int per_head = nqs > qs0 ? nqs - qs0 : 0;
+  const int n_steps = per_head * p.group;
+
+  // DMA of step t (Q, dO rows and their stats) into ring stage S.
+  auto issue = [&]<int S>(int t) {
+    const int hl = t / per_head;
+    const int qs = qs0 + (t - hl * per_head);
+    const int hq = g * p.group + hl;
+    const size_t qhead = (size_t)(b * p.Hq + hq) * p.Nq;
+    const int q0 = qs * C::BQ;
+    const rsrc_t rq = make_rsrc(static_cast<const uint16_t*>(p.q) + qhead * D, (uint32_t)p.Nq * C::ROWB);
+    const rsrc_t ro = make_rsrc(static_cast<const uint16_t*>(p.dout) + qhead * D, (uint32_t)p.Nq * C::ROWB);
+#pragma unroll
+    for (int u = 0; u < C::DPW; ++u) {
+      const int i = wave * C::DPW + u;
+      const bool isd = i >= C::CH;
+      const int ci = isd ? i - C::CH : i;
+      const int slot = ci * 64 + lane;
+      const int row = slot / C::NCH;
+      const int c = (slot % C::NCH) ^ swz_k<D>(row);
+      lds_t* dst = (isd ? ost.template operator()<S>() : qst.template operator()<S>()) + ci * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isd ? ro : rq, dst, 16, (q0 + row) * C::ROWB + c * 16,
+                                               0, 0, 0);
+    }
+    if (wave == 0) {
+      const rsrc_t rs = make_rsrc(p.stats + qhead, (uint32_t)p.Nq * 8u);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, sst.template operator()<S>(), 4, q0 * 8 + lane * 4,
+                                               0, 0, 0);
+    }
+  };
+  // End of a step: the next step's transfers (the last ones this wave
+  // issued) have landed, and every wave is done with the current stage.
+  auto wait_step = [&]() {
+    wait_vm_lgkm<0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  if (n_steps > 0) issue.template operator()<0>(0);
+  wait_vm_lgkm<0>();   // V, K registers (and step 0) complete for this wave
+  __builtin_amdgcn_s_barrier();
+
+  const int kbase = l32 * C::ROWB + ((half ^ (swz_k<D>(l32) & 1)) * 16) + ((swz_k<D>(l32) >> 1) * 32);
+  const int tb0 = tr_base_k<D>(lane, 0), tb1 = tr_base_k<D>(lane, 1);
+
+  f32x16 adv[D / 32], adk[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) {
+    adv[i] = f32x16{};
+    adk[i] = f32x16{};
+  }
+
+  auto step = [&]<int S>(int t) {
+    const bool more = t + 1 < n_steps;
+    if (more) issue.template operator()<S ^ 1>(t + 1);
+    const int hl = t / per_head;
+    const int q0 = (qs0 + (t - hl * per_head)) * C::BQ;
+    const lds_t* qs = qst.template operator()<S>();
+    const lds_t* os = ost.template operator()<S>();
+    const lds_t* ss = sst.template operator()<S>();
+    int kb = kbase, vb = wave * 32 * C::ROWB + kbase, t0 = tb0, t1 = tb1;
+    asm volatile("" : "+v"(kb), "+v"(vb), "+v"(t0), "+v"(t1));
+    // S = Q K^T and dP = dO V^T: one query per register row, this lane's key.
+    f32x16 sc = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int cd = 0; cd < D / 16; ++cd) {
+      const u32x4 a = *(const u32x4 __attribute__((address_space(3)))*)(qs + (kb ^ (cd * 32)));
+      sc = M::mma(a, kreg[cd], sc);
+    }
+#pragma unroll
+    for (int cd = 0; cd < D / 16; ++cd) {
+      const u32x4 a = *(const u32x4 __attribute__((address_space(3)))*)(os + (kb ^ (cd * 32)));
+      const u32x4 bv = *(const u32x4 __attribute__((address_space(3)))*)((const lds_t*)vall + (vb ^ (cd * 32)));
+      dp = M::mma(a, bv, dp);
+    }
+    // P and dS; register e holds query q0 + (e/4)*8 + half*4 + e%4.
+    u32x4 pk[2], dk2[2];
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4 s01 = *(const f32x4 __attribute__((address_space(3)))*)(ss + (g4 * 8 + half * 4) * 8);
+      const f32x4 s23 = *(const f32x4 __attribute__((address_space(3)))*)(ss + (g4 * 8 + half * 4) * 8 + 16);
+      const float l2v[4] = {s01[0], s01[2], s23[0], s23[2]};
+      const float dv4[4] = {s01[1], s01[3], s23[1], s23[3]};
+      float pe[4], de[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = g4 * 4 + j;
+        float x = fast_exp2(fmaf(sc[e], p.sl2, -l2v[j]));
+        if (CAUSAL && key > q0 + g4 * 8 + half * 4 + j) x = 0.f;
+        pe[j] = x;
+        de[j] = x * (dp[e] - dv4[j]);
+      }
+      const int cc = g4 >> 1, w0 = (g4 & 1) * 2;
+      pk[cc][w0] = M::pack(pe[0], pe[1]);
+      pk[cc][w0 + 1] = M::pack(pe[2], pe[3]);
+      dk2[cc][w0] = M::pack(de[0], de[1]);
+      dk2[cc][w0 + 1] = M::pack(de[2], de[3]);
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS (transposed operand reads).
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int off = cc * 16 * C::ROWB;
+        const s16x4 olo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(os + (t0 ^ (db * 64)) + off));
+        const s16x4 ohi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(os + (t1 ^ (db * 64)) + off));
+        const s16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(qs + (t0 ^ (db * 64)) + off));
+        const s16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(qs + (t1 ^ (db * 64)) + off));
+        const u32x2 a0 = __builtin_bit_cast(u32x2, olo), a1 = __builtin_bit_cast(u32x2, ohi);
+        const u32x2 b0 = __builtin_bit_cast(u32x2, qlo), b1 = __builtin_bit_cast(u32x2, qhi);
+        adv[db] = M::mma(u32x4{a0[0], a0[1], a1[0], a1[1]}, pk[cc], adv[db]);
+        adk[db] = M::mma(u32x4{b0[0], b0[1], b1[0], b1[1]}, dk2[cc], adk[db]);
+      }
+    }
+    wait_step();
+  };
+  int t = 0;
+  for (; t + 1 < n_steps; t += 2) {
+    step.template operator()<0>(t);
+    step.template operator()<1>(t + 1);
+  }
+  if (t < n_steps) step.template operator()<0>(t);
+
+  // dV and dK rows of this lane's key: 4 consecutive dims per store.
+  const rsrc_t rdk = make_rsrc(static_cast<uint16_t*>(p.dk) + kvhead * D, (uint32_t)p.Nkv * C::ROWB);
+  const rsrc_t rdv = make_rsrc(static_cast<uint16_t*>(p.dv) + kvhead * D, (uint32_t)p.Nkv * C::ROWB);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int off = (key * D + db * 32 + g4 * 8 + half * 4) * 2;
+      u32x2 w;
+      w[0] = M::pack(adv[db][4 * g4], adv[db][4 * g4 + 1]);
+      w[1] = M::pack(adv[db][4 * g4 + 2], adv[db][4 * g4 + 3]);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, w), rdv, off, 0, 0);
+      w[0] = M::pack(adk[db][4 * g4] * p.scale, adk[db][4 * g4 + 1] * p.scale);
+      w[1] = M::pack(adk[db][4 * g4 + 2] * p.scale, adk[db][4 * g4 + 3] * p.scale);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, w), rdk, off, 0, 0);
+    }
+  }
+}
+
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(CfgBwdKV<D>::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_bwd_dkdv(BwdParams p) {
+  attn_bwd_dkdv_body<T, D, CAUSAL>(p);
+}
+
+template <int D>
+struct CfgBwdQ {
+  static constexpr int NW = 8;                  // waves; 32 query rows each
+  static constexpr int NT = 64 * NW;
+  static constexpr int BR = 32 * NW;            // query rows per workgroup
+  static constexpr int BC = 32;                 // keys per tile
+  static constexpr int ROWB = D * 2;
+  static constexpr int NCH = D / 8;
+  static constexpr int TILEB = BC * ROWB;
+  static constexpr int CH = TILEB / 1024;       // chunks per K (or V) tile
+  static constexpr int DPW = 2 * CH / NW;
+  static_assert(DPW >= 1 && DPW * NW == 2 * CH, "DMA split");
+};
+
+template <typename T, int D, bool CAUSAL>
+__device__ __forceinline__ void attn_bwd_dq_body(const BwdParams& p) {
+  using C = CfgBwdQ<D>;
+  using M = Mma16<T>;
+  __shared__ __attribute__((aligned(1024))) unsigned char k0s[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char k1s[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char k2s[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char k3s[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char v0s[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char v1s[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char v2s[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char v3s[C::TILEB];
+  auto kst = [&]<int S>() -> lds_t* {
+    if constexpr ((S & 3) == 0) return (lds_t*)k0s;
+    else if constexpr ((S & 3) == 1) return (lds_t*)k1s;
+    else if constexpr ((S & 3) == 2) return (lds_t*)k2s;
+    else return (lds_t*)k3s;
+  };
+  auto vst = [&]<int S>() -> lds_t* {
+    if constexpr ((S & 3) == 0) return (lds_t*)v0s;
+    else if constexpr ((S & 3) == 1) return (lds_t*)v1s;
+    else if constexpr ((S & 3) == 2) return (lds_t*)v2s;
+    else return (lds_t*)v3s;
+  };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int qt = blockIdx.x % p.n_tiles;
+  const int bh = blockIdx.x / p.n_tiles;
+  const int hq = bh % p.Hq;
+  const int b = bh / p.Hq;
+  const int hkv = hq / p.group;
+  const int q0 = qt * C::BR;
+  const int qw0 = q0 + wave * 32;
+  const int myq = qw0 + l32;
+
+  const size_t qhead = (size_t)(b * p.Hq + hq) * p.Nq;
+  const size_t kvhead = (size_t)(b * p.Hkv + hkv) * p.Nkv;
+  const rsrc_t rq = make_rsrc(static_cast<const uint16_t*>(p.q) + qhead * D, (uint32_t)p.Nq * C::ROWB);
+  const rsrc_t rdo = make_rsrc(static_cast<const uint16_t*>(p.dout) + qhead * D, (uint32_t)p.Nq * C::ROWB);
+  const rsrc_t rk = make_rsrc(static_cast<const uint16_t*>(p.k) + kvhead * D, (uint32_t)p.Nkv * C::ROWB);
+  const rsrc_t rv = make_rsrc(static_cast<const uint16_t*>(p.v) + kvhead * D, (uint32_t)p.Nkv * C::ROWB);
+
+  const int kv_end = CAUSAL ? min(p.Nkv, q0 + C::BR) : p.Nkv;
+  const int n_tiles = (kv_end + C::BC - 1) / C::BC;
+
+  auto issue = [&]<int S>(int t) {
+    const int kv0 = t * C::BC;
+#pragma unroll
+    for (int u = 0; u < C::DPW; ++u) {
+      const int i = wave * C::DPW + u;
+      const bool isv = i >= C::CH;
+      const int ci = isv ? i - C::CH : i;
+      const int slot = ci * 64 + lane;
+      const int row = slot / C::NCH;
+      const int c = (slot % C::NCH) ^ swz_k<D>(row);
+      lds_t* dst = (isv ? vst.template operator()<S>() : kst.template operator()<S>()) + ci * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? rv : rk, dst, 16, (kv0 + row) * C::ROWB + c * 16,
+                                               0, 0, 0);
+    }
+  };
+  // Tile t landed for every wave; tile t+3 goes into the stage tile t-1 held.
+  auto advance = [&]<int S>(int t) {
+    const int ahead = min(n_tiles - 1 - t, 2);   // groups issued after tile t
+    if (ahead >= 2) wait_vm_lgkm<2 * C::DPW>();
+    else if (ahead == 1) wait_vm_lgkm<C::DPW>();
+    else wait_vm_lgkm<0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (t + 3 < n_tiles) issue.template operator()<S>(t + 3);
+  };
+
+  if (n_tiles > 0) issue.template operator()<0>(0);
+  if (n_tiles > 1) issue.template operator()<1>(1);
+  if (n_tiles > 2) issue.template operator()<2>(2);
+
+  // Q^T and dO^T operands of the wave's 32 rows, and their statistics.
+  u32x4 qreg[D / 16], oreg[D / 16];
+#pragma unroll
+  for (int cd = 0; cd < D / 16; ++cd) {
+    const int off = (myq * D + cd * 16 + half * 8) * 2;
+    qreg[cd] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+    oreg[cd] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rdo, off, 0, 0));
+  }
+  const float2 st = myq < p.Nq ? p.stats[qhead + myq] : make_float2(0.f, 0.f);
+  const float l2v = st.x, dvv = st.y;
+
+  const int kbase = l32 * C::ROWB + ((half ^ (swz_k<D>(l32) & 1)) * 16) + ((swz_k<D>(l32) >> 1) * 32);
+  const int tb0 = tr_base_k<D>(lane, 0), tb1 = tr_base_k<D>(lane, 1);
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
+
+  auto step = [&]<int R>(int t) {
+    advance.template operator()<(R + 3) & 3>(t);
+    const lds_t* ks = kst.template operator()<R>();
+    const lds_t* vs = vst.template operator()<R>();
+    int kb = kbase, t0 = tb0, t1 = tb1;
+    asm volatile("" : "+v"(kb), "+v"(t0), "+v"(t1));
+    // S^T = K Q^T and dP^T = V dO^T: this lane's query, keys in registers.
+    f32x16 sc = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int cd = 0; cd < D / 16; ++cd) {
+      const u32x4 a = *(const u32x4 __attribute__((address_space(3)))*)(ks + (kb ^ (cd * 32)));
+      const u32x4 av = *(const u32x4 __attribute__((address_space(3)))*)(vs + (kb ^ (cd * 32)));
+      sc = M::mma(a, qreg[cd], sc);
+      dp = M::mma(av, oreg[cd], dp);
+    }
+    const int kv0 = t * C::BC;
+    u32x4 dsk[2];
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        float d2[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int e = cc * 8 + 2 * w + j;
+          float x = fast_exp2(fmaf(sc[e], p.sl2, -l2v));
+          const int kk = kv0 + (e >> 2) * 8 + half * 4 + (e & 3);
+          if (CAUSAL && kk > myq) x = 0.f;
+          d2[j] = x * (dp[e] - dvv);
+        }
+        dsk[cc][w] = M::pack(d2[0], d2[1]);
+      }
+    }
+    // dQ^T += K^T dS^T.
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int off = cc * 16 * C::ROWB;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(ks + (t0 ^ (db * 64)) + off));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(ks + (t1 ^ (db * 64)) + off));
+        const u32x2 a0 = __builtin_bit_cast(u32x2, lo), a1 = __builtin_bit_cast(u32x2, hi);
+        acc[db] = M::mma(u32x4{a0[0], a0[1], a1[0], a1[1]}, dsk[cc], acc[db]);
+      }
+    }
+  };
+  int t = 0;
+  for (; t + 4 <= n_tiles; t += 4) {
+    step.template operator()<0>(t);
+    step.template operator()<1>(t + 1);
+    step.template operator()<2>(t + 2);
+    step.template operator()<3>(t + 3);
+  }
+  for (; t < n_tiles; ++t) {
+    switch (t & 3) {
+      case 0: step.template operator()<0>(t); break;
+      case 1: step.template operator()<1>(t); break;
+      case 2: step.template operator()<2>(t); break;
+      default: step.template operator()<3>(t); break;
+    }
+  }
+
+  const rsrc_t rdq = make_rsrc(static_cast<uint16_t*>(p.dq) + qhead * D, (uint32_t)p.Nq * C::ROWB);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      u32x2 w;
+      w[0] = M::pack(acc[db][4 * g4] * p.scale, acc[db][4 * g4 + 1] * p.scale);
+      w[1] = M::pack(acc[db][4 * g4 + 2] * p.scale, acc[db][4 * g4 + 3] * p.scale);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, w), rdq,
+                                            (myq * D + db * 32 + g4 * 8 + half * 4) * 2, 0, 0);
+    }
+  }
+}
+
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(CfgBwdQ<D>::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_bwd_dq(BwdParams p) {
+  attn_bwd_dq_body<T, D, CAUSAL>(p);
+}
+
 // ------------------------------------------------------------- fp32 path
 
 template <int D>
@@ -1235,6 +1724,34 @@ int dispatch_split(const SplitParams& sp, void* o, float* lse, int d, bool causa
   return causal ? run_split<T, 128, true>(sp, ot, lse, s) : run_split<T, 128, false>(sp, ot, lse, s);
 }
 
+template <typename T, int D, bool CAUSAL>
+int run_bwd(BwdParams p, long long rows, hipStream_t stream) {
+  (void)hipGetLastError();
+  const long long pblocks = (rows * (D / 8) + 255) / 256;
+  hipLaunchKernelGGL((attn_bwd_prep<T, D>), dim3((unsigned)pblocks), dim3(256), 0, stream, p, rows);
+  BwdParams pk = p;
+  pk.n_tiles = (p.Nkv + CfgBwdKV<D>::BKV - 1) / CfgBwdKV<D>::BKV;
+  hipLaunchKernelGGL((attn_bwd_dkdv<T, D, CAUSAL>), dim3((unsigned)((long long)p.B * p.Hkv * pk.n_tiles)),
+                     dim3(CfgBwdKV<D>::NT), 0, stream, pk);
+  BwdParams pq = p;
+  pq.n_tiles = (p.Nq + CfgBwdQ<D>::BR - 1) / CfgBwdQ<D>::BR;
+  hipLaunchKernelGGL((attn_bwd_dq<T, D, CAUSAL>), dim3((unsigned)((long long)p.B * p.Hq * pq.n_tiles)),
+                     dim3(CfgBwdQ<D>::NT), 0, stream, pq);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    snprintf(g_hip_error, sizeof g_hip_error, "HIP error: %s (%s)", hipGetErrorName(e),
+             hipGetErrorString(e));
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
+template <typename T>
+int dispatch_bwd(const BwdParams& p, long long rows, int d, bool causal, hipStream_t s) {
+  if (d == 64) return causal ? run_bwd<T, 64, true>(p, rows, s) : run_bwd<T, 64, false>(p, rows, s);
+  return causal ? run_bwd<T, 128, true>(p, rows, s) : run_bwd<T, 128, false>(p, rows, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -1401,6 +1918,69 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
   const bool c = causal != 0;
   if (dtype == FA_BF16) return dispatch_split<__bf16>(sp, o, lse, d, c, s);
   return dispatch_split<_Float16>(sp, o, lse, d, c, s);
+}
+
+size_t fa_bwd_workspace_bytes(int B, int Hq, int N_q) {
+  if (B < 1 || Hq < 1 || N_q < 1) return 0;
+  return (size_t)((unsigned long long)B * Hq * N_q * 8ull);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N_q,
+           int N_kv, int d, float scale, int causal, int dtype, void* workspace,
+           size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace)
+    return FA_ERR_NULL_PTR;
+  if (dtype == FA_F32) return FA_ERR_DTYPE;
+  int st = check_dims(B, Hq, Hkv, N_q, N_kv, d, dtype, nullptr);
+  if (st != FA_OK) return st;
+  const long long kvtiles = ((long long)N_kv + 255) / 256;
+  if ((long long)B * Hkv * kvtiles > 0x7fffffffLL) return FA_ERR_BAD_DIM;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  const uintptr_t in[6] = {(uintptr_t)q, (uintptr_t)k, (uintptr_t)v, (uintptr_t)o, (uintptr_t)lse,
+                           (uintptr_t)dout};
+  const uintptr_t out[4] = {(uintptr_t)dq, (uintptr_t)dk, (uintptr_t)dv, (uintptr_t)workspace};
+  if (((in[0] | in[1] | in[2] | in[3] | in[5] | out[0] | out[1] | out[2] | out[3]) & 15u) != 0 ||
+      (in[4] & 3u) != 0)
+    return FA_ERR_ALIGN;
+  const size_t es = elem_size(dtype);
+  const size_t nq = (size_t)B * Hq * N_q * d * es;
+  const size_t nkv = (size_t)B * Hkv * N_kv * d * es;
+  const size_t nl = (size_t)B * Hq * N_q * sizeof(float);
+  const size_t nws = fa_bwd_workspace_bytes(B, Hq, N_q);
+  if (workspace_bytes < nws) return FA_ERR_WORKSPACE;
+  const size_t in_n[6] = {nq, nkv, nkv, nq, nl, nq};
+  const size_t out_n[4] = {nq, nkv, nkv, nws};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(out[i], out_n[i], in[j], in_n[j])) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(out[i], out_n[i], out[j], out_n[j])) return FA_ERR_ALIAS;
+  }
+  BwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.dout = dout;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.stats = static_cast<float2*>(workspace);
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Nq = N_q;
+  p.Nkv = N_kv;
+  p.group = Hq / Hkv;
+  p.scale = scale;
+  p.sl2 = scale * kLog2e;
+  p.n_tiles = 0;
+  const long long rows = (long long)B * Hq * N_q;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == FA_BF16) return dispatch_bwd<__bf16>(p, rows, d, causal != 0, s);
+  return dispatch_bwd<_Float16>(p, rows, d, causal != 0, s);
 }
 
 const char* fa_status_string(int status) {

@@ -165,6 +165,42 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    float scale, int causal, int dtype, int num_splits,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Backward pass: gradients of the scalar sum(O * dO) with respect to q, k
+ * and v, for the forward above (same arguments, layouts and masking), by
+ * recomputation as the kyonqi walkthrough ("Flash Attention Backward") and
+ * the omica exam notes (section 2.5) describe it: the forward's o and lse are
+ * inputs, and S and P = exp(scale * q.k - lse) are formed again tile by tile,
+ * never stored.  With D = rowsum(dO * O):
+ *
+ *     dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),
+ *     dQ = scale * dS K,  dK = scale * dS^T Q,
+ *
+ * dK and dV of a key/value head summing over its Hq/Hkv query heads.
+ *
+ * Inputs q, k, v, o, dout (dtype) and lse (fp32) as the forward wrote them;
+ * outputs dq [B,Hq,N_q,d], dk and dv [B,Hkv,N_kv,d] in the same dtype
+ * (products on the matrix cores, fp32 accumulation, P and dS rounded to the
+ * dtype before their products, one rounding of each output).  dtype FA_BF16
+ * or FA_F16 (FA_ERR_DTYPE for FA_F32); d 64 or 128; any finite scale.
+ *
+ * workspace: caller-owned device memory of at least
+ * fa_bwd_workspace_bytes(B, Hq, N_q) bytes (8 per query row: lse * log2(e)
+ * and D in fp32), 16-byte aligned; fully rewritten by every call.
+ * dq, dk, dv and the workspace must not overlap any input or each other
+ * (FA_ERR_ALIAS); pointer alignment as for fa_fwd (FA_ERR_ALIGN).  Three
+ * launches on `stream` (NULL = null stream): the row pass, the dK/dV pass,
+ * the dQ pass.  Every output element is written once, by one wave: the
+ * result is deterministic.  The library allocates nothing.
+ */
+size_t fa_bwd_workspace_bytes(int B, int Hq, int N_q);
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv,
+           int B, int Hq, int Hkv, int N_q, int N_kv, int d,
+           float scale, int causal, int dtype,
+           void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -35,7 +35,8 @@ def test_library_exports_every_declared_symbol(lib):
     names = fa.header_functions()
     assert set(names) == {"fa_fwd", "fa_fwd_stream", "fa_check_args", "fa_status_string",
                           "fa_launch_info", "fa_splitkv_workspace_bytes",
-                          "fa_splitkv_default_splits", "fa_fwd_splitkv"}
+                          "fa_splitkv_default_splits", "fa_fwd_splitkv",
+                          "fa_bwd_workspace_bytes", "fa_bwd"}
     for n in names:
         assert hasattr(lib, n), n
         assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
@@ -198,3 +199,39 @@ def test_splitkv_rejects_on_host(lib):
     assert split(d=96, **good) == fa.FA_ERR_HEAD_DIM
     assert split(Hq=7, **good) == fa.FA_ERR_HEAD_GROUP
     assert split(q=0, **good) == fa.FA_ERR_NULL_PTR
+
+
+# ---- backward entry points ---------------------------------------------------
+
+DO, DQ, DK, DV = 0x70000000, 0x80000000, 0x90000000, 0xA0000000
+
+
+def bwd(q=Q, k=K, v=V, o=O, lse=L, do=DO, dq=DQ, dk=DK, dv=DV, ws=W, ws_bytes=None, **kw):
+    a = args(**kw)
+    if ws_bytes is None:
+        ws_bytes = fa.fa_bwd_workspace_bytes(a["B"], a["Hq"], a["N_q"])
+    # Every case below fails its host checks, so no call reaches HIP.
+    return fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, a["B"], a["Hq"], a["Hkv"], a["N_q"],
+                     a["N_kv"], a["d"], a["scale"], a["causal"], a["dtype"], ws, ws_bytes, None)
+
+
+def test_bwd_workspace_bytes(lib):
+    assert fa.fa_bwd_workspace_bytes(2, 8, 100) == 2 * 8 * 100 * 8
+    assert fa.fa_bwd_workspace_bytes(0, 8, 100) == 0 and fa.fa_bwd_workspace_bytes(1, 1, 0) == 0
+
+
+def test_bwd_rejects_on_host(lib):
+    for name in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv", "ws"):
+        assert bwd(**{name: 0}) == fa.FA_ERR_NULL_PTR, name
+    assert bwd(dtype=fa.FA_F32) == fa.FA_ERR_DTYPE
+    assert bwd(d=96) == fa.FA_ERR_HEAD_DIM
+    assert bwd(Hq=7) == fa.FA_ERR_HEAD_GROUP
+    assert bwd(N_kv=0) == fa.FA_ERR_BAD_DIM
+    assert bwd(scale=math.nan) == fa.FA_ERR_SCALE
+    assert bwd(dq=DQ + 8) == fa.FA_ERR_ALIGN
+    assert bwd(lse=L + 2) == fa.FA_ERR_ALIGN
+    assert bwd(ws_bytes=8) == fa.FA_ERR_WORKSPACE
+    assert bwd(dq=Q) == fa.FA_ERR_ALIAS          # output over an input
+    assert bwd(dk=DO + 64) == fa.FA_ERR_ALIAS
+    assert bwd(dv=DK) == fa.FA_ERR_ALIAS         # outputs over each other
+    assert bwd(ws=DQ + 16) == fa.FA_ERR_ALIAS
