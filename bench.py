@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--path", choices=["auto", "fwd", "splitkv"], default="auto",
                     help="entry point to time: fa_fwd_stream, or fa_fwd_splitkv (auto: split-KV "
                          "for the decoding workload 6, fa_fwd otherwise)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time fa_bwd (gradients of the workload's forward) instead of the forward")
     ap.add_argument("--splits", type=int, default=0,
                     help="split count for the split-KV path (0: fa_splitkv_default_splits)")
     ap.add_argument("--no-context", action="store_true",
@@ -207,6 +209,8 @@ def main():
     fa.load_library()
 
     path = args.path if args.path != "auto" else ("splitkv" if w.index == 6 else "fwd")
+    if args.backward:
+        path = "bwd"
     splits = None
     if path == "splitkv":
         splits = args.splits or fa.fa_splitkv_default_splits(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D,
@@ -217,6 +221,22 @@ def main():
         def step():
             st = fa.fa_fwd_splitkv(qd, kd, vd, o, lse, w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, scale,
                                    w.causal, dcode, splits, workspace, ws_bytes, stream)
+            if st != 0:
+                raise RuntimeError(fa.fa_status_string(st))
+    elif path == "bwd":
+        # The forward's outputs and a seeded dO are inputs of every timed step.
+        st = fa.fa_fwd_stream(qd, kd, vd, o, lse, w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, scale,
+                              w.causal, dcode, stream)
+        if st != 0:
+            raise RuntimeError(fa.fa_status_string(st))
+        dod = workloads.make_inputs(w.B, w.Hq, w.Hq, w.Nq, 1, w.D, w.dtype, w.seed + 100)[0].to(dev)
+        dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+        ws_bytes = fa.fa_bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D)
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+        def step():
+            st = fa.fa_bwd(qd, kd, vd, o, lse, dod, dq, dk, dv, w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D,
+                           scale, w.causal, dcode, workspace, ws_bytes, stream)
             if st != 0:
                 raise RuntimeError(fa.fa_status_string(st))
     else:
@@ -246,7 +266,9 @@ def main():
     median_ms = per_launch[len(per_launch) // 2]
     wall_ms = wall * 1e3 / args.steps
 
-    flops = w.flops()
+    # Backward: the algorithmic count is 2.5x the forward's (dV, dP, dQ, dK and
+    # the recomputed S: 10*N_q*N_kv*d per head, against 4 for the forward).
+    flops = w.flops() * (2.5 if path == "bwd" else 1.0)
     hbm_bound = path == "splitkv"
     if hbm_bound:
         # Decoding reads the whole K/V cache for one query row per head: HBM-bound.
@@ -255,7 +277,8 @@ def main():
     else:
         work, unit, bound = flops / 1e12, "TFLOP/s", "mfma"
         peak = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
-        metric = METRIC
+        metric = METRIC if path != "bwd" else \
+            "attn backward TFLOP/s (2.5x forward FLOPs) and % of MI355X bf16 MFMA peak"
     value = work / (wall_ms * 1e-3)
     achieved = work / (kernel_ms * 1e-3)
     print(f"[bench] {w.name} ({path}): kernel {kernel_ms:.4f} ms/step (events), wall "
@@ -264,7 +287,7 @@ def main():
 
     # Sampled parity of the benchmarked output (a few heads, a few rows each).
     check = None
-    if args.check_rows > 0:
+    if args.check_rows > 0 and path != "bwd":
         from oracle import attention_fp64
         rng = np.random.default_rng(1)
         rows = np.unique(np.concatenate([rng.choice(w.Nq, min(args.check_rows, w.Nq), replace=False),
@@ -285,14 +308,17 @@ def main():
                  "rows_checked": int(len(rows)) * len(errs)}
 
     context = None
-    if not args.no_context and w.dtype != "f32" and not hbm_bound:
+    if not args.no_context and w.dtype != "f32" and not hbm_bound and path == "fwd":
         context = power_context(fa, w, qd, kd, vd, o, lse, scale, stream, dcode)
 
     cpu = None
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and path != "bwd":
         cpu = cpu_baseline(w, q, k, v, args.cpu_seconds, hbm_bound)
 
-    if path == "splitkv":
+    if path == "bwd":
+        launch = {"entry": "fa_bwd", "note": "three launches per step: row pass, dK/dV, dQ",
+                  "keys_per_block_dkdv": 256, "rows_per_block_dq": 256}
+    elif path == "splitkv":
         launch = {"entry": "fa_fwd_splitkv", "num_splits": splits, "keys_per_tile": 32,
                   "rows_per_wave": 32, "waves_per_block": 8,
                   "note": "two launches per step: chunk kernel, then combine"}

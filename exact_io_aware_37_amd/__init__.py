@@ -79,7 +79,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_splitkv_default_splits.restype = _I
     lib.fa_fwd_splitkv.argtypes = list(_FWD_ARGS) + [_I, _VP, ctypes.c_size_t, _VP]
     lib.fa_fwd_splitkv.restype = _I
-    lib.fa_bwd_workspace_bytes.argtypes = [_I] * 3
+    lib.fa_bwd_workspace_bytes.argtypes = [_I] * 6
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_bwd.argtypes = [_VP] * 9 + [_I] * 6 + [_F, _I, _I, _VP, ctypes.c_size_t, _VP]
     lib.fa_bwd.restype = _I
@@ -151,8 +151,8 @@ def fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, N_q, N_kv, d, scale, causal, dty
                                          num_splits, _ptr(workspace), workspace_bytes, s)
 
 
-def fa_bwd_workspace_bytes(B, Hq, N_q) -> int:
-    return load_library().fa_bwd_workspace_bytes(B, Hq, N_q)
+def fa_bwd_workspace_bytes(B, Hq, Hkv, N_q, N_kv, d) -> int:
+    return load_library().fa_bwd_workspace_bytes(B, Hq, Hkv, N_q, N_kv, d)
 
 
 def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N_q, N_kv, d, scale, causal, dtype,
@@ -262,7 +262,7 @@ def attention_backward(q, k, v, o, lse, dout, causal: bool = False, scale: float
             raise FAError(FA_ERR_BAD_DIM, f"{name} must be a contiguous GPU tensor like q")
     if scale is None:
         scale = 1.0 / float(d) ** 0.5
-    need = fa_bwd_workspace_bytes(B, Hq, Nq)
+    need = fa_bwd_workspace_bytes(B, Hq, Hkv, Nq, Nkv, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     dq = torch.empty_like(q) if dq is None else dq

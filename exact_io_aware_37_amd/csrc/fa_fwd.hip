@@ -962,11 +962,13 @@ struct BwdParams {
   void* dk;
   void* dv;
   float2* stats;    // [B*Hq*N_q]: (lse * log2 e, rowsum(dO * O))
+  float* part;      // [hsplit][2][B*Hkv*N_kv*d] fp32 partial dK, dV (hsplit > 1 only)
   int B, Hq, Hkv, Nq, Nkv;
   int group;
   float scale;      // as given (any finite value)
   float sl2;        // scale * log2 e (sign kept)
   int n_tiles;      // workgroup tiles along the stationary axis
+  int hsplit;       // dK/dV pass: query heads of a group dealt over this many workgroups
 };
 
 // Row pass: stats[row] = (lse * log2 e, sum_d dO[row][d] * O[row][d]).
@@ -1025,11 +1027,15 @@ __device__ __forceinline__ void attn_bwd_dkdv_body(const BwdParams& p) {
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
-  // Work item: (b, kv head, key tile), key tiles fastest.
+  // Work item: (b, kv head, head share, key tile), key tiles fastest.  Head
+  // share hs takes the query heads hs, hs + hsplit, ... of the group.
   const int kt = blockIdx.x % p.n_tiles;
-  const int bg = blockIdx.x / p.n_tiles;
+  const int r1 = blockIdx.x / p.n_tiles;
+  const int hs = r1 % p.hsplit;
+  const int bg = r1 / p.hsplit;
   const int g = bg % p.Hkv;
   const int b = bg / p.Hkv;
+  const int n_heads = (p.group - hs + p.hsplit - 1) / p.hsplit;
   const int k0 = kt * C::BKV;
   const int kw0 = k0 + wave * 32;               // this wave's first key
   const int key = kw0 + l32;                    // this lane's key (column of S)
@@ -1060,13 +1066,13 @@ __device__ __forceinline__ void attn_bwd_dkdv_body(const BwdParams& p) {
   const int qs0 = CAUSAL ? k0 / C::BQ : 0;
   const int nqs = (p.Nq + C::BQ - 1) / C::BQ;
   const int per_head = nqs > qs0 ? nqs - qs0 : 0;
-  const int n_steps = per_head * p.group;
+  const int n_steps = per_head * n_heads;
 
   // DMA of step t (Q, dO rows and their stats) into ring stage S.
   auto issue = [&]<int S>(int t) {
     const int hl = t / per_head;
     const int qs = qs0 + (t - hl * per_head);
-    const int hq = g * p.group + hl;
+    const int hq = g * p.group + hs + hl * p.hsplit;
     const size_t qhead = (size_t)(b * p.Hq + hq) * p.Nq;
     const int q0 = qs * C::BQ;
     const rsrc_t rq = make_rsrc(static_cast<const uint16_t*>(p.q) + qhead * D, (uint32_t)p.Nq * C::ROWB);
@@ -1182,6 +1188,26 @@ __device__ __forceinline__ void attn_bwd_dkdv_body(const BwdParams& p) {
   }
   if (t < n_steps) step.template operator()<0>(t);
 
+  if (p.hsplit > 1) {
+    // Partial sums of this head share, fp32, for the reduction pass.
+    if (key < p.Nkv) {
+      const size_t nkvd = (size_t)p.B * p.Hkv * p.Nkv * D;
+      float* pk_ = p.part + (size_t)hs * 2 * nkvd + (kvhead + key) * D;
+      float* pv_ = pk_ + nkvd;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int dim = db * 32 + g4 * 8 + half * 4;
+          *reinterpret_cast<f32x4*>(pk_ + dim) =
+              f32x4{adk[db][4 * g4], adk[db][4 * g4 + 1], adk[db][4 * g4 + 2], adk[db][4 * g4 + 3]} * p.scale;
+          *reinterpret_cast<f32x4*>(pv_ + dim) =
+              f32x4{adv[db][4 * g4], adv[db][4 * g4 + 1], adv[db][4 * g4 + 2], adv[db][4 * g4 + 3]};
+        }
+      }
+    }
+    return;
+  }
   // dV and dK rows of this lane's key: 4 consecutive dims per store.
   const rsrc_t rdk = make_rsrc(static_cast<uint16_t*>(p.dk) + kvhead * D, (uint32_t)p.Nkv * C::ROWB);
   const rsrc_t rdv = make_rsrc(static_cast<uint16_t*>(p.dv) + kvhead * D, (uint32_t)p.Nkv * C::ROWB);
@@ -1205,6 +1231,23 @@ template <typename T, int D, bool CAUSAL>
 __global__ void __launch_bounds__(CfgBwdKV<D>::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dkdv(BwdParams p) {
   attn_bwd_dkdv_body<T, D, CAUSAL>(p);
+}
+
+// dK, dV = sum over the head shares of their fp32 partials, in share order
+// (deterministic), rounded once.  4 elements per thread.
+template <typename T>
+__global__ void __launch_bounds__(256) attn_bwd_reduce(const float* __restrict__ part, T* __restrict__ dk,
+                                                        T* __restrict__ dv, long long n4, int hsplit) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;   // index of 4 elements
+  if (i >= 2 * n4) return;
+  const bool isv = i >= n4;
+  const long long j = isv ? i - n4 : i;
+  const size_t stride = (size_t)2 * n4 * 4;                          // floats per head share
+  const float* src = part + (isv ? (size_t)n4 * 4 : 0) + (size_t)j * 4;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(src);
+  for (int h = 1; h < hsplit; ++h) acc += *reinterpret_cast<const f32x4*>(src + h * stride);
+  T o4[4] = {(T)acc[0], (T)acc[1], (T)acc[2], (T)acc[3]};
+  *reinterpret_cast<u32x2*>((isv ? dv : dk) + j * 4) = __builtin_bit_cast(u32x2, o4);
 }
 
 template <int D>
@@ -1731,8 +1774,15 @@ int run_bwd(BwdParams p, long long rows, hipStream_t stream) {
   hipLaunchKernelGGL((attn_bwd_prep<T, D>), dim3((unsigned)pblocks), dim3(256), 0, stream, p, rows);
   BwdParams pk = p;
   pk.n_tiles = (p.Nkv + CfgBwdKV<D>::BKV - 1) / CfgBwdKV<D>::BKV;
-  hipLaunchKernelGGL((attn_bwd_dkdv<T, D, CAUSAL>), dim3((unsigned)((long long)p.B * p.Hkv * pk.n_tiles)),
+  hipLaunchKernelGGL((attn_bwd_dkdv<T, D, CAUSAL>),
+                     dim3((unsigned)((long long)p.B * p.Hkv * p.hsplit * pk.n_tiles)),
                      dim3(CfgBwdKV<D>::NT), 0, stream, pk);
+  if (p.hsplit > 1) {
+    const long long n4 = (long long)p.B * p.Hkv * p.Nkv * D / 4;
+    hipLaunchKernelGGL((attn_bwd_reduce<T>), dim3((unsigned)((2 * n4 + 255) / 256)), dim3(256), 0,
+                       stream, (const float*)p.part, static_cast<T*>(p.dk), static_cast<T*>(p.dv),
+                       n4, p.hsplit);
+  }
   BwdParams pq = p;
   pq.n_tiles = (p.Nq + CfgBwdQ<D>::BR - 1) / CfgBwdQ<D>::BR;
   hipLaunchKernelGGL((attn_bwd_dq<T, D, CAUSAL>), dim3((unsigned)((long long)p.B * p.Hq * pq.n_tiles)),
@@ -1920,9 +1970,30 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
   return dispatch_split<_Float16>(sp, o, lse, d, c, s);
 }
 
-size_t fa_bwd_workspace_bytes(int B, int Hq, int N_q) {
-  if (B < 1 || Hq < 1 || N_q < 1) return 0;
-  return (size_t)((unsigned long long)B * Hq * N_q * 8ull);
+}  // extern "C"
+
+namespace {
+// Head shares of the dK/dV pass: enough workgroups for about eight per CU,
+// never more shares than query heads per key/value head.
+int bwd_hsplit(int B, int Hq, int Hkv, int N_kv) {
+  const long long base = (long long)B * Hkv * ((N_kv + 255) / 256);
+  long long hs = (2048 + base - 1) / base;
+  const int group = Hq / Hkv;
+  if (hs > group) hs = group;
+  return hs < 1 ? 1 : (int)hs;
+}
+}  // namespace
+
+extern "C" {
+
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N_q, int N_kv, int d) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || N_q < 1 || N_kv < 1 || Hq % Hkv != 0 || (d != 64 && d != 128))
+    return 0;
+  const unsigned long long stats = (unsigned long long)B * Hq * N_q * 8ull;
+  const int hs = bwd_hsplit(B, Hq, Hkv, N_kv);
+  const unsigned long long part =
+      hs > 1 ? (unsigned long long)hs * 2ull * B * Hkv * N_kv * d * 4ull : 0ull;
+  return (size_t)(((stats + 255) / 256) * 256 + part);
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -1947,7 +2018,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   const size_t nq = (size_t)B * Hq * N_q * d * es;
   const size_t nkv = (size_t)B * Hkv * N_kv * d * es;
   const size_t nl = (size_t)B * Hq * N_q * sizeof(float);
-  const size_t nws = fa_bwd_workspace_bytes(B, Hq, N_q);
+  const size_t nws = fa_bwd_workspace_bytes(B, Hq, Hkv, N_q, N_kv, d);
   if (workspace_bytes < nws) return FA_ERR_WORKSPACE;
   const size_t in_n[6] = {nq, nkv, nkv, nq, nl, nq};
   const size_t out_n[4] = {nq, nkv, nkv, nws};
@@ -1968,6 +2039,9 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   p.dk = dk;
   p.dv = dv;
   p.stats = static_cast<float2*>(workspace);
+  p.hsplit = bwd_hsplit(B, Hq, Hkv, N_kv);
+  p.part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                    (((size_t)B * Hq * N_q * 8 + 255) / 256) * 256);
   p.B = B;
   p.Hq = Hq;
   p.Hkv = Hkv;

@@ -185,15 +185,18 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
  * or FA_F16 (FA_ERR_DTYPE for FA_F32); d 64 or 128; any finite scale.
  *
  * workspace: caller-owned device memory of at least
- * fa_bwd_workspace_bytes(B, Hq, N_q) bytes (8 per query row: lse * log2(e)
- * and D in fp32), 16-byte aligned; fully rewritten by every call.
+ * fa_bwd_workspace_bytes(B, Hq, Hkv, N_q, N_kv, d) bytes, 16-byte aligned,
+ * fully rewritten by every call: 8 bytes per query row (lse * log2(e) and D
+ * in fp32) and, when the key/value pass deals the query heads of a group
+ * over several workgroups (few key/value heads), their fp32 partial dK and
+ * dV, which a fourth launch sums in a fixed order.
  * dq, dk, dv and the workspace must not overlap any input or each other
- * (FA_ERR_ALIAS); pointer alignment as for fa_fwd (FA_ERR_ALIGN).  Three
- * launches on `stream` (NULL = null stream): the row pass, the dK/dV pass,
- * the dQ pass.  Every output element is written once, by one wave: the
+ * (FA_ERR_ALIAS); pointer alignment as for fa_fwd (FA_ERR_ALIGN).  Three or
+ * four launches on `stream` (NULL = null stream): the row pass, the dK/dV
+ * pass, its reduction when used, the dQ pass.  Every output element is written once, by one wave: the
  * result is deterministic.  The library allocates nothing.
  */
-size_t fa_bwd_workspace_bytes(int B, int Hq, int N_q);
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N_q, int N_kv, int d);
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
            const void* dout, void* dq, void* dk, void* dv,

@@ -209,15 +209,23 @@ DO, DQ, DK, DV = 0x70000000, 0x80000000, 0x90000000, 0xA0000000
 def bwd(q=Q, k=K, v=V, o=O, lse=L, do=DO, dq=DQ, dk=DK, dv=DV, ws=W, ws_bytes=None, **kw):
     a = args(**kw)
     if ws_bytes is None:
-        ws_bytes = fa.fa_bwd_workspace_bytes(a["B"], a["Hq"], a["N_q"])
+        ws_bytes = fa.fa_bwd_workspace_bytes(a["B"], a["Hq"], a["Hkv"], a["N_q"], a["N_kv"], a["d"])
     # Every case below fails its host checks, so no call reaches HIP.
     return fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, a["B"], a["Hq"], a["Hkv"], a["N_q"],
                      a["N_kv"], a["d"], a["scale"], a["causal"], a["dtype"], ws, ws_bytes, None)
 
 
 def test_bwd_workspace_bytes(lib):
-    assert fa.fa_bwd_workspace_bytes(2, 8, 100) == 2 * 8 * 100 * 8
-    assert fa.fa_bwd_workspace_bytes(0, 8, 100) == 0 and fa.fa_bwd_workspace_bytes(1, 1, 0) == 0
+    # row statistics (8 B per query row, rounded up to 256 B) ...
+    assert fa.fa_bwd_workspace_bytes(2, 32, 32, 8192, 8192, 128) == 2 * 32 * 8192 * 8
+    assert fa.fa_bwd_workspace_bytes(1, 1, 1, 10, 10, 64) == 256
+    # ... plus fp32 partial dK, dV per head share when few key/value heads:
+    # 1 x 4 kv heads x 16 key tiles = 64 workgroups -> 7 shares (all 7 heads)
+    assert fa.fa_bwd_workspace_bytes(1, 28, 4, 4096, 4096, 128) == \
+        28 * 4096 * 8 + 7 * 2 * 4 * 4096 * 128 * 4
+    for bad in [(0, 8, 8, 100, 100, 64), (1, 7, 2, 10, 10, 64), (1, 1, 1, 0, 1, 64),
+                (1, 1, 1, 1, 1, 96)]:
+        assert fa.fa_bwd_workspace_bytes(*bad) == 0
 
 
 def test_bwd_rejects_on_host(lib):
