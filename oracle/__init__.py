@@ -15,6 +15,7 @@ from .attention_ref import (  # noqa: F401
     attention_fp64,
     attention_fp64_keys,
     attention_bwd_fp64,
+    attention_bwd_fp64_rows,
     attention_fp64_key_range,
     attention_bruteforce,
     attention_online_blocked,

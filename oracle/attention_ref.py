@@ -236,6 +236,57 @@ def attention_bwd_fp64(q, k, v, do, scale: float, causal: bool = False):
     return dq, dk, dv
 
 
+def attention_bwd_fp64_rows(q, k, v, do, scale: float, causal: bool, q_rows, key_rows):
+    """Selected rows of dQ (query rows ``q_rows``) and of dK, dV (key rows
+    ``key_rows``), by the same definition as ``attention_bwd_fp64``.
+
+    For sequences too long to form every gradient: lse and O come from
+    ``attention_fp64`` (exact, row by row), so P[i, j] = exp(s_ij - lse_i) is
+    available for any single row or column.  A dQ row needs its own P and dP
+    rows; a dK/dV row needs the P and dP columns of its key over every query:
+
+        dQ[i] = sigma sum_j P[i,j] (dP[i,j] - D_i) K[j]
+        dV[j] = sum_i P[i,j] dO[i],   dK[j] = sigma sum_i P[i,j] (dP[i,j] - D_i) Q[i]
+
+    with D_i = sum_t dO[i,t] O[i,t] = sum_j P[i,j] dP[i,j].  Key rows sum over
+    the query heads of their group.  Returns (dq[:, :, q_rows], dk[:, :, key_rows],
+    dv[:, :, key_rows]) in float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, Hq, Hkv, Nq, Nkv, D = _check_shapes(q, k, v)
+    sigma = _sigma(scale)
+    qr = np.asarray(q_rows, dtype=np.int64).reshape(-1)
+    kr = np.asarray(key_rows, dtype=np.int64).reshape(-1)
+    o, lse = attention_fp64(q, k, v, scale, causal)
+    dvec = np.sum(do * o, axis=-1)                            # D_i
+    dq = np.zeros((B, Hq, qr.size, D))
+    dk = np.zeros((B, Hkv, kr.size, D))
+    dv = np.zeros((B, Hkv, kr.size, D))
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            # query rows: full rows of P and dP
+            s = sigma * (q[b, h, qr] @ k[b, g].T)             # [len(qr), Nkv]
+            if causal:
+                s = np.where(np.arange(Nkv)[None, :] <= qr[:, None], s, -np.inf)
+            p = np.exp(s - lse[b, h, qr][:, None])
+            dp = do[b, h, qr] @ v[b, g].T
+            dq[b, h] = sigma * ((p * (dp - dvec[b, h, qr][:, None])) @ k[b, g])
+            # key rows: full columns of P and dP
+            s = sigma * (q[b, h] @ k[b, g, kr].T)             # [Nq, len(kr)]
+            if causal:
+                s = np.where(kr[None, :] <= np.arange(Nq)[:, None], s, -np.inf)
+            p = np.exp(s - lse[b, h][:, None])
+            dp = do[b, h] @ v[b, g, kr].T
+            ds = p * (dp - dvec[b, h][:, None])
+            dv[b, g] += p.T @ do[b, h]
+            dk[b, g] += sigma * (ds.T @ q[b, h])
+    return dq, dk, dv
+
+
 def probabilities_fp64(q, k, scale: float, causal: bool = False):
     """Full probability tensor P [B, Hq, Nq, Nkv] (masked entries are 0).
 

@@ -93,3 +93,69 @@ def test_deterministic():
     b = run_case("det", 1, 8, 2, 200, 300, 128, True, seed=19)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+# ---- full-size workloads, in the launch configuration bench.py --backward times ----
+
+def full_size(widx):
+    w = workloads.WORKLOADS[widx]
+    q, k, v, scale = workloads.workload_inputs(w)
+    do = workloads.make_inputs(w.B, w.Hq, w.Hq, w.Nq, 1, w.D, w.dtype, w.seed + 100)[0]
+    qd, kd, vd, dod = (x.to(DEV) for x in (q, k, v, do))
+    o, lse = fa.attention(qd, kd, vd, causal=w.causal, scale=scale)
+    dq = torch.full_like(qd, float("nan"))
+    dk = torch.full_like(kd, float("nan"))
+    dv = torch.full_like(vd, float("nan"))
+    fa.attention_backward(qd, kd, vd, o, lse, dod, causal=w.causal, scale=scale, dq=dq, dk=dk,
+                          dv=dv)
+    torch.cuda.synchronize()
+    return w, (q, k, v, do, scale), (dq.cpu(), dk.cpu(), dv.cpu())
+
+
+def compare_slice(name, got, ref):
+    for nm, g, r in zip(("dq", "dk", "dv"), got, ref):
+        gg = workloads.to_f64(g)
+        assert np.all(np.isfinite(gg)), f"{nm}: unwritten or non-finite"
+        err = float(np.max(np.abs(gg - r)))
+        mag = float(np.max(np.abs(r)))
+        say(f"    {name} {nm}: max|err|={err:.3e} max|ref|={mag:.3e}")
+        assert err <= 2e-2 * max(1.0, mag), (nm, err, mag)
+
+
+def test_full_workload3_one_head():
+    """B=2 H=32 N=8192 d=128: the last (batch, head), every gradient element."""
+    say("[case] workload 3 backward, head (1, 31)")
+    w, (q, k, v, do, scale), (dq, dk, dv) = full_size(3)
+    sl = (slice(1, 2), slice(31, 32))
+    ref = attention_bwd_fp64(*(workloads.to_f64(x[sl]) for x in (q, k, v, do)), scale, w.causal)
+    compare_slice("w3", (dq[sl], dk[sl], dv[sl]), ref)
+
+
+def test_full_workload4_one_group():
+    """B=1 Hq=28 Hkv=4 N=4096 causal: the last key/value group (7 query heads), every element."""
+    say("[case] workload 4 backward, kv group 3")
+    w, (q, k, v, do, scale), (dq, dk, dv) = full_size(4)
+    hq, hk = slice(21, 28), slice(3, 4)
+    ref = attention_bwd_fp64(workloads.to_f64(q[:, hq]), workloads.to_f64(k[:, hk]),
+                             workloads.to_f64(v[:, hk]), workloads.to_f64(do[:, hq]), scale,
+                             w.causal)
+    compare_slice("w4", (dq[:, hq], dk[:, hk], dv[:, hk]), ref)
+
+
+def test_full_workload5_sampled_rows():
+    """B=1 Hq=28 Hkv=4 N=32768 causal, outlier keys: group 0, sampled dQ rows and dK/dV rows
+    (first and last 64, both sides of 4096-row boundaries, 128 at random)."""
+    from oracle import attention_bwd_fp64_rows
+    say("[case] workload 5 backward, kv group 0, sampled rows")
+    w, (q, k, v, do, scale), (dq, dk, dv) = full_size(5)
+    N = w.Nq
+    rng = np.random.default_rng(91)
+    picks = [np.arange(64), np.arange(N - 64, N), rng.choice(N, 128, replace=False)]
+    for b in range(4096, N, 4096):
+        picks.append(np.arange(b - 2, b + 2))
+    rows = np.unique(np.concatenate(picks))
+    hq, hk = slice(0, 7), slice(0, 1)
+    ref = attention_bwd_fp64_rows(workloads.to_f64(q[:, hq]), workloads.to_f64(k[:, hk]),
+                                  workloads.to_f64(v[:, hk]), workloads.to_f64(do[:, hq]), scale,
+                                  w.causal, rows, rows)
+    compare_slice("w5", (dq[:, hq][:, :, rows], dk[:, hk][:, :, rows], dv[:, hk][:, :, rows]), ref)

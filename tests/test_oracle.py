@@ -18,7 +18,8 @@ import pytest
 import torch
 from scipy.special import logsumexp, softmax
 
-from oracle import (attention_bruteforce, attention_bwd_fp64, attention_fp64,
+from oracle import (attention_bruteforce, attention_bwd_fp64, attention_bwd_fp64_rows,
+                    attention_fp64,
                     attention_fp64_key_range, attention_fp64_keys, attention_online_blocked,
                     probabilities_fp64, kv_head_of)
 import workloads
@@ -436,3 +437,17 @@ def test_backward_closed_forms():
     dq, dk, dv = attention_bwd_fp64(q, k, v, do, 0.0, False)
     assert np.allclose(dv[0, 0], np.broadcast_to(do[0, 0].sum(axis=0) / 4, (4, 2)), atol=1e-14)
     assert np.max(np.abs(dq)) == 0 and np.max(np.abs(dk)) == 0
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_rows_match_whole_backward(causal):
+    """Selected gradient rows (lse and O taken from the forward oracle) equal the
+    whole-matrix backward, which the tests above pin to central differences."""
+    q, k, v = _rand(2, 6, 2, 37, 41, 8, seed=59)
+    do = np.random.default_rng(60).standard_normal(q.shape)
+    dq, dk, dv = attention_bwd_fp64(q, k, v, do, 0.45, causal)
+    qr, kr = np.array([0, 5, 36, 17]), np.array([40, 0, 3, 22])
+    rq, rk, rv = attention_bwd_fp64_rows(q, k, v, do, 0.45, causal, qr, kr)
+    assert np.max(np.abs(rq - dq[:, :, qr])) <= 1e-12
+    assert np.max(np.abs(rk - dk[:, :, kr])) <= 1e-12
+    assert np.max(np.abs(rv - dv[:, :, kr])) <= 1e-12
