@@ -6,9 +6,10 @@ and the benchmark's CPU-baseline leg use it.  It shares no code with the HIP
 library (no kernels, headers, helpers, tables or pre/post-processing).
 
 What it computes and which passage of the source pages each function follows
-is stated in ``attention_ref``'s docstrings.  Every function here is pinned by
-CPU tests against values the pages print, closed forms, invariants, a library
-routine and pure-Python brute force (tests/test_oracle.py).
+is stated in the docstrings of ``attention_ref`` and ``fp8_ref``.  Every
+function here is pinned by CPU tests against values the pages print, closed
+forms, invariants, a library routine and pure-Python brute force
+(tests/test_oracle.py, tests/test_oracle_fp8.py).
 """
 
 from .attention_ref import (  # noqa: F401
@@ -22,4 +23,10 @@ from .attention_ref import (  # noqa: F401
     probabilities_fp64,
     kv_head_of,
     allowed_keys,
+)
+from .fp8_ref import (  # noqa: F401
+    e4m3_decode,
+    dequantize_e4m3,
+    attention_fp8_fp64,
+    fp8_p_rounding_bound,
 )

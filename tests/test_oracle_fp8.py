@@ -1,0 +1,176 @@
+"""Pins of the FP8 (E4M3) part of the oracle (oracle/fp8_ref.py), CPU only.
+
+* ``e4m3_decode`` against the closed forms of the OCP E4M3 format and against
+  torch's own float8_e4m3fn conversion, code by code.
+* ``attention_fp8_fp64`` against ``attention_fp64`` on inputs dequantised by
+  torch, and against scaling laws of the dequantisation factors.
+* ``fp8_p_rounding_bound`` against a simulation of the GPU's rounding of P
+  (torch's float8_e4m3fn conversion, an independent round-to-nearest-even),
+  for every admissible position of the exponent reference; and shown not to
+  be vacuous: a coarser format (E5M2) breaks it.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import (attention_fp64, attention_fp8_fp64, dequantize_e4m3, e4m3_decode,
+                    fp8_p_rounding_bound, probabilities_fp64)
+
+
+def torch_decode(codes):
+    t = torch.from_numpy(np.asarray(codes, dtype=np.uint8).copy()).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def test_decode_matches_torch_for_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    ours, ref = e4m3_decode(codes), torch_decode(codes)
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(ours[fin], ref[fin])
+    assert np.array_equal(np.signbit(ours[fin]), np.signbit(ref[fin]))
+
+
+def test_decode_closed_forms():
+    d = lambda c: float(e4m3_decode(np.array([c]))[0])   # noqa: E731
+    assert d(0x38) == 1.0 and d(0x40) == 2.0 and d(0x30) == 0.5
+    assert d(0x7E) == 448.0 and d(0xFE) == -448.0          # largest finite
+    assert d(0x01) == 2.0 ** -9 and d(0x07) == 7 * 2.0 ** -9   # subnormals
+    assert d(0x08) == 2.0 ** -6                             # smallest normal
+    assert d(0x00) == 0.0 and math.copysign(1.0, d(0x80)) == -1.0
+    assert math.isnan(d(0x7F)) and math.isnan(d(0xFF))
+    pos = e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    assert np.all(np.diff(pos) > 0)                         # monotone, no gaps or repeats
+    assert np.array_equal(e4m3_decode(np.arange(0x80, 0xFF, dtype=np.uint8)), -pos)
+
+
+def test_dequantize_widens_the_float32_descale():
+    codes = np.arange(0x7F, dtype=np.uint8)
+    got = dequantize_e4m3(codes, 0.1)
+    assert np.array_equal(got, e4m3_decode(codes) * float(np.float32(0.1)))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_equals_attention_of_torch_dequantised_inputs(causal):
+    (q8, k8, v8), (dq, dk, dv) = workloads.make_inputs_fp8(1, 4, 2, 37, 53, 64, seed=5)
+    o, lse = attention_fp8_fp64(workloads.codes_of(q8), workloads.codes_of(k8),
+                                workloads.codes_of(v8), dq, dk, dv, 0.125, causal)
+    deq = [x.to(torch.float64).numpy() * float(np.float32(s)) for x, s in ((q8, dq), (k8, dk), (v8, dv))]
+    ro, rl = attention_fp64(*deq, 0.125, causal)
+    assert np.array_equal(o, ro) and np.array_equal(lse, rl)
+
+
+def _codes(seed, shape):
+    rng = np.random.default_rng(seed)
+    c = rng.integers(0, 256, size=shape).astype(np.uint8)
+    c[(c & 0x7F) == 0x7F] = 0x38          # no NaN codes
+    return c
+
+
+def test_descale_laws():
+    q8, k8, v8 = _codes(1, (1, 2, 9, 16)), _codes(2, (1, 1, 11, 16)), _codes(3, (1, 1, 11, 16))
+    o, lse = attention_fp8_fp64(q8, k8, v8, 0.01, 0.02, 0.03, 0.25)
+    # V's factor scales O only (a power of two: exactly)
+    o2, lse2 = attention_fp8_fp64(q8, k8, v8, 0.01, 0.02, 0.06, 0.25)
+    assert np.array_equal(o2, 2 * o) and np.array_equal(lse2, lse)
+    # Q's and K's factors enter through their product with scale
+    o3, lse3 = attention_fp8_fp64(q8, k8, v8, 0.02, 0.01, 0.03, 0.25)
+    assert np.allclose(o3, o, rtol=0, atol=1e-13) and np.allclose(lse3, lse, rtol=0, atol=1e-13)
+    o4, lse4 = attention_fp8_fp64(q8, k8, v8, 0.02, 0.02, 0.03, 0.125)
+    assert np.allclose(o4, o, rtol=0, atol=1e-13) and np.allclose(lse4, lse, rtol=0, atol=1e-13)
+
+
+def test_all_one_value_codes_give_descale():
+    q8, k8 = _codes(4, (2, 2, 7, 64)), _codes(5, (2, 1, 13, 64))
+    v8 = np.full((2, 1, 13, 64), 0x38, dtype=np.uint8)
+    o, _ = attention_fp8_fp64(q8, k8, v8, 0.05, 0.05, 0.75, 0.125, True)
+    assert np.allclose(o, 0.75, rtol=0, atol=1e-15)
+
+
+def test_quantisation_recipe():
+    (q8, k8, v8), ds = workloads.make_inputs_fp8(2, 3, 1, 40, 50, 64, seed=9, sigma=0.5)
+    xs = workloads.make_inputs(2, 3, 1, 40, 50, 64, "f32", 9, 0.5)
+    for c, s, x in zip((q8, k8, v8), ds, xs):
+        assert c.dtype == torch.float8_e4m3fn
+        assert s == float(np.float32(s)) and s > 0
+        val = e4m3_decode(workloads.codes_of(c))
+        assert np.max(np.abs(val)) == 448.0               # the largest |x| maps to the top code
+        xd = x.double().numpy() / s
+        normal = np.abs(xd) >= 2.0 ** -6
+        rel = np.abs(val[normal] - xd[normal]) / np.abs(xd[normal])
+        assert rel.max() <= 2.0 ** -4 * (1 + 1e-6)        # round to nearest, 3 mantissa bits
+        assert np.max(np.abs(val[~normal] - xd[~normal]), initial=0.0) <= 2.0 ** -10 * (1 + 1e-6)
+
+
+# ---- the tolerance model of the GPU path ----
+
+def _simulate(q, k, v, scale, causal, log2_c, fmt=torch.float8_e4m3fn):
+    """O with P formed against a reference log2_c below the row maximum, rounded to
+    ``fmt`` (torch's conversion), divided by the sum of the unrounded P."""
+    w = probabilities_fp64(q, k, scale, causal)             # exact softmax rows
+    wmax = w.max(axis=-1, keepdims=True)
+    p = (2.0 ** log2_c) * w / wmax
+    pr = torch.from_numpy(p).to(fmt).to(torch.float64).numpy()
+    B, Hq, Nq, Nkv = w.shape
+    Hkv = k.shape[1]
+    o = np.empty((B, Hq, Nq, v.shape[-1]))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            o[b, h] = (pr[b, h] @ v[b, g]) / p[b, h].sum(axis=-1, keepdims=True)
+    return o
+
+
+REGIMES = [("diffuse", 0.05), ("typical", 0.125), ("sharp", 0.6), ("very sharp", 2.5)]
+
+
+@pytest.mark.parametrize("name,scale", REGIMES)
+@pytest.mark.parametrize("causal", [False, True])
+def test_bound_holds_for_every_reference_offset(name, scale, causal):
+    rng = np.random.default_rng(int(scale * 1000) + causal)
+    q = rng.standard_normal((1, 2, 24, 32))
+    k = rng.standard_normal((1, 1, 300, 32))
+    v = rng.standard_normal((1, 1, 300, 32))
+    o_ref, _ = attention_fp64(q, k, v, scale, causal)
+    bound = fp8_p_rounding_bound(q, k, v, scale, causal)
+    for log2_c in (0.0, 0.37, 1.0, 3.5, 7.9, 8.0):          # the reference may trail the max by < 2^8
+        err = np.abs(_simulate(q, k, v, scale, causal, log2_c) - o_ref)
+        assert np.all(err <= bound * (1 + 1e-9) + 1e-15), (name, log2_c, float((err - bound).max()))
+
+
+def test_bound_is_not_vacuous():
+    """Rounding P to E5M2 (2 mantissa bits, relative error up to 2^-3) breaks the bound."""
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((1, 1, 64, 32))
+    k = rng.standard_normal((1, 1, 64, 32))
+    v = rng.standard_normal((1, 1, 64, 32))
+    o_ref, _ = attention_fp64(q, k, v, 0.6, False)
+    bound = fp8_p_rounding_bound(q, k, v, 0.6, False)
+    err = np.abs(_simulate(q, k, v, 0.6, False, 0.37, torch.float8_e5m2) - o_ref)
+    assert np.any(err > bound)
+    # and the E4M3 error uses a fair share of it, somewhere
+    err4 = np.abs(_simulate(q, k, v, 0.6, False, 0.37) - o_ref)
+    assert err4.max() > 0.05 * bound.max()
+
+
+def test_bound_special_cases():
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((1, 1, 8, 16))
+    k = rng.standard_normal((1, 1, 20, 16))
+    v = rng.standard_normal((1, 1, 20, 16))
+    assert np.all(fp8_p_rounding_bound(q, k, np.zeros_like(v), 0.3) == 0)
+    b = fp8_p_rounding_bound(q, k, v, 0.3)
+    w = probabilities_fp64(q, k, 0.3)
+    upper = 2.0 ** -4 * (w @ np.abs(v[0, 0])) + 2.0 ** -10 * w.max(-1, keepdims=True) * np.abs(v).sum(2)
+    assert np.all(b <= upper + 1e-15)
+    assert np.all(b >= 2.0 ** -4 * (w @ np.abs(v[0, 0])) - 1e-15)
+    # one key: p = c exactly representable only for some c; the bound is 2^-4 |v|
+    b1 = fp8_p_rounding_bound(q, k[:, :, :1], v[:, :, :1], 0.3)
+    assert np.allclose(b1, 2.0 ** -4 * np.abs(v[:, :, :1]), rtol=1e-15, atol=0)
+    # rows restricted
+    br = fp8_p_rounding_bound(q, k, v, 0.3, rows=[5, 2])
+    assert np.array_equal(br[:, :, 0], b[:, :, 5]) and np.array_equal(br[:, :, 1], b[:, :, 2])

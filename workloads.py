@@ -12,8 +12,10 @@ with a causal mask; the others are multi-head and long-sequence variants.
 Workload 6 is one decoding step of that 7B shape (one new query row per
 sequence against a 32768-key cache, batch 8), the case the same page (§3,
 where the method helps and where it does not) sends to the split-KV
-FlashDecoding variant.  No public dataset is involved; nothing is read from
-disk.
+FlashDecoding variant.  Workload 7 is workload 3's shape with 8-bit E4M3
+inputs (the FP8 direction the pages name for FlashAttention-3), quantised from
+the same kind of draws by ``make_inputs_fp8``.  No public dataset is
+involved; nothing is read from disk.
 
 Recipe (all workloads): ``numpy.random.default_rng(seed)`` (PCG64), draw Q,
 then K, then (for outlier workloads) the outlier rows of K, then V, each as
@@ -65,11 +67,13 @@ class Workload:
         return f / 2.0 if self.causal else f
 
     def io_bytes(self) -> float:
-        """Compulsory HBM bytes of one forward: Q, K, V read once, O and lse written once."""
-        es = 4 if self.dtype == "f32" else 2
+        """Compulsory HBM bytes of one forward: Q, K, V read once, O and lse written once
+        (an e4m3 workload reads 1-byte Q, K, V and writes a bf16 O)."""
+        es_in = {"f32": 4, "e4m3": 1}.get(self.dtype, 2)
+        es_out = 4 if self.dtype == "f32" else 2
         q = self.B * self.Hq * self.Nq * self.D
         kv = self.B * self.Hkv * self.Nkv * self.D
-        return float(es * (2 * q + 2 * kv) + 4 * self.B * self.Hq * self.Nq)
+        return float(es_in * (q + 2 * kv) + es_out * q + 4 * self.B * self.Hq * self.Nq)
 
     def as_dict(self) -> dict:
         d = asdict(self)
@@ -85,6 +89,7 @@ WORKLOADS = {
     5: Workload(5, "long_causal_gqa_n32768_outlier_keys", 1, 28, 4, 32768, 32768, 128, "bf16",
                 True, sigma=0.5, outlier_frac=0.01, outlier_mult=8.0),
     6: Workload(6, "decode_gqa_7b_b8_n32768", 8, 28, 4, 1, 32768, 128, "bf16", False),
+    7: Workload(7, "long_noncausal_e4m3_n8192_d128", 2, 32, 32, 8192, 8192, 128, "e4m3", False),
 }
 
 
@@ -112,6 +117,42 @@ def make_inputs(B, Hq, Hkv, Nq, Nkv, D, dtype="bf16", seed=0, sigma=1.0,
         v *= np.float32(sigma)
     tdt = DTYPES[dtype]
     return tuple(torch.from_numpy(x).to(tdt).contiguous() for x in (q, k, v))
+
+
+E4M3_MAX = 448.0
+
+
+def make_inputs_fp8(B, Hq, Hkv, Nq, Nkv, D, seed=0, sigma=1.0, outlier_frac=0.0,
+                    outlier_mult=8.0):
+    """Draw (q8, k8, v8) as torch.float8_e4m3fn CPU tensors plus their fp32 descales.
+
+    The float32 draws are those of ``make_inputs`` with the same arguments.
+    Each tensor is quantised with one factor: descale = float32(max|x| / 448)
+    (1 for an all-zero tensor), codes = x / descale rounded to nearest even by
+    torch's CPU conversion (clamped to +-448 first against a last-bit overshoot
+    of the division).  Value of a code: decode(code) * descale.
+    """
+    xs = make_inputs(B, Hq, Hkv, Nq, Nkv, D, "f32", seed, sigma, outlier_frac, outlier_mult)
+    codes, descales = [], []
+    for x in xs:
+        amax = float(x.abs().max()) if x.numel() else 0.0
+        ds = float(np.float32(amax / E4M3_MAX)) if amax > 0.0 else 1.0
+        y = (x / torch.tensor(ds, dtype=torch.float32)).clamp(-E4M3_MAX, E4M3_MAX)
+        codes.append(y.to(torch.float8_e4m3fn).contiguous())
+        descales.append(ds)
+    return tuple(codes), tuple(descales)
+
+
+def workload_inputs_fp8(w: Workload):
+    """((q8, k8, v8), (descale_q, descale_k, descale_v), scale) for an e4m3 workload."""
+    codes, ds = make_inputs_fp8(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, w.seed, w.sigma,
+                                w.outlier_frac, w.outlier_mult)
+    return codes, ds, w.scale
+
+
+def codes_of(t: torch.Tensor) -> np.ndarray:
+    """The raw byte codes of a float8 CPU tensor, as a uint8 array."""
+    return t.detach().to("cpu").contiguous().view(torch.uint8).numpy()
 
 
 def workload_inputs(w: Workload):
