@@ -13,7 +13,8 @@ FLOPs per step = 4*B*Hq*N_q*N_kv*d, halved for causal.
 
 The CPU baseline times the fp64 oracle on the host cores on a bounded
 sample (whole heads of the same workload, about 10 s of CPU work) and scales
-its rate to the same FLOP count.
+its rate to the same FLOP count; the heads it computed are then compared with
+the GPU's output of the timed launches (``parity_sample``).
 """
 
 from __future__ import annotations
@@ -28,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_FP8_TFLOPS = 5033.2    # 256 CU x 2.4 GHz x 8192 dense fp8 FLOP/clk/CU
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 METRIC = "attn fwd TFLOP/s and % of MI355X bf16 MFMA peak (N=8k/32k, d=128)"
@@ -38,11 +40,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=3, help="named workload index (1-5)")
+    ap.add_argument("--workload", type=int, default=3,
+                    help="named workload index (1-7; 7 is the E4M3 variant of 3)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline (0 disables)")
-    ap.add_argument("--check-rows", type=int, default=64,
-                    help="rows per sampled head checked against the oracle after timing")
     ap.add_argument("--path", choices=["auto", "fwd", "splitkv"], default="auto",
                     help="entry point to time: fa_fwd_stream, or fa_fwd_splitkv (auto: split-KV "
                          "for the decoding workload 6, fa_fwd otherwise)")
@@ -95,7 +96,7 @@ def measured_traffic(workload_name: str):
     return float(fields["traffic_bytes_per_launch"])
 
 
-def power_context(fa, w, qd, kd, vd, o, lse, scale, stream, dcode):
+def power_context(fa, w, qd, kd, vd, o, lse, scale, stream, dcode, fp8_descales=None):
     """Context for the roofline fraction, measured on the same GPU in the same process.
 
     MI355X lowers its clock under sustained dense MFMA load on random operands, so the
@@ -129,11 +130,17 @@ def power_context(fa, w, qd, kd, vd, o, lse, scale, stream, dcode):
         b.zero_()
         ms_zero = timed(lambda: torch.mm(a, b, out=c), 40)
     del a, b, c
-    zq, zk, zv = torch.zeros_like(qd), torch.zeros_like(kd), torch.zeros_like(vd)
+    zdt = torch.uint8 if fp8_descales is not None else qd.dtype   # E4M3 code 0 is +0.0
+    zq, zk, zv = (torch.zeros(x.shape, dtype=zdt, device=x.device) for x in (qd, kd, vd))
+    o, lse = torch.empty_like(o), torch.empty_like(lse)   # keep the benchmarked outputs intact
 
     def attn_zero():
-        st = fa.fa_fwd_stream(zq, zk, zv, o, lse, w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, scale,
-                              w.causal, dcode, stream)
+        if fp8_descales is not None:
+            st = fa.fa_fwd_fp8(zq, zk, zv, o, lse, w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, scale,
+                               w.causal, *fp8_descales, stream)
+        else:
+            st = fa.fa_fwd_stream(zq, zk, zv, o, lse, w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, scale,
+                                  w.causal, dcode, stream)
         if st != 0:
             raise RuntimeError(fa.fa_status_string(st))
     ms_attn_zero = timed(attn_zero, 20)
@@ -145,15 +152,21 @@ def power_context(fa, w, qd, kd, vd, o, lse, scale, stream, dcode):
     }
 
 
-def cpu_baseline(w, q, k, v, budget_s, hbm_bound=False):
+def cpu_baseline(w, q, k, v, budget_s, hbm_bound=False, fp8_descales=None, o_gpu=None,
+                 lse_gpu=None, scale=None):
     """Time the oracle on whole (b, h) heads until ~budget_s of wall time.
 
     The rate is in the benchmark's unit: FLOPs of the heads done (TFLOP/s), or
     for the HBM-bound decoding workload their share of the compulsory bytes
-    (GB/s)."""
+    (GB/s).  For an E4M3 workload the oracle is the exact attention of the
+    dequantised codes.
+
+    Outside the timed calls, the heads the oracle computed are compared with
+    the GPU's output of the benchmarked launches (o_gpu, lse_gpu): max-abs
+    errors, and for E4M3 the worst ratio to the oracle's tolerance model."""
     import numpy as np
     import workloads
-    from oracle import attention_fp64
+    from oracle import attention_fp64, attention_fp8_fp64, dequantize_e4m3, fp8_tolerances
     from oracle.attention_ref import _default_threads
     cores = _default_threads()
     heads = [(b, h) for b in range(w.B) for h in range(w.Hq)]
@@ -162,24 +175,46 @@ def cpu_baseline(w, q, k, v, budget_s, hbm_bound=False):
     g = w.Hq // w.Hkv
     done, t_total, flops = 0, 0.0, 0.0
     per_head = (w.io_bytes() if hbm_bound else w.flops()) / (w.B * w.Hq)
+    o_cpu = None if o_gpu is None else o_gpu.cpu()
+    l_cpu = None if lse_gpu is None else lse_gpu.cpu()
+    err_o, err_l, worst = 0.0, 0.0, 0.0
     for i in order:
         b, h = heads[i]
-        qh = workloads.to_f64(q[b:b + 1, h:h + 1])
-        kh = workloads.to_f64(k[b:b + 1, h // g:h // g + 1])
-        vh = workloads.to_f64(v[b:b + 1, h // g:h // g + 1])
-        t0 = time.perf_counter()
-        attention_fp64(qh, kh, vh, w.scale, w.causal)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        skv = (slice(b, b + 1), slice(h // g, h // g + 1))
+        if fp8_descales is not None:
+            qh, kh, vh = (workloads.codes_of(x[s_]) for x, s_ in ((q, sl), (k, skv), (v, skv)))
+            t0 = time.perf_counter()
+            ro, rl = attention_fp8_fp64(qh, kh, vh, *fp8_descales, w.scale, w.causal)
+        else:
+            qh, kh, vh = (workloads.to_f64(x[s_]) for x, s_ in ((q, sl), (k, skv), (v, skv)))
+            t0 = time.perf_counter()
+            ro, rl = attention_fp64(qh, kh, vh, w.scale, w.causal)
         t_total += time.perf_counter() - t0
         flops += per_head
         done += 1
+        if o_cpu is not None:
+            eo = np.abs(workloads.to_f64(o_cpu[sl]) - ro)
+            el = np.abs(l_cpu[sl].double().numpy() - rl)
+            err_o, err_l = max(err_o, float(eo.max())), max(err_l, float(el.max()))
+            if fp8_descales is not None:
+                deq = [dequantize_e4m3(x, s_) for x, s_ in zip((qh, kh, vh), fp8_descales)]
+                to, tl = fp8_tolerances(*deq, w.scale, w.causal)
+                worst = max(worst, float(np.max(eo / to)), float(np.max(el / tl)))
         if t_total >= budget_s:
             break
-    scale, unit = (1e9, "GB/s") if hbm_bound else (1e12, "TFLOP/s")
-    return {"value": flops / t_total / scale, "unit": unit, "cores": cores,
+    scale_, unit = (1e9, "GB/s") if hbm_bound else (1e12, "TFLOP/s")
+    parity = None
+    if o_cpu is not None:
+        parity = {"heads_checked": done, "rows_per_head": w.Nq, "max_abs_err_O": err_o,
+                  "max_abs_err_lse": err_l}
+        if fp8_descales is not None:
+            parity["worst_err_over_tolerance"] = worst
+    return {"value": flops / t_total / scale_, "unit": unit, "cores": cores,
             "kind": "oracle",
             "sample": f"{done} of {len(heads)} (b,h) heads of the same workload, all "
                       f"{w.Nq} rows each, fp64 numpy, {t_total:.2f} s",
-            "seconds": t_total}
+            "seconds": t_total, "parity": parity}
 
 
 def main():
@@ -200,17 +235,27 @@ def main():
     w = workloads.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    q, k, v, scale = workloads.workload_inputs(w)
+    fp8 = w.dtype == "e4m3"
+    descales = None
+    if fp8:
+        (q, k, v), descales, scale = workloads.workload_inputs_fp8(w)
+    else:
+        q, k, v, scale = workloads.workload_inputs(w)
     qd, kd, vd = (x.to(dev) for x in (q, k, v))
-    o = torch.empty_like(qd)
+    o = torch.empty(qd.shape, dtype=torch.bfloat16 if fp8 else qd.dtype, device=dev)
     lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    dcode = fa.dtype_code(qd.dtype)
+    dcode = None if fp8 else fa.dtype_code(qd.dtype)
     fa.load_library()
 
     path = args.path if args.path != "auto" else ("splitkv" if w.index == 6 else "fwd")
     if args.backward:
         path = "bwd"
+    if fp8:
+        if path != "fwd":
+            print("the E4M3 workload has a forward entry point only", file=sys.stderr)
+            sys.exit(2)
+        path = "fp8"
     splits = None
     if path == "splitkv":
         splits = args.splits or fa.fa_splitkv_default_splits(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D,
@@ -237,6 +282,12 @@ def main():
         def step():
             st = fa.fa_bwd(qd, kd, vd, o, lse, dod, dq, dk, dv, w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D,
                            scale, w.causal, dcode, workspace, ws_bytes, stream)
+            if st != 0:
+                raise RuntimeError(fa.fa_status_string(st))
+    elif path == "fp8":
+        def step():
+            st = fa.fa_fwd_fp8(qd, kd, vd, o, lse, w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, scale,
+                               w.causal, *descales, stream)
             if st != 0:
                 raise RuntimeError(fa.fa_status_string(st))
     else:
@@ -276,44 +327,25 @@ def main():
         metric = "decode attention HBM GB/s (split-KV, compulsory bytes)"
     else:
         work, unit, bound = flops / 1e12, "TFLOP/s", "mfma"
-        peak = PEAK_F32_TFLOPS if w.dtype == "f32" else PEAK_BF16_TFLOPS
-        metric = METRIC if path != "bwd" else \
-            "attn backward TFLOP/s (2.5x forward FLOPs) and % of MI355X bf16 MFMA peak"
+        peak = {"f32": PEAK_F32_TFLOPS, "e4m3": PEAK_FP8_TFLOPS}.get(w.dtype, PEAK_BF16_TFLOPS)
+        metric = METRIC
+        if path == "bwd":
+            metric = "attn backward TFLOP/s (2.5x forward FLOPs) and % of MI355X bf16 MFMA peak"
+        elif path == "fp8":
+            metric = "attn fwd TFLOP/s with E4M3 inputs and % of MI355X fp8 MFMA peak (N=8k, d=128)"
     value = work / (wall_ms * 1e-3)
     achieved = work / (kernel_ms * 1e-3)
     print(f"[bench] {w.name} ({path}): kernel {kernel_ms:.4f} ms/step (events), wall "
           f"{wall_ms:.4f} ms/step -> {achieved:.1f} {unit} = {100 * achieved / peak:.1f}% of "
           f"{peak} peak", file=sys.stderr, flush=True)
 
-    # Sampled parity of the benchmarked output (a few heads, a few rows each).
-    check = None
-    if args.check_rows > 0 and path != "bwd":
-        from oracle import attention_fp64
-        rng = np.random.default_rng(1)
-        rows = np.unique(np.concatenate([rng.choice(w.Nq, min(args.check_rows, w.Nq), replace=False),
-                                         [0, w.Nq - 1]]))
-        g = w.Hq // w.Hkv
-        errs = []
-        o_cpu, l_cpu = o.cpu(), lse.cpu()
-        for b, h in [(0, 0), (w.B - 1, w.Hq - 1)]:
-            ro, rl = attention_fp64(workloads.to_f64(q[b:b + 1, h:h + 1]),
-                                    workloads.to_f64(k[b:b + 1, h // g:h // g + 1]),
-                                    workloads.to_f64(v[b:b + 1, h // g:h // g + 1]),
-                                    scale, w.causal, rows=rows)
-            go = workloads.to_f64(o_cpu[b:b + 1, h:h + 1])[:, :, rows]
-            gl = l_cpu[b:b + 1, h:h + 1].double().numpy()[:, :, rows]
-            errs.append((float(np.max(np.abs(go - ro))), float(np.max(np.abs(gl - rl)))))
-        check = {"max_abs_err_O": max(e[0] for e in errs),
-                 "max_abs_err_lse": max(e[1] for e in errs),
-                 "rows_checked": int(len(rows)) * len(errs)}
-
     context = None
-    if not args.no_context and w.dtype != "f32" and not hbm_bound and path == "fwd":
-        context = power_context(fa, w, qd, kd, vd, o, lse, scale, stream, dcode)
+    if not args.no_context and w.dtype != "f32" and not hbm_bound and path in ("fwd", "fp8"):
+        context = power_context(fa, w, qd, kd, vd, o, lse, scale, stream, dcode, descales)
 
     cpu = None
     if args.cpu_seconds > 0 and path != "bwd":
-        cpu = cpu_baseline(w, q, k, v, args.cpu_seconds, hbm_bound)
+        cpu = cpu_baseline(w, q, k, v, args.cpu_seconds, hbm_bound, descales, o, lse, scale)
 
     if path == "bwd":
         launch = {"entry": "fa_bwd", "note": "three launches per step: row pass, dK/dV, dQ",
@@ -322,6 +354,10 @@ def main():
         launch = {"entry": "fa_fwd_splitkv", "num_splits": splits, "keys_per_tile": 32,
                   "rows_per_wave": 32, "waves_per_block": 8,
                   "note": "two launches per step: chunk kernel, then combine"}
+    elif path == "fp8":
+        launch = {"entry": "fa_fwd_fp8", "rows_per_block": 256, "keys_per_tile": 64,
+                  "threads_per_block": 512, "blocks": w.B * w.Hq * ((w.Nq + 255) // 256),
+                  "descales": list(descales)}
     else:
         launch = fa.fa_launch_info(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, w.causal, dcode)[1]
     line = {
@@ -349,7 +385,7 @@ def main():
         "context": context,
         "cpu_baseline": None if cpu is None else {k_: cpu[k_] for k_ in
                                                   ("value", "unit", "cores", "kind", "sample")},
-        "parity_sample": check,
+        "parity_sample": None if cpu is None else cpu["parity"],
     }
     print(json.dumps(line), flush=True)
 

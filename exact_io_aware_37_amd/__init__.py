@@ -83,6 +83,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_bwd.argtypes = [_VP] * 9 + [_I] * 6 + [_F, _I, _I, _VP, ctypes.c_size_t, _VP]
     lib.fa_bwd.restype = _I
+    lib.fa_fwd_fp8.argtypes = list(_FWD_ARGS[:13]) + [_F, _F, _F, _VP]
+    lib.fa_fwd_fp8.restype = _I
     _lib = lib
     return lib
 
@@ -161,6 +163,14 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, N_q, N_kv, d, scale, c
     return load_library().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
                                  _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, N_q, N_kv, d, scale,
                                  int(causal), dtype, _ptr(workspace), workspace_bytes, s)
+
+
+def fa_fwd_fp8(q, k, v, o, lse, B, Hq, Hkv, N_q, N_kv, d, scale, causal, descale_q, descale_k,
+               descale_v, stream) -> int:
+    s = stream if (stream is None or isinstance(stream, int)) else stream.cuda_stream
+    return load_library().fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv,
+                                     N_q, N_kv, d, scale, int(causal), descale_q, descale_k,
+                                     descale_v, s)
 
 
 def dtype_code(torch_dtype) -> int:
@@ -247,6 +257,34 @@ def attention_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
     return out, lse
 
 
+def attention_fp8(q, k, v, descale_q: float, descale_k: float, descale_v: float,
+                  causal: bool = False, scale: float | None = None, out=None, lse=None,
+                  stream=None):
+    """E4M3 form of ``attention``: q, k, v are torch.float8_e4m3fn (or uint8 code) GPU
+    tensors whose values are code * descale; returns (out bf16, lse fp32)."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype not in (torch.float8_e4m3fn, torch.uint8):
+            raise FAError(FA_ERR_DTYPE, f"{name} must hold E4M3 codes (float8_e4m3fn or uint8)")
+    B, Hq, Hkv, Nq, Nkv, d = _check_tensors(q, k, v)
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    if out is None:
+        out = torch.empty((B, Hq, Nq, d), dtype=torch.bfloat16, device=q.device)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (B, Hq, Nq, d) or \
+            not out.is_contiguous():
+        raise FAError(FA_ERR_BAD_DIM, "out must be a contiguous bf16 tensor shaped like q")
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = fa_fwd_fp8(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, d, float(scale), causal,
+                    float(descale_q), float(descale_k), float(descale_v), stream)
+    if st != FA_OK:
+        raise FAError(st, fa_status_string(st))
+    return out, lse
+
+
 def attention_backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
                        workspace=None, dq=None, dk=None, dv=None, stream=None):
     """(dq, dk, dv): gradients of sum(o * dout) for o, lse = attention(q, k, v, causal, scale).
@@ -279,6 +317,6 @@ def attention_backward(q, k, v, o, lse, dout, causal: bool = False, scale: float
 
 __all__ = ["fa_fwd", "fa_fwd_stream", "fa_check_args", "fa_status_string", "fa_launch_info",
            "fa_splitkv_workspace_bytes", "fa_splitkv_default_splits", "fa_fwd_splitkv",
-           "fa_bwd_workspace_bytes", "fa_bwd",
-           "attention", "attention_splitkv", "attention_backward", "load_library", "header_functions", "FAError", "dtype_code",
+           "fa_bwd_workspace_bytes", "fa_bwd", "fa_fwd_fp8",
+           "attention", "attention_splitkv", "attention_backward", "attention_fp8", "load_library", "header_functions", "FAError", "dtype_code",
            "FA_F32", "FA_F16", "FA_BF16"]

@@ -63,6 +63,7 @@ struct Params {
   int n_heads;    // B * Hq
   float sl2;      // |scale| * log2(e), or 1 when scale == 0
   int qmode;      // 0: Q as given, 1: negated (scale < 0), 2: zeroed (scale == 0)
+  float oscale;   // factor applied to O at the end (FP8 path: V's dequantisation factor)
 };
 
 // ---------------------------------------------------------------- helpers
@@ -593,6 +594,372 @@ __global__ void __launch_bounds__(kNT16<D>)
     __attribute__((amdgpu_waves_per_eu(kWavesPerEU16<D>, kWavesPerEU16<D>)))
 attn_fwd_mfma16(Params p) {
   attn_fwd_mfma16_body<T, D, CAUSAL>(p);
+}
+
+// ----------------------------------------------------- FP8 (e4m3) path
+//
+// The FlashAttention-3 direction the course page "FlashAttention:
+// IO-aware attention kernel" (section 3.3) and the omica exam notes
+// (section 4.5) name: the same exact tiled algorithm with 8-bit inputs on
+// the matrix cores.  Q, K and V arrive as OCP E4M3 codes with one fp32
+// dequantisation factor each.  The products run on
+// v_mfma_f32_32x32x64_f8f6f4 (fp32 accumulation, products of two E4M3
+// values are exact in fp32): S^T = K Q^T contracts 64 head dimensions per
+// instruction, and O^T += V^T P^T contracts the 64 keys of a whole tile in
+// one instruction per 32 output dimensions, with P rounded to E4M3 (round to
+// nearest even) on the way.  The row sum adds the unrounded fp32
+// probabilities.  Q's and K's factors fold into the exponent scale, V's
+// into the final 1/l; O is written in bf16, lse in fp32.
+//
+// Workgroup, ring, DMA, software pipeline and lazy reference are those of
+// the 16-bit path (256 rows, 64-key tiles, 4-stage ring issued two tiles
+// ahead).  The lazy reference bounds every probability by 2^8, inside
+// E4M3's range (largest finite 448).
+//
+// Operand layouts.  The 8-bit instruction pairs byte j of lane-half h of A
+// with byte j of lane-half h of B, so both operands only need the same
+// assignment of the contraction index to (lane-half, byte):
+//   S:   lane-half h, byte j  <->  head dimension 64*cd + 32*h + j.  Q rows
+//        sit in registers in that order; K rows are read from LDS as two
+//        16-byte chunks.
+//   P*V: lane-half h, byte j = 16*kt + r  <->  key 32*kt + 8*(r/4) + 4*h +
+//        r%4, which is where the S accumulator leaves score r of 32-key block
+//        kt.  P is packed straight from it, four bytes per dword.  V^T comes
+//        from row-major V by four ds_read_b64_tr_b8 per 32 output columns:
+//        within each group of 16 lanes the instruction hands result lane r,
+//        byte t, the byte r%8 of what source lane 2t + r/8 addressed, so
+//        source lane (t, r/8) of lane-group G addresses key row
+//        16*i + 8*(t/4) + 4*(G/2) + t%4 (read i), head-dimension bytes
+//        32*db + 16*(G%2) + 8*(r/8).
+// Swizzles (XOR of the 16-byte chunk index within a row, period 16 rows)
+// keep both reads free of bank conflicts: 16 rows reading one logical K
+// chunk, and the 8 rows x 32 bytes of each half-wave of a V^T read, land on
+// distinct banks.
+
+template <int D>
+struct Cfg8 {
+  static constexpr int NW = 8;                  // waves per workgroup
+  static constexpr int NT = 64 * NW;            // threads per workgroup
+  static constexpr int BR = 32 * NW;            // query rows per workgroup
+  static constexpr int BC = 64;                 // keys per K/V tile
+  static constexpr int KT = BC / 32;            // 32-key blocks of S per tile
+  static constexpr int STAGES = 4;              // LDS ring depth (tiles)
+  static constexpr int ROWB = D;                // bytes per K/V row
+  static constexpr int NCH = D / 16;            // 16-byte chunks per row
+  static constexpr int TILEB = BC * ROWB;       // bytes of one K (or V) tile
+  static constexpr int STAGEB = 2 * TILEB;      // K tile then V tile
+  static constexpr int LDS_BYTES = STAGES * STAGEB;
+  static constexpr int CHUNKS = STAGEB / 1024;  // 1 KiB DMA instructions per tile
+  static constexpr int DPW = CHUNKS / NW;       // ... per wave
+  static_assert(DPW * NW == CHUNKS && DPW >= 1, "DMA split");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+// K: 16 rows reading one logical chunk touch 16 distinct (bank line, chunk)
+// pairs.  V: the XOR moves whole 32-byte blocks (bit 0 of the chunk index is
+// kept), so that rows {0-3, 8-11} (or {4-7, 12-15}) hit distinct banks.
+template <int D>
+__device__ __forceinline__ int swz8_k(int row) { return D == 128 ? ((row >> 1) & 7) : ((row >> 2) & 3); }
+template <int D>
+__device__ __forceinline__ int swz8_v(int row) {
+  return D == 128 ? ((((row >> 1) & 1) | (((row >> 3) & 1) << 1)) << 1) : (((row >> 3) & 1) << 1);
+}
+
+__device__ __forceinline__ f32x16 mma_e4m3(i32x8 a, i32x8 b, f32x16 c) {
+  // Format fields 0 (E4M3 for both operands), no block scales.
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void attn_fwd_e4m3_body(const Params& p) {
+  using C = Cfg8<D>;
+  constexpr int KT = C::KT;
+  __shared__ __attribute__((aligned(1024))) unsigned char k0[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char k1[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char k2[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char k3[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char v0[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char v1[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char v2[C::TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char v3[C::TILEB];
+  auto kst = [&]<int S>() -> lds_t* {
+    if constexpr ((S & 3) == 0) return (lds_t*)k0;
+    else if constexpr ((S & 3) == 1) return (lds_t*)k1;
+    else if constexpr ((S & 3) == 2) return (lds_t*)k2;
+    else return (lds_t*)k3;
+  };
+  auto vst = [&]<int S>() -> lds_t* {
+    if constexpr ((S & 3) == 0) return (lds_t*)v0;
+    else if constexpr ((S & 3) == 1) return (lds_t*)v1;
+    else if constexpr ((S & 3) == 2) return (lds_t*)v2;
+    else return (lds_t*)v3;
+  };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+
+  int b, hq, qt;
+  map_block(p, CAUSAL, b, hq, qt);
+  const int hkv = hq / p.group;
+  const int q0 = qt * C::BR;
+  const int qw0 = q0 + wave * 32;        // first query row of this wave
+  const int myq = qw0 + l32;             // this lane's query row
+
+  const size_t qhead = (size_t)(b * p.Hq + hq) * p.Nq;
+  const size_t kvhead = (size_t)(b * p.Hkv + hkv) * p.Nkv;
+  const rsrc_t rq = make_rsrc(static_cast<const uint8_t*>(p.q) + qhead * D, (uint32_t)p.Nq * C::ROWB);
+  const rsrc_t rk = make_rsrc(static_cast<const uint8_t*>(p.k) + kvhead * D, (uint32_t)p.Nkv * C::ROWB);
+  const rsrc_t rv = make_rsrc(static_cast<const uint8_t*>(p.v) + kvhead * D, (uint32_t)p.Nkv * C::ROWB);
+
+  const int kv_end = CAUSAL ? min(p.Nkv, q0 + C::BR) : p.Nkv;
+  const int n_tiles = (kv_end + C::BC - 1) / C::BC;
+  const int n_main = CAUSAL ? min((q0 + 1) / C::BC, p.Nkv / C::BC) : p.Nkv / C::BC;
+
+  auto issue = [&]<int S>(int t) {
+    const int kv0 = t * C::BC;
+#pragma unroll
+    for (int u = 0; u < C::DPW; ++u) {
+      const int i = wave * C::DPW + u;
+      const bool isv = i >= C::CHUNKS / 2;
+      const int ci = isv ? i - C::CHUNKS / 2 : i;
+      const int slot = ci * 64 + lane;
+      const int row = slot / C::NCH;
+      const int c = (slot % C::NCH) ^ (isv ? swz8_v<D>(row) : swz8_k<D>(row));
+      lds_t* dst = (isv ? vst.template operator()<S>() : kst.template operator()<S>()) + ci * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? rv : rk, (lds_t*)dst, 16,
+                                               (kv0 + row) * C::ROWB + c * 16, 0, 0, 0);
+    }
+  };
+
+  auto advance = [&]<int S>(int t) {
+    if (t + 1 < n_tiles) wait_vm_lgkm<C::DPW>();
+    else wait_vm_lgkm<0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (t + 2 < n_tiles) issue.template operator()<S>(t + 2);
+  };
+
+  issue.template operator()<0>(0);
+  if (n_tiles > 1) issue.template operator()<1>(1);
+
+  // Q operand: 32 bytes per lane and 64-dimension block, rows past N_q read
+  // as zeros.  qmode 1 flips every sign bit (exact negation), 2 zeroes Q.
+  const uint32_t qxor = p.qmode == 1 ? 0x80808080u : 0u;
+  const uint32_t qand = p.qmode == 2 ? 0u : 0xffffffffu;
+  i32x8 qreg[D / 64];
+#pragma unroll
+  for (int cd = 0; cd < D / 64; ++cd) {
+    const int off = myq * D + cd * 64 + half * 32;
+    const u32x4 lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+    const u32x4 hi = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, off + 16, 0, 0));
+    const u32x4 a = (lo ^ qxor) & qand, c = (hi ^ qxor) & qand;
+    qreg[cd] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)c[0], (int)c[1], (int)c[2], (int)c[3]};
+  }
+
+  // Lane bases of the LDS reads (swizzles have period 16 rows and act on
+  // bits that the loop indices only XOR):
+  //   K chunk pair of dims 64*cd + 32*half ..: kbase ^ (cd * 64), second chunk ^ 16
+  //   V^T bytes of output block db:            vbase ^ (db * 32), read i at + 16 i rows
+  const int kbase = l32 * C::ROWB + (((half * 2) ^ swz8_k<D>(l32)) * 16);
+  const int g16 = lane >> 4, s16 = lane & 15, t8 = s16 >> 1;
+  const int vrow = (t8 >> 2) * 8 + (g16 >> 1) * 4 + (t8 & 3);
+  const int vbase = vrow * C::ROWB + swz8_v<D>(vrow) * 16 + (g16 & 1) * 16 + (s16 & 1) * 8;
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
+  float m_run = -INFINITY;   // exponent reference (log2 units), same in both half-waves
+  float l_run = 0.f;         // this lane's part of the row sum, against m_run
+
+  auto compute_s = [&](const lds_t* st, f32x16 (&s)[KT]) {
+    int kb = kbase;
+    asm volatile("" : "+v"(kb));
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) s[kt] = f32x16{};
+#pragma unroll
+    for (int cd = 0; cd < D / 64; ++cd) {
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        const int o = (kb ^ (cd * 64)) + kt * 32 * C::ROWB;
+        const u32x4 x0 = *(const u32x4 __attribute__((address_space(3)))*)(st + o);
+        const u32x4 x1 = *(const u32x4 __attribute__((address_space(3)))*)(st + (o ^ 16));
+        const i32x8 a = {(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                         (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+        s[kt] = mma_e4m3(a, qreg[cd], s[kt]);
+      }
+    }
+  };
+
+  auto compute_pv = [&](const lds_t* st, const i32x8& pk) {
+    int vb = vbase;
+    asm volatile("" : "+v"(vb));
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const lds_t* a0 = st + (vb ^ (db * 32));
+      i32x2 r[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        r[i] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(a0 + i * 16 * C::ROWB));
+      const i32x8 x = {r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
+      acc[db] = mma_e4m3(x, pk, acc[db]);
+    }
+  };
+
+  auto new_reference = [&](const f32x16 (&s)[KT]) -> float {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+    mx = pair_max(mx);
+    const float mc = mx * p.sl2;
+    const float m_new = (mc > m_run + kLazy) ? mc : m_run;
+    const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+    m_run = m_new;
+    return alpha;
+  };
+
+  auto rescale = [&](float alpha) {
+    l_run *= alpha;
+    if (wave_any(alpha != 1.f)) {
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
+    }
+  };
+
+  // P = exp2(s * sl2 - ref) in fp32, summed unrounded, packed to E4M3 in the
+  // byte order of the P*V operand.
+  auto exponentiate = [&](const f32x16 (&s)[KT], i32x8& pk) {
+    const float mu = (m_run == -INFINITY) ? 0.f : m_run;
+    float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float e0 = fast_exp2(fmaf(s[kt][4 * w], p.sl2, -mu));
+        const float e1 = fast_exp2(fmaf(s[kt][4 * w + 1], p.sl2, -mu));
+        const float e2 = fast_exp2(fmaf(s[kt][4 * w + 2], p.sl2, -mu));
+        const float e3 = fast_exp2(fmaf(s[kt][4 * w + 3], p.sl2, -mu));
+        int d = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+        d = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, d, true);
+        pk[kt * 4 + w] = d;
+        ls0 += e0 + e1;
+        ls1 += e2 + e3;
+        // Sum now: left to itself the compiler defers the sums to the end of
+        // the loop body and keeps (or spills) every probability until then.
+        asm volatile("" : "+v"(ls0), "+v"(ls1));
+      }
+    }
+    l_run += ls0 + ls1;
+  };
+
+  f32x16 s_cur[KT];
+  i32x8 pk;
+
+  auto steady = [&]<int R>(int j) {
+    advance.template operator()<(R + 3) & 3>(j + 1);
+    f32x16 s_next[KT];
+    exponentiate(s_cur, pk);                                   // VALU on S(j) ...
+    compute_s(kst.template operator()<(R + 1) & 3>(), s_next); // ... under MFMA S(j+1)
+    compute_pv(vst.template operator()<R>(), pk);              // MFMA O += V(j) P(j) ...
+    rescale(new_reference(s_next));                            // ... under the scan of S(j+1)
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) s_cur[kt] = s_next[kt];
+  };
+  auto last_main = [&]<int R>(int j) {
+    if (j + 1 < n_tiles) advance.template operator()<(R + 3) & 3>(j + 1);
+    exponentiate(s_cur, pk);
+    compute_pv(vst.template operator()<R>(), pk);
+  };
+  auto masked = [&]<int R>(int t) {
+    if (t > n_main || n_main == 0) advance.template operator()<(R + 2) & 3>(t);
+    const int kv0 = t * C::BC;
+    const bool active = (qw0 < p.Nq) && (!CAUSAL || kv0 <= qw0 + 31);
+    if (active) {
+      f32x16 s[KT];
+      compute_s(kst.template operator()<R>(), s);
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + kt * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+          if ((key >= p.Nkv) || (CAUSAL && key > myq)) s[kt][r] = -INFINITY;
+        }
+      }
+      rescale(new_reference(s));
+      exponentiate(s, pk);
+      compute_pv(vst.template operator()<R>(), pk);
+    }
+  };
+
+  if (n_main > 0) {
+    advance.template operator()<2>(0);
+    compute_s(kst.template operator()<0>(), s_cur);
+    rescale(new_reference(s_cur));
+    int j = 0;
+    for (; j + 4 < n_main; j += 4) {
+      steady.template operator()<0>(j);
+      steady.template operator()<1>(j + 1);
+      steady.template operator()<2>(j + 2);
+      steady.template operator()<3>(j + 3);
+    }
+    for (; j + 1 < n_main; ++j) {
+      switch (j & 3) {
+        case 0: steady.template operator()<0>(j); break;
+        case 1: steady.template operator()<1>(j); break;
+        case 2: steady.template operator()<2>(j); break;
+        default: steady.template operator()<3>(j); break;
+      }
+    }
+    switch (j & 3) {
+      case 0: last_main.template operator()<0>(j); break;
+      case 1: last_main.template operator()<1>(j); break;
+      case 2: last_main.template operator()<2>(j); break;
+      default: last_main.template operator()<3>(j); break;
+    }
+  }
+  for (int t = n_main; t < n_tiles; ++t) {
+    switch (t & 3) {
+      case 0: masked.template operator()<0>(t); break;
+      case 1: masked.template operator()<1>(t); break;
+      case 2: masked.template operator()<2>(t); break;
+      default: masked.template operator()<3>(t); break;
+    }
+  }
+
+  // Epilogue: O = acc * (V's factor / l) in bf16, lse in fp32.
+  const rsrc_t ro = make_rsrc(static_cast<uint16_t*>(p.o) + qhead * D, (uint32_t)p.Nq * D * 2u);
+  const rsrc_t rl = make_rsrc(p.lse + qhead, (uint32_t)p.Nq * 4u);
+  const float l_tot = pair_sum(l_run);
+  const float inv = p.oscale / l_tot;
+  using M = Mma16<__bf16>;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      u32x2 w;
+      w[0] = M::pack(acc[db][4 * g] * inv, acc[db][4 * g + 1] * inv);
+      w[1] = M::pack(acc[db][4 * g + 2] * inv, acc[db][4 * g + 3] * inv);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, w), ro,
+                                            (myq * D + db * 32 + g * 8 + half * 4) * 2, 0, 0);
+    }
+  }
+  if (half == 0)
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((m_run + fast_log2(l_tot)) * kLn2), rl,
+                                          myq * 4, 0, 0);
+}
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(Cfg8<D>::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_fwd_e4m3(Params p) {
+  attn_fwd_e4m3_body<D, CAUSAL>(p);
 }
 
 // --------------------------------------------------- split-KV (16-bit) path
@@ -1714,6 +2081,36 @@ int dispatch16(const Params& p, int d, bool causal, long long blocks, hipStream_
   return causal ? run16<T, 128, true>(p, blocks, s) : run16<T, 128, false>(p, blocks, s);
 }
 
+template <int D, bool CAUSAL>
+int run8(const Params& p, long long blocks, hipStream_t stream) {
+  return launch(attn_fwd_e4m3<D, CAUSAL>, 0, p, blocks, Cfg8<D>::NT, stream);
+}
+
+// Host checks of the FP8 entry point (dimensions as for the 16-bit path with
+// 2-byte output elements; the 1-byte inputs are covered by the same limits).
+int check_fp8_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   int B, int Hq, int Hkv, int N_q, int N_kv, int d, float scale, float dsq,
+                   float dsk, float dsv, long long* blocks) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_PTR;
+  const int st = check_dims(B, Hq, Hkv, N_q, N_kv, d, FA_BF16, blocks);
+  if (st != FA_OK) return st;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if (!(isfinite(dsq) && dsq > 0.f) || !(isfinite(dsk) && dsk > 0.f) || !(isfinite(dsv) && dsv > 0.f))
+    return FA_ERR_SCALE;
+  const uintptr_t pq = (uintptr_t)q, pk = (uintptr_t)k, pv = (uintptr_t)v, po = (uintptr_t)o,
+                  pl = (uintptr_t)lse;
+  if (((pq | pk | pv | po) & 15u) != 0 || (pl & 3u) != 0) return FA_ERR_ALIGN;
+  const size_t nq = (size_t)B * Hq * N_q * d;
+  const size_t nkv = (size_t)B * Hkv * N_kv * d;
+  const size_t no = nq * 2;
+  const size_t nl = (size_t)B * Hq * N_q * sizeof(float);
+  if (overlaps(po, no, pq, nq) || overlaps(po, no, pk, nkv) || overlaps(po, no, pv, nkv) ||
+      overlaps(pl, nl, pq, nq) || overlaps(pl, nl, pk, nkv) || overlaps(pl, nl, pv, nkv) ||
+      overlaps(po, no, pl, nl))
+    return FA_ERR_ALIAS;
+  return FA_OK;
+}
+
 // Split-KV geometry for valid dimensions (d, dtype already checked).
 struct SplitGeometry {
   int R, nrb, n_tiles;   // packed rows per kv head, row blocks, 32-key tiles of N_kv
@@ -1877,6 +2274,7 @@ int fa_fwd_stream(const void* q, const void* k, const void* v, void* o, float* l
     p.sl2 = 1.f;
     p.qmode = 2;
   }
+  p.oscale = 1.f;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool c = causal != 0;
   switch (dtype) {
@@ -1891,6 +2289,44 @@ int fa_fwd_stream(const void* q, const void* k, const void* v, void* o, float* l
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
            int Hkv, int N_q, int N_kv, int d, float scale, int causal, int dtype) {
   return fa_fwd_stream(q, k, v, o, lse, B, Hq, Hkv, N_q, N_kv, d, scale, causal, dtype, nullptr);
+}
+
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+               int Hkv, int N_q, int N_kv, int d, float scale, int causal, float descale_q,
+               float descale_k, float descale_v, void* stream) {
+  long long blocks = 0;
+  const int st = check_fp8_args(q, k, v, o, lse, B, Hq, Hkv, N_q, N_kv, d, scale, descale_q,
+                                descale_k, descale_v, &blocks);
+  if (st != FA_OK) return st;
+  Params p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Nq = N_q;
+  p.Nkv = N_kv;
+  p.group = Hq / Hkv;
+  p.n_qtiles = (N_q + Cfg8<128>::BR - 1) / Cfg8<128>::BR;
+  p.n_heads = B * Hq;
+  // Q's and K's factors scale every score: fold them into the exponent scale.
+  const double eff = (double)scale * ((double)descale_q * (double)descale_k);   // exact product
+  const float mag = (float)(fabs(eff) * (double)kLog2e);
+  if (eff != 0.0 && mag > 0.f) {
+    p.sl2 = mag;
+    p.qmode = eff > 0.0 ? 0 : 1;
+  } else {
+    p.sl2 = 1.f;
+    p.qmode = 2;
+  }
+  p.oscale = descale_v;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool c = causal != 0;
+  if (d == 64) return c ? run8<64, true>(p, blocks, s) : run8<64, false>(p, blocks, s);
+  return c ? run8<128, true>(p, blocks, s) : run8<128, false>(p, blocks, s);
 }
 
 size_t fa_splitkv_workspace_bytes(int B, int Hq, int N_q, int d, int num_splits) {

@@ -30,8 +30,9 @@
  *
  * Arithmetic.  dtype FA_BF16 / FA_F16: products on the bf16/f16 matrix
  * cores with fp32 accumulation; probabilities are rounded to the input
- * dtype (round to nearest even) before the P*V product, the normaliser is
- * summed from the unrounded fp32 values.  dtype FA_F32: fp32 matrix cores,
+ * dtype (round to nearest even) before the P*V product, and the normaliser
+ * sums those rounded values in fp32 (O is an exact convex combination of V
+ * rows with the rounded weights).  dtype FA_F32: fp32 matrix cores,
  * no intermediate rounding below fp32.
  *
  * Ownership.  The caller allocates and owns every buffer.  The library
@@ -112,6 +113,37 @@ const char* fa_status_string(int status);
 int fa_launch_info(int B, int Hq, int Hkv, int N_q, int N_kv, int d, int causal,
                    int dtype, int* rows_per_block, int* keys_per_tile,
                    int* threads_per_block, long long* blocks, int* lds_bytes);
+
+/*
+ * FP8 forward: the same operation, masking and layouts with 8-bit inputs,
+ * the FlashAttention-3 direction named by the course page "FlashAttention:
+ * IO-aware attention kernel" (section 3.3) and the omica exam notes (section
+ * 4.5).  q, k and v hold codes of the OCP 8-bit floating point format, E4M3
+ * variant (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, largest
+ * finite 448, NaN codes 0x7F/0xFF, no infinities), one byte per element, in
+ * the layouts of fa_fwd; the element value is code * descale_<tensor>:
+ *
+ *     O   = softmax(scale * (descale_q Q)(descale_k K)^T) (descale_v V)
+ *     lse = its per-row logsumexp (natural log, fp32)
+ *
+ * o is written in bf16 [B, Hq, N_q, d], lse in fp32 [B, Hq, N_q].
+ *
+ * Arithmetic: Q K^T on the 8-bit matrix cores (exact products, fp32
+ * accumulation); probabilities in fp32, rounded to E4M3 (round to nearest
+ * even) for the P V product, whose accumulation is fp32; the normaliser sums
+ * the unrounded fp32 probabilities.  The E4M3 rounding of P is the dominant
+ * error: relative 2^-4 per probability in the normal range.
+ *
+ * scale: any finite value.  descale_q, descale_k, descale_v: finite and
+ * > 0 (FA_ERR_SCALE otherwise).  d: 64 or 128.  Size limits as fa_fwd with
+ * 2-byte elements.  q, k, v, o 16-byte aligned, lse 4-byte aligned
+ * (FA_ERR_ALIGN); o and lse overlap no input or each other (FA_ERR_ALIAS).
+ * One launch on `stream` (NULL = null stream); the library allocates nothing.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int Hq, int Hkv, int N_q, int N_kv, int d,
+               float scale, int causal,
+               float descale_q, float descale_k, float descale_v, void* stream);
 
 /*
  * Split-KV forward (FlashDecoding).  Same operation, arguments, layouts,

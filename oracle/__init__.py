@@ -29,4 +29,5 @@ from .fp8_ref import (  # noqa: F401
     dequantize_e4m3,
     attention_fp8_fp64,
     fp8_p_rounding_bound,
+    fp8_tolerances,
 )

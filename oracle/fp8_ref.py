@@ -19,10 +19,12 @@ Sources:
   bias 7, 3 mantissa bits, subnormals at exponent field 0, no infinities, and
   NaN only for exponent and mantissa fields all ones (largest finite 448).
 
-``fp8_p_rounding_bound`` is the tolerance model of the GPU path, which
-rounds the probabilities to E4M3 before the P*V product (the way the
-FlashAttention-3 line feeds its second product) and divides by the sum of
-the unrounded probabilities.
+``fp8_p_rounding_bound`` and ``fp8_tolerances`` are the tolerance model of
+the GPU path, which rounds the probabilities to E4M3 before the P*V product
+(the way the FlashAttention-3 line feeds its second product), divides by the
+sum of the unrounded probabilities, and forms the scores on a matrix
+instruction that does not sum its 64 products in IEEE fp32 (see
+``SCORE_SUM_REL``).
 """
 
 from __future__ import annotations
@@ -115,3 +117,54 @@ def fp8_p_rounding_bound(q, k, v, scale: float, causal: bool = False, rows=None,
                 per_key = np.maximum(REL_E4M3 * w, np.minimum(w, ABS_E4M3 * wmax))
                 out[b, h, r0:r0 + idx.size] = per_key @ av
     return out
+
+
+# The 8-bit matrix instruction (v_mfma_f32_32x32x64_f8f6f4) forms each of
+# its 64 products exactly but sums them with less than fp32 precision.
+# Measured on MI355X over 2^16 outputs per input family (uniform codes over
+# the whole E4M3 range, quantised normals, cancelling pairs, one dominant
+# product): |error| <= 2^-12.3 * sum|products| and <= 2^-11.2 * max|product|.
+# The tolerance model takes 2^-10 * sum|products| per score, a margin of
+# about 4.6x over the worst case seen; the GPU tests check it on single-key
+# rows, where lse is the score itself.
+SCORE_SUM_REL = 2.0 ** -10
+
+
+def fp8_tolerances(q, k, v, scale: float, causal: bool = False, rows=None):
+    """(tol_o, tol_lse): per-element bounds on |O_gpu - O| and |lse_gpu - lse|.
+
+    q, k, v are the dequantised float64 inputs.  Model:
+      * each score is off by at most d_j = 2^-10 * |scale| * sum_k |q_k k_jk|
+        (``SCORE_SUM_REL``); D = max of d_j over a row's allowed keys;
+      * lse = ln sum exp(s_j) then moves by at most D;
+      * the weights move by a factor within e^(+-2D), so O moves by at most
+        (e^(2D) - 1) * sum_j w_j |v_j| = (e^(2D) - 1) * W, W being the exact
+        attention of |V|, and the E4M3 rounding bound E of those weights grows
+        to at most e^(2D) * E;
+      * O is rounded to bf16 at the end (relative 2^-8), and the fp32 work
+        around it (exp2, sums, the final division) stays below
+        1e-4 * max|V| on O and 1e-5 * (1 + |lse|) on lse.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, Hkv, Nq, Nkv, D = _check_shapes(q, k, v)
+    sigma = abs(_sigma(scale))
+    idx_all = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64).reshape(-1)
+    R = idx_all.size
+    dmax = np.zeros((B, Hq, R), dtype=np.float64)
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            sabs = sigma * (np.abs(q[b, h, idx_all]) @ np.abs(k[b, g]).T)
+            if causal:
+                sabs = np.where(np.arange(Nkv)[None, :] <= idx_all[:, None], sabs, 0.0)
+            dmax[b, h] = SCORE_SUM_REL * sabs.max(axis=1)
+    o, lse = attention_fp64(q, k, v, scale, causal, rows=rows)
+    w_abs, _ = attention_fp64(q, k, np.abs(v), scale, causal, rows=rows)
+    e = fp8_p_rounding_bound(q, k, v, scale, causal, rows=rows)
+    grow = np.exp(2.0 * dmax)[..., None]
+    vmax = float(np.max(np.abs(v))) if v.size else 0.0
+    tol_o = (grow * e + (grow - 1.0) * w_abs) * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(o) + 1e-4 * vmax
+    tol_lse = dmax + 1e-5 * (1.0 + np.abs(lse))
+    return tol_o, tol_lse

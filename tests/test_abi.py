@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol(lib):
     assert set(names) == {"fa_fwd", "fa_fwd_stream", "fa_check_args", "fa_status_string",
                           "fa_launch_info", "fa_splitkv_workspace_bytes",
                           "fa_splitkv_default_splits", "fa_fwd_splitkv",
-                          "fa_bwd_workspace_bytes", "fa_bwd"}
+                          "fa_bwd_workspace_bytes", "fa_bwd", "fa_fwd_fp8"}
     for n in names:
         assert hasattr(lib, n), n
         assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
@@ -243,3 +243,31 @@ def test_bwd_rejects_on_host(lib):
     assert bwd(dk=DO + 64) == fa.FA_ERR_ALIAS
     assert bwd(dv=DK) == fa.FA_ERR_ALIAS         # outputs over each other
     assert bwd(ws=DQ + 16) == fa.FA_ERR_ALIAS
+
+
+def fp8(q=Q, k=K, v=V, o=O, lse=L, dq_=0.01, dk_=0.02, dv_=0.03, **kw):
+    a = args(**kw)
+    return fa.fa_fwd_fp8(q, k, v, o, lse, a["B"], a["Hq"], a["Hkv"], a["N_q"], a["N_kv"], a["d"],
+                         a["scale"], a["causal"], dq_, dk_, dv_, None)
+
+
+def test_fp8_rejects_on_host(lib):
+    for name in ("q", "k", "v", "o", "lse"):
+        assert fp8(**{name: 0}) == fa.FA_ERR_NULL_PTR, name
+    assert fp8(d=96) == fa.FA_ERR_HEAD_DIM
+    assert fp8(Hq=7) == fa.FA_ERR_HEAD_GROUP
+    assert fp8(N_q=0) == fa.FA_ERR_BAD_DIM
+    assert fp8(B=-1) == fa.FA_ERR_BAD_DIM
+    assert fp8(N_kv=1 << 30) == fa.FA_ERR_BAD_DIM
+    assert fp8(scale=math.inf) == fa.FA_ERR_SCALE
+    for bad in (0.0, -0.5, math.nan, math.inf):
+        assert fp8(dq_=bad) == fa.FA_ERR_SCALE
+        assert fp8(dk_=bad) == fa.FA_ERR_SCALE
+        assert fp8(dv_=bad) == fa.FA_ERR_SCALE
+    assert fp8(q=Q + 8) == fa.FA_ERR_ALIGN
+    assert fp8(o=O + 4) == fa.FA_ERR_ALIGN
+    assert fp8(lse=L + 2) == fa.FA_ERR_ALIGN
+    # o holds 2-byte elements over 1-byte inputs: its extent is twice q's
+    nq = 2 * 8 * 100 * 128
+    assert fp8(o=Q + nq - 16) == fa.FA_ERR_ALIAS
+    assert fp8(lse=O + 2 * nq - 16) == fa.FA_ERR_ALIAS

@@ -8,6 +8,10 @@
   (torch's float8_e4m3fn conversion, an independent round-to-nearest-even),
   for every admissible position of the exponent reference; and shown not to
   be vacuous: a coarser format (E5M2) breaks it.
+* ``fp8_tolerances`` against a simulation of both error sources of the GPU
+  path at once (scores moved by the modelled accumulation error, randomly and
+  adversarially, then P rounded), and against its own special case without
+  score error.
 """
 
 import math
@@ -174,3 +178,50 @@ def test_bound_special_cases():
     # rows restricted
     br = fp8_p_rounding_bound(q, k, v, 0.3, rows=[5, 2])
     assert np.array_equal(br[:, :, 0], b[:, :, 5]) and np.array_equal(br[:, :, 1], b[:, :, 2])
+
+
+@pytest.mark.parametrize("name,scale", REGIMES)
+@pytest.mark.parametrize("causal", [False, True])
+def test_tolerances_cover_perturbed_scores_and_rounded_p(name, scale, causal):
+    """Simulate the GPU path's two error sources together: every score moved by up to the
+    modelled accumulation error (random, and adversarially signed against V), P formed
+    against a trailing reference, rounded to E4M3, divided by the unrounded sum."""
+    from oracle import fp8_tolerances
+    from oracle.fp8_ref import SCORE_SUM_REL
+    rng = np.random.default_rng(int(scale * 100) + 7 * causal)
+    q = rng.standard_normal((1, 1, 20, 32)) * 2
+    k = rng.standard_normal((1, 1, 200, 32)) * 2
+    v = rng.standard_normal((1, 1, 200, 32))
+    o_ref, l_ref = attention_fp64(q, k, v, scale, causal)
+    tol_o, tol_l = fp8_tolerances(q, k, v, scale, causal)
+    s = scale * (q[0, 0] @ k[0, 0].T)
+    d = SCORE_SUM_REL * abs(scale) * (np.abs(q[0, 0]) @ np.abs(k[0, 0]).T)
+    mask = np.arange(200)[None, :] <= np.arange(20)[:, None] if causal else np.ones((20, 200), bool)
+    for trial in range(4):
+        if trial < 2:
+            eps = d * rng.uniform(-1, 1, size=d.shape)
+        else:                                   # push weight towards large (or small) v[:, 0]
+            sign = np.sign(v[0, 0, :, 0])[None, :] * (1 if trial == 2 else -1)
+            eps = d * sign
+        st = np.where(mask, s + eps, -np.inf)
+        mx = st.max(axis=1, keepdims=True)
+        p = np.exp(st - mx) * 2.0 ** 3.3         # reference 3.3 (log2) below the maximum
+        pr = torch.from_numpy(p).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+        o = (pr @ v[0, 0]) / p.sum(axis=1, keepdims=True)
+        lse = mx[:, 0] + np.log(np.exp(st - mx).sum(axis=1))
+        assert np.all(np.abs(o - o_ref[0, 0]) <= tol_o[0, 0]), (name, trial)
+        assert np.all(np.abs(lse - l_ref[0, 0]) <= tol_l[0, 0]), (name, trial)
+
+
+def test_tolerances_reduce_to_the_rounding_bound_without_score_error():
+    from oracle import fp8_tolerances
+    rng = np.random.default_rng(8)
+    q = rng.standard_normal((1, 2, 9, 16))
+    k = rng.standard_normal((1, 1, 30, 16))
+    v = rng.standard_normal((1, 1, 30, 16))
+    t0, l0 = fp8_tolerances(q, k, v, 0.0)            # scale 0: no score error at all
+    o, lse = attention_fp64(q, k, v, 0.0)
+    e = fp8_p_rounding_bound(q, k, v, 0.0)
+    assert np.allclose(t0, e * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(o) + 1e-4 * np.abs(v).max(),
+                       rtol=1e-14, atol=0)
+    assert np.allclose(l0, 1e-5 * (1 + np.abs(lse)), rtol=1e-14, atol=0)
