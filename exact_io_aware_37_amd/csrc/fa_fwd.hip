@@ -603,18 +603,21 @@ attn_fwd_mfma16(Params p) {
 // (section 4.5) name: the same exact tiled algorithm with 8-bit inputs on
 // the matrix cores.  Q, K and V arrive as OCP E4M3 codes with one fp32
 // dequantisation factor each.  The products run on
-// v_mfma_f32_32x32x64_f8f6f4 (fp32 accumulation, products of two E4M3
-// values are exact in fp32): S^T = K Q^T contracts 64 head dimensions per
-// instruction, and O^T += V^T P^T contracts the 64 keys of a whole tile in
-// one instruction per 32 output dimensions, with P rounded to E4M3 (round to
-// nearest even) on the way.  The row sum adds the unrounded fp32
-// probabilities.  Q's and K's factors fold into the exponent scale, V's
-// into the final 1/l; O is written in bf16, lse in fp32.
+// v_mfma_f32_32x32x64_f8f6f4 (exact 8-bit products, fp32 accumulators):
+// S^T = K Q^T contracts 64 head dimensions per instruction, and
+// O^T += V^T P^T contracts the 64 keys of a whole tile in one instruction
+// per 32 output dimensions, with P rounded to E4M3 (round to nearest even)
+// on the way.  The row sums of that rounded P come from the matrix cores
+// too (a v_mfma_f32_16x16x128_f8f6f4 per tile), so O is a convex
+// combination of V rows with the rounded weights, and the vector units do
+// no additions for them.  Q's and K's factors fold into the exponent scale,
+// V's into the final 1/l; O is written in bf16, lse in fp32.
 //
-// Workgroup, ring, DMA, software pipeline and lazy reference are those of
-// the 16-bit path (256 rows, 64-key tiles, 4-stage ring issued two tiles
-// ahead).  The lazy reference bounds every probability by 2^8, inside
-// E4M3's range (largest finite 448).
+// Workgroup, ring, DMA and lazy reference are those of the 16-bit path
+// (256 rows, 64-key tiles, 4-stage ring).  The lazy reference bounds every
+// probability by 2^8, inside E4M3's range (largest finite 448).  The
+// unmasked tiles run as a ping-pong between the two halves of the
+// workgroup (described at the loop).
 //
 // Operand layouts.  The 8-bit instruction pairs byte j of lane-half h of A
 // with byte j of lane-half h of B, so both operands only need the same
@@ -702,6 +705,7 @@ __device__ __forceinline__ void attn_fwd_e4m3_body(const Params& p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool second = wave >= C::NW / 2;   // the half of the workgroup that runs half a step behind
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
@@ -722,6 +726,20 @@ __device__ __forceinline__ void attn_fwd_e4m3_body(const Params& p) {
   const int n_tiles = (kv_end + C::BC - 1) / C::BC;
   const int n_main = CAUSAL ? min((q0 + 1) / C::BC, p.Nkv / C::BC) : p.Nkv / C::BC;
 
+  // Q operand first, so that waiting for it never waits for a K/V transfer.
+  const uint32_t qxor = p.qmode == 1 ? 0x80808080u : 0u;
+  const uint32_t qand = p.qmode == 2 ? 0u : 0xffffffffu;
+  i32x8 qreg[D / 64];
+#pragma unroll
+  for (int cd = 0; cd < D / 64; ++cd) {
+    const int off = myq * D + cd * 64 + half * 32;
+    const u32x4 lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+    const u32x4 hi = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, off + 16, 0, 0));
+    const u32x4 a = (lo ^ qxor) & qand, c = (hi ^ qxor) & qand;
+    qreg[cd] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)c[0], (int)c[1], (int)c[2], (int)c[3]};
+  }
+
+  // DMA of tile t into ring stage S (= t mod 4), DPW 1 KiB pieces per wave.
   auto issue = [&]<int S>(int t) {
     const int kv0 = t * C::BC;
 #pragma unroll
@@ -737,36 +755,19 @@ __device__ __forceinline__ void attn_fwd_e4m3_body(const Params& p) {
                                                (kv0 + row) * C::ROWB + c * 16, 0, 0, 0);
     }
   };
-
-  auto advance = [&]<int S>(int t) {
-    if (t + 1 < n_tiles) wait_vm_lgkm<C::DPW>();
-    else wait_vm_lgkm<0>();
+  auto issue_any = [&](int t) {
+    switch (t & 3) {
+      case 0: issue.template operator()<0>(t); break;
+      case 1: issue.template operator()<1>(t); break;
+      case 2: issue.template operator()<2>(t); break;
+      default: issue.template operator()<3>(t); break;
+    }
+  };
+  auto barrier = [&]() {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (t + 2 < n_tiles) issue.template operator()<S>(t + 2);
   };
 
-  issue.template operator()<0>(0);
-  if (n_tiles > 1) issue.template operator()<1>(1);
-
-  // Q operand: 32 bytes per lane and 64-dimension block, rows past N_q read
-  // as zeros.  qmode 1 flips every sign bit (exact negation), 2 zeroes Q.
-  const uint32_t qxor = p.qmode == 1 ? 0x80808080u : 0u;
-  const uint32_t qand = p.qmode == 2 ? 0u : 0xffffffffu;
-  i32x8 qreg[D / 64];
-#pragma unroll
-  for (int cd = 0; cd < D / 64; ++cd) {
-    const int off = myq * D + cd * 64 + half * 32;
-    const u32x4 lo = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
-    const u32x4 hi = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, off + 16, 0, 0));
-    const u32x4 a = (lo ^ qxor) & qand, c = (hi ^ qxor) & qand;
-    qreg[cd] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)c[0], (int)c[1], (int)c[2], (int)c[3]};
-  }
-
-  // Lane bases of the LDS reads (swizzles have period 16 rows and act on
-  // bits that the loop indices only XOR):
-  //   K chunk pair of dims 64*cd + 32*half ..: kbase ^ (cd * 64), second chunk ^ 16
-  //   V^T bytes of output block db:            vbase ^ (db * 32), read i at + 16 i rows
   const int kbase = l32 * C::ROWB + (((half * 2) ^ swz8_k<D>(l32)) * 16);
   const int g16 = lane >> 4, s16 = lane & 15, t8 = s16 >> 1;
   const int vrow = (t8 >> 2) * 8 + (g16 >> 1) * 4 + (t8 & 3);
@@ -775,19 +776,29 @@ __device__ __forceinline__ void attn_fwd_e4m3_body(const Params& p) {
   f32x16 acc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
+  // Row sums of the rounded P come from the matrix cores too, on
+  // v_mfma_f32_16x16x128_f8f6f4 with the P operand unchanged as B: that
+  // instruction reads lane 16g + c as column c, 32-byte group g, so group g
+  // holds half g/2 of query c + 16 (g % 2).  A is 1.0 on the (row, group)
+  // pairs that add up both halves of one query: rows 0 and 8 take groups 0
+  // and 2 (query c), rows 4 and 12 groups 1 and 3 (query c + 16).  Output
+  // register 0 of lane l is row 4 (l / 16), column l % 16: the sum of query
+  // l % 32 over the 64 keys of the tile; the other rows are zero.
+  f32x4 accs = f32x4{};
+  const int rsel = lane & 15, gsel = lane >> 4;
+  const bool on = ((rsel == 0 || rsel == 8) && !(gsel & 1)) || ((rsel == 4 || rsel == 12) && (gsel & 1));
+  const int onev = on ? 0x38383838 : 0;   // E4M3 1.0 in every byte
+  const i32x8 sel = {onev, onev, onev, onev, onev, onev, onev, onev};
   float m_run = -INFINITY;   // exponent reference (log2 units), same in both half-waves
-  float l_run = 0.f;         // this lane's part of the row sum, against m_run
 
   auto compute_s = [&](const lds_t* st, f32x16 (&s)[KT]) {
-    int kb = kbase;
-    asm volatile("" : "+v"(kb));
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) s[kt] = f32x16{};
 #pragma unroll
     for (int cd = 0; cd < D / 64; ++cd) {
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
-        const int o = (kb ^ (cd * 64)) + kt * 32 * C::ROWB;
+        const int o = (kbase ^ (cd * 64)) + kt * 32 * C::ROWB;
         const u32x4 x0 = *(const u32x4 __attribute__((address_space(3)))*)(st + o);
         const u32x4 x1 = *(const u32x4 __attribute__((address_space(3)))*)(st + (o ^ 16));
         const i32x8 a = {(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
@@ -798,11 +809,9 @@ __device__ __forceinline__ void attn_fwd_e4m3_body(const Params& p) {
   };
 
   auto compute_pv = [&](const lds_t* st, const i32x8& pk) {
-    int vb = vbase;
-    asm volatile("" : "+v"(vb));
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const lds_t* a0 = st + (vb ^ (db * 32));
+      const lds_t* a0 = st + (vbase ^ (db * 32));
       i32x2 r[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -810,9 +819,12 @@ __device__ __forceinline__ void attn_fwd_e4m3_body(const Params& p) {
       const i32x8 x = {r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
       acc[db] = mma_e4m3(x, pk, acc[db]);
     }
+    accs = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, pk, accs, 0, 0, 0, 0, 0, 0);
   };
 
-  auto new_reference = [&](const f32x16 (&s)[KT]) -> float {
+  // New exponent reference from a tile of raw scores; O and the sum move to
+  // it (only when it moves: lazy reference).
+  auto rebase = [&](const f32x16 (&s)[KT]) {
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
@@ -823,22 +835,16 @@ __device__ __forceinline__ void attn_fwd_e4m3_body(const Params& p) {
     const float m_new = (mc > m_run + kLazy) ? mc : m_run;
     const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
     m_run = m_new;
-    return alpha;
-  };
-
-  auto rescale = [&](float alpha) {
-    l_run *= alpha;
+    accs[0] *= alpha;
     if (wave_any(alpha != 1.f)) {
 #pragma unroll
       for (int i = 0; i < D / 32; ++i) acc[i] *= alpha;
     }
   };
 
-  // P = exp2(s * sl2 - ref) in fp32, summed unrounded, packed to E4M3 in the
-  // byte order of the P*V operand.
+  // P = exp2(s * sl2 - ref), rounded to E4M3 in the byte order of the P*V operand.
   auto exponentiate = [&](const f32x16 (&s)[KT], i32x8& pk) {
     const float mu = (m_run == -INFINITY) ? 0.f : m_run;
-    float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
@@ -847,97 +853,118 @@ __device__ __forceinline__ void attn_fwd_e4m3_body(const Params& p) {
         const float e1 = fast_exp2(fmaf(s[kt][4 * w + 1], p.sl2, -mu));
         const float e2 = fast_exp2(fmaf(s[kt][4 * w + 2], p.sl2, -mu));
         const float e3 = fast_exp2(fmaf(s[kt][4 * w + 3], p.sl2, -mu));
-        int d = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+        // The first conversion's upper half is rewritten by the second.  It
+        // must not be pk's own register: writing the registers that the last
+        // P*V product takes its B operand from gave wrong products.
+        int d = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, __builtin_nondeterministic_value(0), false);
         d = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, d, true);
         pk[kt * 4 + w] = d;
-        ls0 += e0 + e1;
-        ls1 += e2 + e3;
-        // Sum now: left to itself the compiler defers the sums to the end of
-        // the loop body and keeps (or spills) every probability until then.
-        asm volatile("" : "+v"(ls0), "+v"(ls1));
       }
     }
-    l_run += ls0 + ls1;
   };
 
-  f32x16 s_cur[KT];
+  f32x16 s[KT];
   i32x8 pk;
 
-  auto steady = [&]<int R>(int j) {
-    advance.template operator()<(R + 3) & 3>(j + 1);
-    f32x16 s_next[KT];
-    exponentiate(s_cur, pk);                                   // VALU on S(j) ...
-    compute_s(kst.template operator()<(R + 1) & 3>(), s_next); // ... under MFMA S(j+1)
-    compute_pv(vst.template operator()<R>(), pk);              // MFMA O += V(j) P(j) ...
-    rescale(new_reference(s_next));                            // ... under the scan of S(j+1)
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) s_cur[kt] = s_next[kt];
-  };
-  auto last_main = [&]<int R>(int j) {
-    if (j + 1 < n_tiles) advance.template operator()<(R + 3) & 3>(j + 1);
-    exponentiate(s_cur, pk);
-    compute_pv(vst.template operator()<R>(), pk);
-  };
-  auto masked = [&]<int R>(int t) {
-    if (t > n_main || n_main == 0) advance.template operator()<(R + 2) & 3>(t);
+  issue.template operator()<0>(0);
+  if (n_tiles > 1) issue.template operator()<1>(1);
+  if (n_tiles > 2) issue.template operator()<2>(2);
+
+  // Unmasked tiles.  Per tile j a wave runs a matrix-core phase G(j)
+  // (O += V_j P_j, then S_{j+1} = K_{j+1} Q^T) and a vector phase X(j)
+  // (reference and P_{j+1} from S_{j+1}), separated by workgroup barriers.
+  // The second half of the workgroup runs the same code one barrier later,
+  // so each SIMD holds one wave in G while its other wave is in X (the
+  // ping-pong of FlashAttention-3):
+  //   first half:   X(-1) | G(0) ... X(0) | G(1) ... X(1) | ...
+  //   second half:  X(-1) ......... | G(0) ... X(0) | G(1) ... X(1) | ...
+  // Tile k+3 is issued at the start of step k into the stage of tile k-1,
+  // whose last reader (the second half's G(k-1)) finished one barrier earlier.
+  if (n_main > 0) {
+    if (n_tiles > 2) wait_vm_lgkm<C::DPW>();
+    else wait_vm_lgkm<0>();
+    barrier();
+    compute_s(kst.template operator()<0>(), s);
+    rebase(s);
+    exponentiate(s, pk);
+    if (second) barrier();
+    auto step = [&]<int R>(int k) {
+      if (k + 3 < n_tiles) issue.template operator()<(R + 3) & 3>(k + 3);
+      compute_pv(vst.template operator()<R>(), pk);
+      compute_s(kst.template operator()<(R + 1) & 3>(), s);
+      if (k + 3 < n_tiles) wait_vm_lgkm<C::DPW>();   // tile k+2 has landed
+      else wait_vm_lgkm<0>();
+      barrier();
+      // Keep each phase's work between its barriers: the scores count as
+      // produced here (no max hoisted above), P as consumed (no exp sunk below).
+      asm volatile("" : "+v"(s[0]), "+v"(s[1]));
+      rebase(s);
+      exponentiate(s, pk);
+      asm volatile("" : "+v"(pk));
+      barrier();
+    };
+    int k = 0;
+    for (; k + 4 <= n_main - 1; k += 4) {
+      step.template operator()<0>(k);
+      step.template operator()<1>(k + 1);
+      step.template operator()<2>(k + 2);
+      step.template operator()<3>(k + 3);
+    }
+    for (; k < n_main - 1; ++k) {
+      switch (k & 3) {
+        case 0: step.template operator()<0>(k); break;
+        case 1: step.template operator()<1>(k); break;
+        case 2: step.template operator()<2>(k); break;
+        default: step.template operator()<3>(k); break;
+      }
+    }
+    switch ((n_main - 1) & 3) {
+      case 0: compute_pv(vst.template operator()<0>(), pk); break;
+      case 1: compute_pv(vst.template operator()<1>(), pk); break;
+      case 2: compute_pv(vst.template operator()<2>(), pk); break;
+      default: compute_pv(vst.template operator()<3>(), pk); break;
+    }
+    if (!second) barrier();
+  }
+
+  // Masked tiles (ragged tail, causal diagonal): one tile at a time, every
+  // wave in step.  Tiles up to max(2, n_main + 1) were issued above.
+  const int issued = max(2, n_main + 1);
+  for (int t = n_main; t < n_tiles; ++t) {
+    if (t > issued) issue_any(t);
+    wait_vm_lgkm<0>();
+    barrier();
     const int kv0 = t * C::BC;
     const bool active = (qw0 < p.Nq) && (!CAUSAL || kv0 <= qw0 + 31);
     if (active) {
-      f32x16 s[KT];
-      compute_s(kst.template operator()<R>(), s);
+      auto body = [&]<int R>() {
+        compute_s(kst.template operator()<R>(), s);
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
+        for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + kt * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-          if ((key >= p.Nkv) || (CAUSAL && key > myq)) s[kt][r] = -INFINITY;
+          for (int r = 0; r < 16; ++r) {
+            const int key = kv0 + kt * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+            if ((key >= p.Nkv) || (CAUSAL && key > myq)) s[kt][r] = -INFINITY;
+          }
         }
-      }
-      rescale(new_reference(s));
-      exponentiate(s, pk);
-      compute_pv(vst.template operator()<R>(), pk);
-    }
-  };
-
-  if (n_main > 0) {
-    advance.template operator()<2>(0);
-    compute_s(kst.template operator()<0>(), s_cur);
-    rescale(new_reference(s_cur));
-    int j = 0;
-    for (; j + 4 < n_main; j += 4) {
-      steady.template operator()<0>(j);
-      steady.template operator()<1>(j + 1);
-      steady.template operator()<2>(j + 2);
-      steady.template operator()<3>(j + 3);
-    }
-    for (; j + 1 < n_main; ++j) {
-      switch (j & 3) {
-        case 0: steady.template operator()<0>(j); break;
-        case 1: steady.template operator()<1>(j); break;
-        case 2: steady.template operator()<2>(j); break;
-        default: steady.template operator()<3>(j); break;
+        rebase(s);
+        exponentiate(s, pk);
+        compute_pv(vst.template operator()<R>(), pk);
+      };
+      switch (t & 3) {
+        case 0: body.template operator()<0>(); break;
+        case 1: body.template operator()<1>(); break;
+        case 2: body.template operator()<2>(); break;
+        default: body.template operator()<3>(); break;
       }
     }
-    switch (j & 3) {
-      case 0: last_main.template operator()<0>(j); break;
-      case 1: last_main.template operator()<1>(j); break;
-      case 2: last_main.template operator()<2>(j); break;
-      default: last_main.template operator()<3>(j); break;
-    }
-  }
-  for (int t = n_main; t < n_tiles; ++t) {
-    switch (t & 3) {
-      case 0: masked.template operator()<0>(t); break;
-      case 1: masked.template operator()<1>(t); break;
-      case 2: masked.template operator()<2>(t); break;
-      default: masked.template operator()<3>(t); break;
-    }
+    barrier();
   }
 
   // Epilogue: O = acc * (V's factor / l) in bf16, lse in fp32.
   const rsrc_t ro = make_rsrc(static_cast<uint16_t*>(p.o) + qhead * D, (uint32_t)p.Nq * D * 2u);
   const rsrc_t rl = make_rsrc(p.lse + qhead, (uint32_t)p.Nq * 4u);
-  const float l_tot = pair_sum(l_run);
+  const float l_tot = accs[0];
   const float inv = p.oscale / l_tot;
   using M = Mma16<__bf16>;
 #pragma unroll

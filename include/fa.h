@@ -129,10 +129,13 @@ int fa_launch_info(int B, int Hq, int Hkv, int N_q, int N_kv, int d, int causal,
  * o is written in bf16 [B, Hq, N_q, d], lse in fp32 [B, Hq, N_q].
  *
  * Arithmetic: Q K^T on the 8-bit matrix cores (exact products, fp32
- * accumulation); probabilities in fp32, rounded to E4M3 (round to nearest
- * even) for the P V product, whose accumulation is fp32; the normaliser sums
- * the unrounded fp32 probabilities.  The E4M3 rounding of P is the dominant
- * error: relative 2^-4 per probability in the normal range.
+ * accumulators; the instruction adds its 64 products with somewhat less than
+ * fp32 precision); probabilities in fp32, rounded to E4M3 (round to nearest
+ * even) for the P V product; the normaliser is the sum of those rounded
+ * probabilities, so O is a convex combination of V rows.  The E4M3 rounding
+ * of P is the dominant error: relative 2^-4 per probability in the normal
+ * range, which also bounds the relative error of the summed probabilities
+ * that lse is taken from.
  *
  * scale: any finite value.  descale_q, descale_k, descale_v: finite and
  * > 0 (FA_ERR_SCALE otherwise).  d: 64 or 128.  Size limits as fa_fwd with

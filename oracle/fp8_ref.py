@@ -22,9 +22,10 @@ Sources:
 ``fp8_p_rounding_bound`` and ``fp8_tolerances`` are the tolerance model of
 the GPU path, which rounds the probabilities to E4M3 before the P*V product
 (the way the FlashAttention-3 line feeds its second product), divides by the
-sum of the unrounded probabilities, and forms the scores on a matrix
-instruction that does not sum its 64 products in IEEE fp32 (see
-``SCORE_SUM_REL``).
+sum of those rounded probabilities (the convention of the 16-bit path, so
+that O is a convex combination of V rows), and forms its sums on a matrix
+instruction that does not add its 64 products in IEEE fp32 (see
+``MFMA8_SUM_REL``).
 """
 
 from __future__ import annotations
@@ -75,96 +76,127 @@ def attention_fp8_fp64(q8, k8, v8, descale_q: float, descale_k: float, descale_v
 REL_E4M3 = 2.0 ** -4
 ABS_E4M3 = 2.0 ** -10
 
+# The 8-bit matrix instruction (v_mfma_f32_32x32x64_f8f6f4) forms each of
+# its 64 products exactly but adds them with less than fp32 precision.
+# Measured on MI355X over 2^16 outputs per input family (uniform codes over
+# the whole E4M3 range, quantised normals, cancelling pairs, one dominant
+# product): |error| <= 2^-12.3 * sum|products| and <= 2^-11.2 * max|product|.
+# The tolerance model allows 2^-10 * sum|products| for every such sum (a
+# margin of about 4.6x over the worst case seen): the scores, the P*V
+# products and the row sums; the GPU tests check it on single-key rows,
+# where lse is the score itself.
+MFMA8_SUM_REL = 2.0 ** -10
 
-def fp8_p_rounding_bound(q, k, v, scale: float, causal: bool = False, rows=None,
-                         row_chunk: int = 256) -> np.ndarray:
-    """Per-element bound on |O_gpu - O| caused by rounding P to E4M3.
 
-    The GPU forms p_j = 2^(s_j - r) against an exponent reference r that is
-    never above the row maximum of the scores (it moves to a running maximum),
-    rounds every p_j to E4M3 for the P*V product and divides by the fp32 sum
-    of the unrounded p_j.  With weights w_j = p_j / sum p (the exact softmax
-    row) and w_max their maximum, p_j = c * w_j / w_max for some c >= 1, so
-    the rounding error of key j, divided by the sum, is at most
+def _rows(Nq, rows):
+    return np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64).reshape(-1)
 
-        max(2^-4 * w_j, min(w_j, 2^-10 * w_max))
 
-    for every admissible c.  Summed against |V| this bounds the error of each
-    output element (to first order; the fp32 arithmetic around it is far
-    below).  q, k, v are the dequantised float64 inputs.  Returns an array
-    shaped like the output ([B, Hq, R, D], R = Nq or len(rows)).
+def _rounding_terms(q, k, v, scale, causal, rows, row_chunk=None):
+    """Per-row softmax terms of the rounding model (exact fp64 weights w_j).
+
+    eta_j = max(2^-4 w_j, min(w_j, 2^-10 w_max)) bounds the E4M3 rounding
+    error of key j divided by the row sum, for every position of the
+    exponent reference (see ``fp8_p_rounding_bound``).  Returns, per output
+    element or row:
+      A   = sum_j eta_j |v_j - O|        rho = sum_j eta_j
+      Bw  = sum_j w_j |v_j - O|          W   = sum_j w_j |v_j|
+      S   = max_j |scale| sum_d |q_d k_jd|   (allowed keys), and O.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     B, Hq, Hkv, Nq, Nkv, D = _check_shapes(q, k, v)
     sigma = _sigma(scale)
-    idx_all = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64).reshape(-1)
+    idx_all = _rows(Nq, rows)
     R = idx_all.size
-    out = np.empty((B, Hq, R, D), dtype=np.float64)
+    if row_chunk is None:   # |v_j - O| is materialised per chunk: keep it near 16 Mi elements
+        row_chunk = max(1, min(256, (1 << 24) // max(1, Nkv * D)))
+    A = np.empty((B, Hq, R, D))
+    Bw = np.empty((B, Hq, R, D))
+    W = np.empty((B, Hq, R, D))
+    O = np.empty((B, Hq, R, D))
+    rho = np.empty((B, Hq, R))
+    S = np.empty((B, Hq, R))
     for b in range(B):
         for h in range(Hq):
             g = kv_head_of(h, Hq, Hkv)
-            av = np.abs(v[b, g])
+            vb, kb = v[b, g], k[b, g]
             for r0 in range(0, R, row_chunk):
                 idx = idx_all[r0:r0 + row_chunk]
-                s = sigma * (q[b, h, idx] @ k[b, g].T)
+                sl = slice(r0, r0 + idx.size)
+                s = sigma * (q[b, h, idx] @ kb.T)
+                sabs = abs(sigma) * (np.abs(q[b, h, idx]) @ np.abs(kb).T)
                 if causal:
-                    s = np.where(np.arange(Nkv)[None, :] <= idx[:, None], s, -np.inf)
+                    allowed = np.arange(Nkv)[None, :] <= idx[:, None]
+                    s = np.where(allowed, s, -np.inf)
+                    sabs = np.where(allowed, sabs, 0.0)
                 e = np.exp(s - s.max(axis=1, keepdims=True))
                 w = e / e.sum(axis=1, keepdims=True)
-                wmax = w.max(axis=1, keepdims=True)
-                per_key = np.maximum(REL_E4M3 * w, np.minimum(w, ABS_E4M3 * wmax))
-                out[b, h, r0:r0 + idx.size] = per_key @ av
-    return out
+                eta = np.maximum(REL_E4M3 * w, np.minimum(w, ABS_E4M3 * w.max(axis=1, keepdims=True)))
+                o = w @ vb
+                dev = np.abs(vb[None, :, :] - o[:, None, :])          # |v_j - O| per row
+                A[b, h, sl] = np.einsum("rj,rjd->rd", eta, dev)
+                Bw[b, h, sl] = np.einsum("rj,rjd->rd", w, dev)
+                W[b, h, sl] = w @ np.abs(vb)
+                O[b, h, sl] = o
+                rho[b, h, sl] = eta.sum(axis=1)
+                S[b, h, sl] = sabs.max(axis=1)
+    return A, rho, Bw, W, S, O
 
 
-# The 8-bit matrix instruction (v_mfma_f32_32x32x64_f8f6f4) forms each of
-# its 64 products exactly but sums them with less than fp32 precision.
-# Measured on MI355X over 2^16 outputs per input family (uniform codes over
-# the whole E4M3 range, quantised normals, cancelling pairs, one dominant
-# product): |error| <= 2^-12.3 * sum|products| and <= 2^-11.2 * max|product|.
-# The tolerance model takes 2^-10 * sum|products| per score, a margin of
-# about 4.6x over the worst case seen; the GPU tests check it on single-key
-# rows, where lse is the score itself.
-SCORE_SUM_REL = 2.0 ** -10
+def fp8_p_rounding_bound(q, k, v, scale: float, causal: bool = False, rows=None) -> np.ndarray:
+    """Per-element bound on |O_gpu - O| caused by rounding P to E4M3 alone.
+
+    The GPU forms p_j = 2^(s_j - r) against an exponent reference r that is
+    never above the row maximum of the scores (it moves to a running maximum),
+    rounds every p_j to E4M3 (p~_j) and returns sum_j p~_j v_j / sum_j p~_j.
+    With the exact weights w_j (w_max their maximum), p_j = c * w_j / w_max
+    for some c >= 1, so the rounding error e_j of key j, divided by the exact
+    sum L, is at most eta_j = max(2^-4 w_j, min(w_j, 2^-10 w_max)) for every
+    admissible c.  The rounded weights p~_j / sum p~ then differ from w_j by
+    at most (eta_j + w_j rho) / (1 - rho), rho = sum eta, and since both sets
+    of weights sum to 1,
+        |O_gpu - O| <= (sum_j eta_j |v_j - O| + rho sum_j w_j |v_j - O|) / (1 - rho).
+    q, k, v are the dequantised float64 inputs.  Returns an array shaped like
+    the output ([B, Hq, R, D], R = Nq or len(rows)).
+    """
+    A, rho, Bw, _, _, _ = _rounding_terms(q, k, v, scale, causal, rows)
+    r = rho[..., None]
+    return (A + r * Bw) / (1.0 - r)
 
 
 def fp8_tolerances(q, k, v, scale: float, causal: bool = False, rows=None):
     """(tol_o, tol_lse): per-element bounds on |O_gpu - O| and |lse_gpu - lse|.
 
     q, k, v are the dequantised float64 inputs.  Model:
-      * each score is off by at most d_j = 2^-10 * |scale| * sum_k |q_k k_jk|
-        (``SCORE_SUM_REL``); D = max of d_j over a row's allowed keys;
-      * lse = ln sum exp(s_j) then moves by at most D;
-      * the weights move by a factor within e^(+-2D), so O moves by at most
-        (e^(2D) - 1) * sum_j w_j |v_j| = (e^(2D) - 1) * W, W being the exact
-        attention of |V|, and the E4M3 rounding bound E of those weights grows
-        to at most e^(2D) * E;
+      * every score is off by at most 2^-10 |scale| sum_k |q_k k_jk|
+        (``MFMA8_SUM_REL``); D = its maximum over the row's allowed keys.  The
+        unrounded weights then move by a factor within e^(+-2D): with
+        g = e^(2D), the rounding terms of ``fp8_p_rounding_bound`` grow to at
+        most g eta_j and g rho, and
+          |O_gpu - O| <= (g A + g^2 rho Bw) / (1 - g rho) + (g - 1) Bw
+        with A = sum eta_j |v_j - O|, Bw = sum w_j |v_j - O|;
+      * the P*V sums add at most 2^-10 g W (1 + 2^-4) / (1 - g rho), W the
+        exact attention of |V|;
       * O is rounded to bf16 at the end (relative 2^-8), and the fp32 work
-        around it (exp2, sums, the final division) stays below
-        1e-4 * max|V| on O and 1e-5 * (1 + |lse|) on lse.
+        around it stays below 1e-4 * max|V|;
+      * lse = r + ln(sum p~): it moves by at most D from the scores, by
+        -ln(1 - g rho) from the rounding of the summed probabilities, by
+        2^-10 from the sum's own accumulation, and 1e-5 (1 + |lse|) of fp32.
     """
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
+    A, rho, Bw, W, S, O = _rounding_terms(q, k, v, scale, causal, rows)
+    _, lse = attention_fp64(q, k, v, scale, causal, rows=rows)
+    dmax = MFMA8_SUM_REL * S
+    g = np.exp(2.0 * dmax)
+    gr = (g * rho)[..., None]
+    gg = g[..., None]
+    if np.any(gr >= 1.0):
+        raise ValueError("rounding model not applicable (g * rho >= 1)")
+    e = (gg * A + gg * gr * Bw) / (1.0 - gr) + (gg - 1.0) * Bw
+    e += MFMA8_SUM_REL * gg * W * (1.0 + REL_E4M3) / (1.0 - gr)
     v = np.asarray(v, dtype=np.float64)
-    B, Hq, Hkv, Nq, Nkv, D = _check_shapes(q, k, v)
-    sigma = abs(_sigma(scale))
-    idx_all = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64).reshape(-1)
-    R = idx_all.size
-    dmax = np.zeros((B, Hq, R), dtype=np.float64)
-    for b in range(B):
-        for h in range(Hq):
-            g = kv_head_of(h, Hq, Hkv)
-            sabs = sigma * (np.abs(q[b, h, idx_all]) @ np.abs(k[b, g]).T)
-            if causal:
-                sabs = np.where(np.arange(Nkv)[None, :] <= idx_all[:, None], sabs, 0.0)
-            dmax[b, h] = SCORE_SUM_REL * sabs.max(axis=1)
-    o, lse = attention_fp64(q, k, v, scale, causal, rows=rows)
-    w_abs, _ = attention_fp64(q, k, np.abs(v), scale, causal, rows=rows)
-    e = fp8_p_rounding_bound(q, k, v, scale, causal, rows=rows)
-    grow = np.exp(2.0 * dmax)[..., None]
     vmax = float(np.max(np.abs(v))) if v.size else 0.0
-    tol_o = (grow * e + (grow - 1.0) * w_abs) * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(o) + 1e-4 * vmax
-    tol_lse = dmax + 1e-5 * (1.0 + np.abs(lse))
+    tol_o = e * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(O) + 1e-4 * vmax
+    tol_lse = dmax - np.log1p(-(g * rho)) + MFMA8_SUM_REL + 1e-5 * (1.0 + np.abs(lse))
     return tol_o, tol_lse

@@ -6,12 +6,13 @@ oracle is exact attention of the dequantised values (attention_fp8_fp64).
 Bar, per output element: the oracle's fp8_tolerances, derived from the
 arithmetic of the path.  Its two sources of error:
   * the E4M3 rounding of every probability before P*V (relative 2^-4, or
-    2^-10 absolute in the subnormal range) while the normaliser sums the
-    unrounded values (fp8_p_rounding_bound);
-  * the score sums: the 8-bit matrix instruction forms its 64 products exactly
-    but adds them with less than fp32 precision.  The model allows
-    2^-10 * sum_k |q_k k_k| per score; test_score_accumulation_model checks
-    that on single-key rows, where lse is the score itself.
+    2^-10 absolute in the subnormal range), with the normaliser summing the
+    rounded values (fp8_p_rounding_bound);
+  * the 8-bit matrix instruction forms its 64 products exactly but adds them
+    with less than fp32 precision.  The model allows 2^-10 of the sum of
+    |products| for every such sum (scores, P*V, row sums);
+    test_score_accumulation_model checks it on single-key rows, where lse is
+    the score itself.
 plus the final bf16 rounding of O (2^-8 relative) and the fp32 arithmetic.
 Outputs are poisoned with NaN first, so an unwritten element fails.
 """
@@ -23,7 +24,7 @@ import torch
 import exact_io_aware_37_amd as fa
 import workloads
 from oracle import attention_fp8_fp64, dequantize_e4m3, fp8_tolerances
-from oracle.fp8_ref import SCORE_SUM_REL
+from oracle.fp8_ref import MFMA8_SUM_REL
 
 pytestmark = pytest.mark.gpu
 
@@ -127,7 +128,7 @@ def test_score_accumulation_model(family):
     s = float(np.float32(scale)) * np.einsum("bhnd,bd->bhn", q, k[:, 0, 0])
     sabs = abs(float(np.float32(scale))) * np.einsum("bhnd,bd->bhn", np.abs(q), np.abs(k[:, 0, 0]))
     err = np.abs(l.double().numpy() - s)
-    allow = SCORE_SUM_REL * sabs + 1e-6 * (1 + np.abs(s))
+    allow = MFMA8_SUM_REL * sabs + 1e-6 * (1 + np.abs(s))
     say(f"    max|dS|={err.max():.3e} worst err/allowance {np.max(err / allow):.3f} "
         f"(log2 of worst err/sum|terms|: {np.log2(np.max(err / np.maximum(sabs, 1e-300))):.2f})")
     assert np.all(err <= allow)

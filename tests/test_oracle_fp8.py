@@ -7,7 +7,7 @@
 * ``fp8_p_rounding_bound`` against a simulation of the GPU's rounding of P
   (torch's float8_e4m3fn conversion, an independent round-to-nearest-even),
   for every admissible position of the exponent reference; and shown not to
-  be vacuous: a coarser format (E5M2) breaks it.
+  be vacuous: the slip of dividing by the unrounded sum breaks it.
 * ``fp8_tolerances`` against a simulation of both error sources of the GPU
   path at once (scores moved by the modelled accumulation error, randomly and
   adversarially, then P rounded), and against its own special case without
@@ -114,7 +114,7 @@ def test_quantisation_recipe():
 
 def _simulate(q, k, v, scale, causal, log2_c, fmt=torch.float8_e4m3fn):
     """O with P formed against a reference log2_c below the row maximum, rounded to
-    ``fmt`` (torch's conversion), divided by the sum of the unrounded P."""
+    ``fmt`` (torch's conversion), divided by the sum of the rounded P."""
     w = probabilities_fp64(q, k, scale, causal)             # exact softmax rows
     wmax = w.max(axis=-1, keepdims=True)
     p = (2.0 ** log2_c) * w / wmax
@@ -125,7 +125,7 @@ def _simulate(q, k, v, scale, causal, log2_c, fmt=torch.float8_e4m3fn):
     for b in range(B):
         for h in range(Hq):
             g = h // (Hq // Hkv)
-            o[b, h] = (pr[b, h] @ v[b, g]) / p[b, h].sum(axis=-1, keepdims=True)
+            o[b, h] = (pr[b, h] @ v[b, g]) / pr[b, h].sum(axis=-1, keepdims=True)
     return o
 
 
@@ -147,18 +147,25 @@ def test_bound_holds_for_every_reference_offset(name, scale, causal):
 
 
 def test_bound_is_not_vacuous():
-    """Rounding P to E5M2 (2 mantissa bits, relative error up to 2^-3) breaks the bound."""
+    """A plausible slip, dividing by the sum of the unrounded P, breaks the bound (a V with
+    equal rows makes the rounded-sum error exactly 0); and on random data the true
+    rounding error uses a fair share of the bound."""
     rng = np.random.default_rng(3)
     q = rng.standard_normal((1, 1, 64, 32))
     k = rng.standard_normal((1, 1, 64, 32))
+    v = np.broadcast_to(rng.standard_normal((1, 1, 1, 32)), (1, 1, 64, 32)).copy()
+    o_ref, _ = attention_fp64(q, k, v, 0.6, False)
+    bound = fp8_p_rounding_bound(q, k, v, 0.6, False)
+    w = probabilities_fp64(q, k, 0.6, False)
+    p = (2.0 ** 0.37) * w / w.max(axis=-1, keepdims=True)
+    pr = torch.from_numpy(p).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    o_slip = (pr[0, 0] @ v[0, 0]) / p[0, 0].sum(axis=-1, keepdims=True)
+    assert np.any(np.abs(o_slip - o_ref[0, 0]) > bound[0, 0])
     v = rng.standard_normal((1, 1, 64, 32))
     o_ref, _ = attention_fp64(q, k, v, 0.6, False)
     bound = fp8_p_rounding_bound(q, k, v, 0.6, False)
-    err = np.abs(_simulate(q, k, v, 0.6, False, 0.37, torch.float8_e5m2) - o_ref)
-    assert np.any(err > bound)
-    # and the E4M3 error uses a fair share of it, somewhere
-    err4 = np.abs(_simulate(q, k, v, 0.6, False, 0.37) - o_ref)
-    assert err4.max() > 0.05 * bound.max()
+    err = np.abs(_simulate(q, k, v, 0.6, False, 0.37) - o_ref)
+    assert err.max() > 0.05 * bound.max()
 
 
 def test_bound_special_cases():
@@ -167,14 +174,16 @@ def test_bound_special_cases():
     k = rng.standard_normal((1, 1, 20, 16))
     v = rng.standard_normal((1, 1, 20, 16))
     assert np.all(fp8_p_rounding_bound(q, k, np.zeros_like(v), 0.3) == 0)
+    # the rounded weights still sum to 1: a V whose rows are all equal comes back exactly
+    vc = np.broadcast_to(v[:, :, :1], v.shape).copy()
+    assert np.all(fp8_p_rounding_bound(q, k, vc, 0.3) <= 1e-15)   # |v_j - O| is fp64 rounding only
+    # one key: weight 1, output = that value row, nothing to round away
+    assert np.all(fp8_p_rounding_bound(q, k[:, :, :1], v[:, :, :1], 0.3) == 0)
     b = fp8_p_rounding_bound(q, k, v, 0.3)
     w = probabilities_fp64(q, k, 0.3)
-    upper = 2.0 ** -4 * (w @ np.abs(v[0, 0])) + 2.0 ** -10 * w.max(-1, keepdims=True) * np.abs(v).sum(2)
-    assert np.all(b <= upper + 1e-15)
-    assert np.all(b >= 2.0 ** -4 * (w @ np.abs(v[0, 0])) - 1e-15)
-    # one key: p = c exactly representable only for some c; the bound is 2^-4 |v|
-    b1 = fp8_p_rounding_bound(q, k[:, :, :1], v[:, :, :1], 0.3)
-    assert np.allclose(b1, 2.0 ** -4 * np.abs(v[:, :, :1]), rtol=1e-15, atol=0)
+    o = w[0, 0] @ v[0, 0]
+    dev = np.abs(v[0, 0][None] - o[:, None])
+    assert np.all(b[0, 0] >= 2.0 ** -4 * np.einsum("rj,rjd->rd", w[0, 0], dev) - 1e-15)
     # rows restricted
     br = fp8_p_rounding_bound(q, k, v, 0.3, rows=[5, 2])
     assert np.array_equal(br[:, :, 0], b[:, :, 5]) and np.array_equal(br[:, :, 1], b[:, :, 2])
@@ -187,7 +196,7 @@ def test_tolerances_cover_perturbed_scores_and_rounded_p(name, scale, causal):
     modelled accumulation error (random, and adversarially signed against V), P formed
     against a trailing reference, rounded to E4M3, divided by the unrounded sum."""
     from oracle import fp8_tolerances
-    from oracle.fp8_ref import SCORE_SUM_REL
+    from oracle.fp8_ref import MFMA8_SUM_REL
     rng = np.random.default_rng(int(scale * 100) + 7 * causal)
     q = rng.standard_normal((1, 1, 20, 32)) * 2
     k = rng.standard_normal((1, 1, 200, 32)) * 2
@@ -195,7 +204,7 @@ def test_tolerances_cover_perturbed_scores_and_rounded_p(name, scale, causal):
     o_ref, l_ref = attention_fp64(q, k, v, scale, causal)
     tol_o, tol_l = fp8_tolerances(q, k, v, scale, causal)
     s = scale * (q[0, 0] @ k[0, 0].T)
-    d = SCORE_SUM_REL * abs(scale) * (np.abs(q[0, 0]) @ np.abs(k[0, 0]).T)
+    d = MFMA8_SUM_REL * abs(scale) * (np.abs(q[0, 0]) @ np.abs(k[0, 0]).T)
     mask = np.arange(200)[None, :] <= np.arange(20)[:, None] if causal else np.ones((20, 200), bool)
     for trial in range(4):
         if trial < 2:
@@ -207,8 +216,8 @@ def test_tolerances_cover_perturbed_scores_and_rounded_p(name, scale, causal):
         mx = st.max(axis=1, keepdims=True)
         p = np.exp(st - mx) * 2.0 ** 3.3         # reference 3.3 (log2) below the maximum
         pr = torch.from_numpy(p).to(torch.float8_e4m3fn).to(torch.float64).numpy()
-        o = (pr @ v[0, 0]) / p.sum(axis=1, keepdims=True)
-        lse = mx[:, 0] + np.log(np.exp(st - mx).sum(axis=1))
+        o = (pr @ v[0, 0]) / pr.sum(axis=1, keepdims=True)
+        lse = mx[:, 0] - 3.3 * np.log(2.0) + np.log(pr.sum(axis=1))
         assert np.all(np.abs(o - o_ref[0, 0]) <= tol_o[0, 0]), (name, trial)
         assert np.all(np.abs(lse - l_ref[0, 0]) <= tol_l[0, 0]), (name, trial)
 
@@ -221,7 +230,10 @@ def test_tolerances_reduce_to_the_rounding_bound_without_score_error():
     v = rng.standard_normal((1, 1, 30, 16))
     t0, l0 = fp8_tolerances(q, k, v, 0.0)            # scale 0: no score error at all
     o, lse = attention_fp64(q, k, v, 0.0)
+    w_abs, _ = attention_fp64(q, k, np.abs(v), 0.0)
     e = fp8_p_rounding_bound(q, k, v, 0.0)
-    assert np.allclose(t0, e * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(o) + 1e-4 * np.abs(v).max(),
-                       rtol=1e-14, atol=0)
-    assert np.allclose(l0, 1e-5 * (1 + np.abs(lse)), rtol=1e-14, atol=0)
+    rho = 2.0 ** -4                                    # uniform weights, all in the normal range
+    pv = 2.0 ** -10 * w_abs * (1 + 2.0 ** -4) / (1 - rho)
+    assert np.allclose(t0, (e + pv) * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(o) + 1e-4 * np.abs(v).max(),
+                       rtol=1e-12, atol=0)
+    assert np.allclose(l0, -np.log1p(-rho) + 2.0 ** -10 + 1e-5 * (1 + np.abs(lse)), rtol=1e-12, atol=0)
