@@ -245,6 +245,12 @@ def main():
         (q, k, v), descales, scale = workloads.workload_inputs_fp8(w)
     else:
         q, k, v, scale = workloads.workload_inputs(w)
+    paged = None
+    if w.block_size > 0:
+        # the same keys, held in a paged cache (block tables in device memory)
+        kc, vc, tab, sl = workloads.paginate(k, v, [w.Nkv] * w.B, w.block_size, seed=w.seed)
+        paged = tuple(x.to(dev) for x in (kc, vc, tab, sl))
+        del kc, vc
     qd, kd, vd = (x.to(dev) for x in (q, k, v))
     o = torch.empty(qd.shape, dtype=torch.bfloat16 if fp8 else qd.dtype, device=dev)
     lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
@@ -255,13 +261,33 @@ def main():
     path = args.path if args.path != "auto" else ("splitkv" if w.index == 6 else "fwd")
     if args.backward:
         path = "bwd"
+    if paged is not None:
+        if path not in ("fwd", "paged"):
+            print("the paged workload has the paged split-KV entry point only", file=sys.stderr)
+            sys.exit(2)
+        path = "paged"
+        del kd, vd
     if fp8:
         if path != "fwd":
             print("the E4M3 workload has a forward entry point only", file=sys.stderr)
             sys.exit(2)
         path = "fp8"
     splits = None
-    if path == "splitkv":
+    if path == "paged":
+        kcd, vcd, tbd, sld = paged
+        nb, bs = kcd.shape[0], kcd.shape[1]
+        mbps = tbd.shape[1]
+        splits = args.splits or fa.fa_splitkv_default_splits(w.B, w.Hq, w.Hkv, w.Nq, mbps * bs, w.D,
+                                                              dcode)
+        ws_bytes = fa.fa_splitkv_workspace_bytes(w.B, w.Hq, w.Nq, w.D, splits)
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+        def step():
+            st = fa.fa_fwd_paged(qd, kcd, vcd, tbd, sld, o, lse, w.B, w.Hq, w.Hkv, w.Nq, w.D, nb, bs,
+                                 mbps, scale, w.causal, dcode, splits, workspace, ws_bytes, stream)
+            if st != 0:
+                raise RuntimeError(fa.fa_status_string(st))
+    elif path == "splitkv":
         splits = args.splits or fa.fa_splitkv_default_splits(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D,
                                                               dcode)
         ws_bytes = fa.fa_splitkv_workspace_bytes(w.B, w.Hq, w.Nq, w.D, splits)
@@ -324,11 +350,13 @@ def main():
     # Backward: the algorithmic count is 2.5x the forward's (dV, dP, dQ, dK and
     # the recomputed S: 10*N_q*N_kv*d per head, against 4 for the forward).
     flops = w.flops() * (2.5 if path == "bwd" else 1.0)
-    hbm_bound = path == "splitkv"
+    hbm_bound = path in ("splitkv", "paged")
     if hbm_bound:
         # Decoding reads the whole K/V cache for one query row per head: HBM-bound.
         work, unit, peak, bound = w.io_bytes() / 1e9, "GB/s", PEAK_HBM_GBS, "hbm"
         metric = "decode attention HBM GB/s (split-KV, compulsory bytes)"
+        if path == "paged":
+            metric = "decode attention HBM GB/s (split-KV over a paged cache, compulsory bytes)"
     else:
         work, unit, bound = flops / 1e12, "TFLOP/s", "mfma"
         peak = {"f32": PEAK_F32_TFLOPS, "e4m3": PEAK_FP8_TFLOPS}.get(w.dtype, PEAK_BF16_TFLOPS)
@@ -354,6 +382,10 @@ def main():
     if path == "bwd":
         launch = {"entry": "fa_bwd", "note": "three launches per step: row pass, dK/dV, dQ",
                   "keys_per_block_dkdv": 256, "rows_per_block_dq": 256}
+    elif path == "paged":
+        launch = {"entry": "fa_fwd_paged", "num_splits": splits, "block_size": w.block_size,
+                  "keys_per_tile": 32, "rows_per_wave": 32, "waves_per_block": 8,
+                  "note": "two launches per step: chunk kernel over the block tables, then combine"}
     elif path == "splitkv":
         launch = {"entry": "fa_fwd_splitkv", "num_splits": splits, "keys_per_tile": 32,
                   "rows_per_wave": 32, "waves_per_block": 8,

@@ -85,6 +85,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd.restype = _I
     lib.fa_fwd_fp8.argtypes = list(_FWD_ARGS[:13]) + [_F, _F, _F, _VP]
     lib.fa_fwd_fp8.restype = _I
+    lib.fa_fwd_paged.argtypes = [_VP] * 7 + [_I] * 8 + [_F, _I, _I, _I, _VP, ctypes.c_size_t, _VP]
+    lib.fa_fwd_paged.restype = _I
     _lib = lib
     return lib
 
@@ -171,6 +173,17 @@ def fa_fwd_fp8(q, k, v, o, lse, B, Hq, Hkv, N_q, N_kv, d, scale, causal, descale
     return load_library().fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv,
                                      N_q, N_kv, d, scale, int(causal), descale_q, descale_k,
                                      descale_v, s)
+
+
+def fa_fwd_paged(q, k_cache, v_cache, block_table, seqlens_k, o, lse, B, Hq, Hkv, N_q, d,
+                 num_blocks, block_size, max_blocks_per_seq, scale, causal, dtype, num_splits,
+                 workspace, workspace_bytes, stream) -> int:
+    s = stream if (stream is None or isinstance(stream, int)) else stream.cuda_stream
+    return load_library().fa_fwd_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                       _ptr(seqlens_k), _ptr(o), _ptr(lse), B, Hq, Hkv, N_q, d,
+                                       num_blocks, block_size, max_blocks_per_seq, scale,
+                                       int(causal), dtype, num_splits, _ptr(workspace),
+                                       workspace_bytes, s)
 
 
 def dtype_code(torch_dtype) -> int:
@@ -285,6 +298,54 @@ def attention_fp8(q, k, v, descale_q: float, descale_k: float, descale_v: float,
     return out, lse
 
 
+def attention_paged(q, k_cache, v_cache, block_table, seqlens_k, causal: bool = False,
+                    scale: float | None = None, num_splits: int | None = None, workspace=None,
+                    out=None, lse=None, stream=None):
+    """Split-KV attention of q [B, Hq, N_q, d] over paged caches.
+
+    k_cache, v_cache: [num_blocks, block_size, Hkv, d] GPU tensors of q's dtype;
+    block_table: int32 [B, max_blocks]; seqlens_k: int32 [B] (GPU).  With
+    ``causal`` the N_q queries are the last N_q positions of each sequence.
+    Returns (out, lse).
+    """
+    import torch
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
+                    ("block_table", block_table), ("seqlens_k", seqlens_k)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise FAError(FA_ERR_NULL_PTR, f"{name} must be a contiguous GPU tensor")
+    if block_table.dtype != torch.int32 or seqlens_k.dtype != torch.int32:
+        raise FAError(FA_ERR_DTYPE, "block_table and seqlens_k must be int32")
+    if q.dtype != k_cache.dtype or q.dtype != v_cache.dtype or k_cache.shape != v_cache.shape:
+        raise FAError(FA_ERR_DTYPE, "q, k_cache and v_cache must share dtype; caches one shape")
+    B, Hq, Nq, d = q.shape
+    nb, bs, Hkv, dk = k_cache.shape
+    if dk != d or block_table.dim() != 2 or block_table.shape[0] != B or seqlens_k.shape != (B,):
+        raise FAError(FA_ERR_BAD_DIM, "shape mismatch between q, caches, block_table and seqlens")
+    mbps = block_table.shape[1]
+    dt = dtype_code(q.dtype)
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    if num_splits is None:
+        num_splits = fa_splitkv_default_splits(B, Hq, Hkv, Nq, mbps * bs, d, dt)
+        if num_splits < 1:
+            raise FAError(FA_ERR_BAD_DIM, "no valid split count for these sizes")
+    need = fa_splitkv_workspace_bytes(B, Hq, Nq, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = fa_fwd_paged(q, k_cache, v_cache, block_table, seqlens_k, out, lse, B, Hq, Hkv, Nq, d,
+                      nb, bs, mbps, float(scale), causal, dt, num_splits, workspace,
+                      workspace.numel() * workspace.element_size(), stream)
+    if st != FA_OK:
+        raise FAError(st, fa_status_string(st))
+    return out, lse
+
+
 def attention_backward(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
                        workspace=None, dq=None, dk=None, dv=None, stream=None):
     """(dq, dk, dv): gradients of sum(o * dout) for o, lse = attention(q, k, v, causal, scale).
@@ -317,6 +378,7 @@ def attention_backward(q, k, v, o, lse, dout, causal: bool = False, scale: float
 
 __all__ = ["fa_fwd", "fa_fwd_stream", "fa_check_args", "fa_status_string", "fa_launch_info",
            "fa_splitkv_workspace_bytes", "fa_splitkv_default_splits", "fa_fwd_splitkv",
-           "fa_bwd_workspace_bytes", "fa_bwd", "fa_fwd_fp8",
-           "attention", "attention_splitkv", "attention_backward", "attention_fp8", "load_library", "header_functions", "FAError", "dtype_code",
+           "fa_bwd_workspace_bytes", "fa_bwd", "fa_fwd_fp8", "fa_fwd_paged",
+           "attention", "attention_splitkv", "attention_backward", "attention_fp8",
+           "attention_paged", "load_library", "header_functions", "FAError", "dtype_code",
            "FA_F32", "FA_F16", "FA_BF16"]

@@ -1045,9 +1045,16 @@ struct SplitParams {
   long long rows;   // B * Hq * N_q
   float sl2;
   int qmode;
+  // Paged K/V only (k and v then point at the block pools):
+  const int* btab;     // [B][mbps] pool block of each run of 2^lbs keys of a sequence
+  const int* seqlens;  // [B] keys held for each sequence
+  int mbps;            // block-table row length
+  int lbs;             // log2 of the keys per block
+  int nblocks;         // blocks in each pool
+  uint32_t pool_bytes; // bytes of each pool
 };
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool PAGED>
 __device__ __forceinline__ void attn_splitkv_body(const SplitParams& p) {
   using C = CfgSplit<D>;
   using M = Mma16<T>;
@@ -1088,41 +1095,85 @@ __device__ __forceinline__ void attn_splitkv_body(const SplitParams& p) {
   // same time, so the memory traffic of all waves stays close to a few
   // sequential streams instead of thousands of streams with equal address
   // strides, which collide in the same memory channels.
-  int c1 = p.Nkv;                                                // one past the last key used
-  if (CAUSAL) c1 = min(c1, qi_max + 1);
-  const int t_all = (c1 + C::BC - 1) / C::BC;
+  // Keys of this (batch, key/value head), and the causal offset: query i
+  // sees key j iff j <= i + coff (0 for the dense layout; the paged layout
+  // aligns the N_q queries with the last N_q keys of the sequence).
+  int nkv = p.Nkv, coff = 0;
+  if constexpr (PAGED) {
+    nkv = min(max(p.seqlens[b], 0), p.mbps << p.lbs);
+    coff = nkv - p.Nq;
+  }
+  int c1 = nkv;                                                  // one past the last key used
+  if (CAUSAL) c1 = min(c1, qi_max + coff + 1);
+  const int t_all = c1 > 0 ? (c1 + C::BC - 1) / C::BC : 0;
   const int n_tiles = s < t_all ? (t_all - s + p.S - 1) / p.S : 0;
   auto tile_key0 = [&](int t) { return (s + t * p.S) * C::BC; };
 
   const size_t kvhead = (size_t)(b * p.Hkv + g) * p.Nkv;
-  const rsrc_t rk = make_rsrc(static_cast<const uint16_t*>(p.k) + kvhead * D, (uint32_t)p.Nkv * C::ROWB);
-  const rsrc_t rv = make_rsrc(static_cast<const uint16_t*>(p.v) + kvhead * D, (uint32_t)p.Nkv * C::ROWB);
+  const rsrc_t rk = PAGED ? make_rsrc(p.k, p.pool_bytes)
+                          : make_rsrc(static_cast<const uint16_t*>(p.k) + kvhead * D, (uint32_t)p.Nkv * C::ROWB);
+  const rsrc_t rv = PAGED ? make_rsrc(p.v, p.pool_bytes)
+                          : make_rsrc(static_cast<const uint16_t*>(p.v) + kvhead * D, (uint32_t)p.Nkv * C::ROWB);
+
+  // Byte offset of key `key` of tile t in K or V.  Dense: row `key` of the
+  // head.  Paged: the block table maps key run key >> lbs of the sequence to
+  // a pool block, whose rows hold [token][Hkv][d]; a 32-key tile touches at
+  // most two blocks (2^lbs >= 16), looked up once per tile with scalar loads.
+  // Keys past the sequence (last tile) re-read its last key and are masked;
+  // block numbers are clamped into the pool, so a bad table entry cannot
+  // send a load outside it.
+  struct TileMap {
+    int key0, blk0, id0, id1;
+  };
+  auto tile_map = [&](int t) -> TileMap {
+    TileMap m{tile_key0(t), 0, 0, 0};
+    if constexpr (PAGED) {
+      // Constant address space: the compiler reads the (wave-uniform) entries with scalar loads.
+      const __attribute__((address_space(4))) int* tab =
+          (const __attribute__((address_space(4))) int*)(uintptr_t)p.btab + (size_t)b * p.mbps;
+      const int last = nkv - 1;
+      m.blk0 = m.key0 >> p.lbs;
+      m.id0 = min(max(tab[m.blk0], 0), p.nblocks - 1);
+      m.id1 = min(max(tab[min(m.key0 + 16, last) >> p.lbs], 0), p.nblocks - 1);
+    }
+    return m;
+  };
+  auto key_off = [&](const TileMap& m, int r) -> uint32_t {
+    if constexpr (PAGED) {
+      const int key = min(m.key0 + r, nkv - 1);
+      const int id = (key >> p.lbs) == m.blk0 ? m.id0 : m.id1;
+      return ((uint32_t)(id << p.lbs) + (uint32_t)(key & ((1 << p.lbs) - 1))) *
+                 (uint32_t)(p.Hkv * C::ROWB) + (uint32_t)(g * C::ROWB);
+    } else {
+      return (uint32_t)(m.key0 + r) * C::ROWB;
+    }
+  };
 
   // K fragments of tile t: lane (l32, half) holds key tile_key0(t) + l32, dims
-  // cd*16 + half*8 .. +7 (rows past N_kv read as zeros).
-  auto load_k = [&](int t, u32x4 (&kr)[C::KPT]) {
-    const int off = (tile_key0(t) + l32) * C::ROWB + half * 16;
+  // cd*16 + half*8 .. +7 (dense rows past N_kv read as zeros).
+  auto load_k = [&](const TileMap& m, u32x4 (&kr)[C::KPT]) {
+    const uint32_t off = key_off(m, l32) + half * 16;
 #pragma unroll
     for (int cd = 0; cd < C::KPT; ++cd)
       kr[cd] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, off + cd * 32, 0, 0));
   };
   // DMA of the V rows of tile t into this wave's part of ring stage S.
-  auto issue_v = [&]<int S>(int t) {
-    const int kv0 = tile_key0(t);
+  auto issue_v = [&]<int S>(const TileMap& m) {
 #pragma unroll
     for (int u = 0; u < C::VPT; ++u) {
       const int slot = u * 64 + lane;
       const int row = slot / C::NCH;
       const int c = (slot % C::NCH) ^ swz_v<D>(row);
       lds_t* dst = vst.template operator()<S>() + wave * C::TILEB + u * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst, 16, (kv0 + row) * C::ROWB + c * 16, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst, 16, key_off(m, row) + c * 16, 0, 0, 0);
     }
   };
 
   u32x4 ka[C::KPT], kb[C::KPT];
   if (n_tiles > 0) {
-    load_k(0, ka);
-    issue_v.template operator()<0>(0);
+    const TileMap m0 = tile_map(0);
+    load_k(m0, ka);
+    issue_v.template operator()<0>(m0);
   }
 
   // Q^T operand of the wave's 32 packed rows (zeros past R).
@@ -1159,21 +1210,21 @@ __device__ __forceinline__ void attn_splitkv_body(const SplitParams& p) {
       (void)kn;
       wait_vm_lgkm<0>();
     } else {
-      const int tn = min(t + 1, n_tiles - 1);
-      load_k(tn, kn);
-      issue_v.template operator()<S ^ 1>(tn);
+      const TileMap mn = tile_map(min(t + 1, n_tiles - 1));
+      load_k(mn, kn);
+      issue_v.template operator()<S ^ 1>(mn);
       wait_vm_lgkm<C::KPT + C::VPT>();
     }
     f32x16 sc = f32x16{};
 #pragma unroll
     for (int cd = 0; cd < D / 16; ++cd) sc = M::mma(kc[cd], qreg[cd], sc);
     const int kv0 = tile_key0(t);
-    const bool need_mask = (kv0 + C::BC > c1) || (CAUSAL && kv0 + C::BC - 1 > qi_min);
+    const bool need_mask = (kv0 + C::BC > c1) || (CAUSAL && kv0 + C::BC - 1 > qi_min + coff);
     if (need_mask) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int key = kv0 + (e >> 2) * 8 + half * 4 + (e & 3);
-        if (key >= c1 || (CAUSAL && key > qi)) sc[e] = -INFINITY;
+        if (key >= c1 || (CAUSAL && key > qi + coff)) sc[e] = -INFINITY;
       }
     }
     float mx = -INFINITY;
@@ -1250,10 +1301,10 @@ __device__ __forceinline__ void attn_splitkv_body(const SplitParams& p) {
   }
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool PAGED>
 __global__ void __launch_bounds__(CfgSplit<D>::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_splitkv_mfma16(SplitParams p) {
-  attn_splitkv_body<T, D, CAUSAL>(p);
+  attn_splitkv_body<T, D, CAUSAL, PAGED>(p);
 }
 
 // Merge of the chunk results of every row: lse = ln sum_s exp(lse_s) and
@@ -1308,7 +1359,7 @@ __global__ void __launch_bounds__(256) attn_splitkv_combine(const float* __restr
     f32x4 t = part[0][tid];
 #pragma unroll
     for (int g2 = 1; g2 < G; ++g2) t += part[g2][tid];
-    const float inv = 1.f / wsum;
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;   // a row with no key at all: O = 0, lse = -inf
     T out4[4] = {(T)(t[0] * inv), (T)(t[1] * inv), (T)(t[2] * inv), (T)(t[3] * inv)};
     *reinterpret_cast<u32x2*>(o + row * D + tid * 4) = __builtin_bit_cast(u32x2, out4);
     if (tid == 0) lse[row] = mx + fast_log2(wsum) * kLn2;
@@ -2165,12 +2216,12 @@ int check_split_dims(int B, int Hq, int Hkv, int N_q, int N_kv, int d, int dtype
   return FA_OK;
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool PAGED = false>
 int run_split(const SplitParams& sp, T* o, float* lse, hipStream_t stream) {
   using C = CfgSplit<D>;
   (void)hipGetLastError();
   const long long blocks = (sp.items + C::NW - 1) / C::NW;
-  hipLaunchKernelGGL((attn_splitkv_mfma16<T, D, CAUSAL>), dim3((unsigned)blocks), dim3(C::NT), 0,
+  hipLaunchKernelGGL((attn_splitkv_mfma16<T, D, CAUSAL, PAGED>), dim3((unsigned)blocks), dim3(C::NT), 0,
                      stream, sp);
   hipLaunchKernelGGL((attn_splitkv_combine<T, D>), dim3((unsigned)sp.rows), dim3(256), 0, stream,
                      sp.ows, sp.lws, o, lse, sp.rows, sp.S);
@@ -2183,12 +2234,12 @@ int run_split(const SplitParams& sp, T* o, float* lse, hipStream_t stream) {
   return FA_OK;
 }
 
-template <typename T>
+template <typename T, bool PAGED = false>
 int dispatch_split(const SplitParams& sp, void* o, float* lse, int d, bool causal, hipStream_t s) {
   T* ot = static_cast<T*>(o);
   if (d == 64)
-    return causal ? run_split<T, 64, true>(sp, ot, lse, s) : run_split<T, 64, false>(sp, ot, lse, s);
-  return causal ? run_split<T, 128, true>(sp, ot, lse, s) : run_split<T, 128, false>(sp, ot, lse, s);
+    return causal ? run_split<T, 64, true, PAGED>(sp, ot, lse, s) : run_split<T, 64, false, PAGED>(sp, ot, lse, s);
+  return causal ? run_split<T, 128, true, PAGED>(sp, ot, lse, s) : run_split<T, 128, false, PAGED>(sp, ot, lse, s);
 }
 
 template <typename T, int D, bool CAUSAL>
@@ -2427,10 +2478,99 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
     sp.sl2 = 1.f;
     sp.qmode = 2;
   }
+  sp.btab = nullptr;
+  sp.seqlens = nullptr;
+  sp.mbps = sp.lbs = sp.nblocks = 0;
+  sp.pool_bytes = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool c = causal != 0;
   if (dtype == FA_BF16) return dispatch_split<__bf16>(sp, o, lse, d, c, s);
   return dispatch_split<_Float16>(sp, o, lse, d, c, s);
+}
+
+int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache, const int* block_table,
+                 const int* seqlens_k, void* o, float* lse, int B, int Hq, int Hkv, int N_q, int d,
+                 int num_blocks, int block_size, int max_blocks_per_seq, float scale, int causal,
+                 int dtype, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !block_table || !seqlens_k || !o || !lse || !workspace)
+    return FA_ERR_NULL_PTR;
+  if (dtype != FA_BF16 && dtype != FA_F16) return FA_ERR_DTYPE;
+  if (B < 1 || Hq < 1 || Hkv < 1 || N_q < 1 || num_blocks < 1 || max_blocks_per_seq < 1)
+    return FA_ERR_BAD_DIM;
+  if (Hq % Hkv != 0) return FA_ERR_HEAD_GROUP;
+  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  if (block_size < 16 || block_size > (1 << 16) || (block_size & (block_size - 1)) != 0)
+    return FA_ERR_BAD_DIM;
+  int lbs = 0;
+  while ((1 << lbs) < block_size) ++lbs;
+  const long long max_len = (long long)max_blocks_per_seq << lbs;
+  if (max_len > 0x7fffffffLL - 64) return FA_ERR_BAD_DIM;
+  const size_t es = elem_size(dtype);
+  const unsigned long long pool = (unsigned long long)num_blocks * block_size * Hkv * d * es;
+  if (pool > 0xffffffffULL - 4096) return FA_ERR_BAD_DIM;   // 32-bit buffer offsets
+  if ((long long)B * max_blocks_per_seq > 0x7fffffffLL) return FA_ERR_BAD_DIM;
+  int st = check_split_dims(B, Hq, Hkv, N_q, (int)max_len, d, dtype, num_splits);
+  if (st != FA_OK) return st;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  const size_t need = fa_splitkv_workspace_bytes(B, Hq, N_q, d, num_splits);
+  if (workspace_bytes < need) return FA_ERR_WORKSPACE;
+  const uintptr_t pq = (uintptr_t)q, pk = (uintptr_t)k_cache, pv = (uintptr_t)v_cache,
+                  po = (uintptr_t)o, pl = (uintptr_t)lse, pt = (uintptr_t)block_table,
+                  pn = (uintptr_t)seqlens_k, pw = (uintptr_t)workspace;
+  if (((pq | pk | pv | po | pw) & 15u) != 0 || ((pl | pt | pn) & 3u) != 0) return FA_ERR_ALIGN;
+  const size_t nq = (size_t)B * Hq * N_q * d * es;
+  const size_t nl = (size_t)B * Hq * N_q * sizeof(float);
+  const size_t nt = (size_t)B * max_blocks_per_seq * sizeof(int);
+  const size_t nn = (size_t)B * sizeof(int);
+  const uintptr_t outs[3] = {po, pl, pw};
+  const size_t outn[3] = {nq, nl, need};
+  const uintptr_t ins[5] = {pq, pk, pv, pt, pn};
+  const size_t inn[5] = {nq, (size_t)pool, (size_t)pool, nt, nn};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 5; ++j)
+      if (overlaps(outs[i], outn[i], ins[j], inn[j])) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], outn[i], outs[j], outn[j])) return FA_ERR_ALIAS;
+  }
+
+  const SplitGeometry g = split_geometry(Hq, Hkv, N_q, (int)max_len);
+  SplitParams sp;
+  sp.q = q;
+  sp.k = k_cache;
+  sp.v = v_cache;
+  sp.rows = (long long)B * Hq * N_q;
+  sp.ows = static_cast<float*>(workspace);
+  sp.lws = sp.ows + (size_t)num_splits * sp.rows * d;
+  sp.B = B;
+  sp.Hq = Hq;
+  sp.Hkv = Hkv;
+  sp.Nq = N_q;
+  sp.Nkv = (int)max_len;
+  sp.group = Hq / Hkv;
+  sp.R = g.R;
+  sp.nrb = g.nrb;
+  sp.S = num_splits;
+  sp.items = (long long)B * Hkv * g.nrb * num_splits;
+  if (scale > 0.f) {
+    sp.sl2 = scale * kLog2e;
+    sp.qmode = 0;
+  } else if (scale < 0.f) {
+    sp.sl2 = -scale * kLog2e;
+    sp.qmode = 1;
+  } else {
+    sp.sl2 = 1.f;
+    sp.qmode = 2;
+  }
+  sp.btab = block_table;
+  sp.seqlens = seqlens_k;
+  sp.mbps = max_blocks_per_seq;
+  sp.lbs = lbs;
+  sp.nblocks = num_blocks;
+  sp.pool_bytes = (uint32_t)pool;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool c = causal != 0;
+  if (dtype == FA_BF16) return dispatch_split<__bf16, true>(sp, o, lse, d, c, s);
+  return dispatch_split<_Float16, true>(sp, o, lse, d, c, s);
 }
 
 }  // extern "C"

@@ -201,6 +201,51 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Split-KV forward over paged K/V caches, for serving.  The course page
+ * "FlashAttention: IO-aware attention kernel" (section 4, reading vLLM's
+ * flash-attention backend) has the serving engine hand the kernel the query,
+ * a paged K/V cache and its block tables.  Each sequence's keys live in
+ * fixed-size blocks of a shared pool:
+ *
+ *     k_cache, v_cache  [num_blocks][block_size][Hkv][d]   dtype
+ *     block_table       [B][max_blocks_per_seq]            int32
+ *     seqlens_k         [B]                                int32
+ *
+ * key j of sequence b is slot j % block_size of block
+ * block_table[b][j / block_size] (the cache layout vLLM's flash-attention
+ * backend passes).  Only entries for j < seqlens_k[b] are read; keys, table
+ * entries and lengths live in device memory and are read by the kernels, so
+ * a caller can rewrite them between launches without any host work.
+ *
+ *     q [B][Hq][N_q][d], o [B][Hq][N_q][d] (dtype), lse [B][Hq][N_q] (fp32)
+ *
+ * The N_q queries of sequence b are its last N_q positions: with causal != 0
+ * query i sees key j iff j <= seqlens_k[b] - N_q + i (decoding: N_q = 1 sees
+ * every key either way).  A row that sees no key (seqlens_k[b] <= 0, or an
+ * early query of a short sequence) gets O = 0 and lse = -inf.  Values of
+ * seqlens_k above max_blocks_per_seq * block_size are taken as that maximum,
+ * and block numbers outside [0, num_blocks) are clamped into it: a bad table
+ * gives wrong values, never an access outside the caches.
+ *
+ * Work split, chunk results and merge: those of fa_fwd_splitkv, with N_kv =
+ * max_blocks_per_seq * block_size for the split count and workspace size
+ * (fa_splitkv_workspace_bytes, fa_splitkv_default_splits).  dtype FA_BF16 or
+ * FA_F16; d 64 or 128; block_size a power of two in [16, 65536]; each cache
+ * below 4 GiB (num_blocks * block_size * Hkv * d * elem_size < 2^32 - 4096)
+ * and B * max_blocks_per_seq < 2^31, else FA_ERR_BAD_DIM.  q, the caches,
+ * o and the workspace 16-byte aligned; lse, block_table and seqlens_k
+ * 4-byte aligned (FA_ERR_ALIGN).  o, lse and the workspace overlap no input
+ * and each other (FA_ERR_ALIAS).  Two launches on `stream`; the library
+ * allocates nothing.
+ */
+int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
+                 const int* block_table, const int* seqlens_k, void* o, float* lse,
+                 int B, int Hq, int Hkv, int N_q, int d,
+                 int num_blocks, int block_size, int max_blocks_per_seq,
+                 float scale, int causal, int dtype, int num_splits,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Backward pass: gradients of the scalar sum(O * dO) with respect to q, k
  * and v, for the forward above (same arguments, layouts and masking), by
  * recomputation as the kyonqi walkthrough ("Flash Attention Backward") and

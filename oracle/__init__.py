@@ -18,6 +18,9 @@ from .attention_ref import (  # noqa: F401
     attention_bwd_fp64,
     attention_bwd_fp64_rows,
     attention_fp64_key_range,
+    attention_fp64_kv_cache,
+    attention_fp64_paged,
+    gather_paged,
     attention_bruteforce,
     attention_online_blocked,
     probabilities_fp64,

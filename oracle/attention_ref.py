@@ -401,3 +401,72 @@ def attention_online_blocked(q, k, v, scale: float, causal: bool = False,
             o_out[b, h] = acc / l[:, None]
             lse[b, h] = m + np.log(l)
     return o_out, lse
+
+
+def attention_fp64_kv_cache(q, k, v, scale: float, causal: bool = False):
+    """Exact attention of N_q new queries against a cache of N keys, in float64.
+
+    q: [Hq, N_q, D]; k, v: [Hkv, N, D] (one sequence).  The queries are the
+    last N_q positions of the sequence, so with ``causal`` query i sees key j
+    iff j <= N - N_q + i (the cache's bottom-right alignment; it equals the
+    top-left rule of ``attention_fp64`` when N_q == N).  [P1]'s vLLM reading
+    (§4) hands the kernel this kind of cache together with its block tables.
+    A row with no allowed key gets O = 0 and lse = -inf.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    Hq, Nq, D = q.shape
+    Hkv, N = k.shape[0], k.shape[1]
+    sigma = _sigma(scale)
+    o = np.zeros((Hq, Nq, D))
+    lse = np.full((Hq, Nq), -np.inf)
+    if N == 0:
+        return o, lse
+    allowed = np.ones((Nq, N), dtype=bool)
+    if causal:
+        allowed = np.arange(N)[None, :] <= (N - Nq) + np.arange(Nq)[:, None]
+    live = allowed.any(axis=1)
+    for h in range(Hq):
+        g = kv_head_of(h, Hq, Hkv)
+        s = np.where(allowed, sigma * (q[h] @ k[g].T), -np.inf)[live]
+        m = s.max(axis=1)
+        e = np.exp(s - m[:, None])
+        l = e.sum(axis=1)
+        o[h, live] = (e / l[:, None]) @ v[g]
+        lse[h, live] = m + np.log(l)
+    return o, lse
+
+
+def gather_paged(cache, block_table_row, n: int):
+    """Keys 0..n-1 of one sequence from a paged cache, as [Hkv, n, D].
+
+    cache: [num_blocks, block_size, Hkv, D]; key j lives in block
+    block_table_row[j // block_size], slot j % block_size.
+    """
+    cache = np.asarray(cache)
+    bs = cache.shape[1]
+    j = np.arange(n)
+    rows = cache[np.asarray(block_table_row)[j // bs], j % bs]     # [n, Hkv, D]
+    return np.ascontiguousarray(rows.transpose(1, 0, 2))
+
+
+def attention_fp64_paged(q, k_cache, v_cache, block_table, seqlens, scale: float,
+                         causal: bool = False):
+    """Exact attention over paged K/V caches, in float64.
+
+    q: [B, Hq, N_q, D]; k_cache, v_cache: [num_blocks, block_size, Hkv, D];
+    block_table: [B, max_blocks]; seqlens: [B].  Sequence b is gathered
+    through its block-table row and attended with ``attention_fp64_kv_cache``.
+    Returns (o [B, Hq, N_q, D], lse [B, Hq, N_q]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, Nq, D = q.shape
+    o = np.zeros((B, Hq, Nq, D))
+    lse = np.full((B, Hq, Nq), -np.inf)
+    for b in range(B):
+        n = int(seqlens[b])
+        k = gather_paged(k_cache, block_table[b], n).astype(np.float64)
+        v = gather_paged(v_cache, block_table[b], n).astype(np.float64)
+        o[b], lse[b] = attention_fp64_kv_cache(q[b], k, v, scale, causal)
+    return o, lse

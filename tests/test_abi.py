@@ -36,7 +36,8 @@ def test_library_exports_every_declared_symbol(lib):
     assert set(names) == {"fa_fwd", "fa_fwd_stream", "fa_check_args", "fa_status_string",
                           "fa_launch_info", "fa_splitkv_workspace_bytes",
                           "fa_splitkv_default_splits", "fa_fwd_splitkv",
-                          "fa_bwd_workspace_bytes", "fa_bwd", "fa_fwd_fp8"}
+                          "fa_bwd_workspace_bytes", "fa_bwd", "fa_fwd_fp8",
+                          "fa_fwd_paged"}
     for n in names:
         assert hasattr(lib, n), n
         assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
@@ -271,3 +272,39 @@ def test_fp8_rejects_on_host(lib):
     nq = 2 * 8 * 100 * 128
     assert fp8(o=Q + nq - 16) == fa.FA_ERR_ALIAS
     assert fp8(lse=O + 2 * nq - 16) == fa.FA_ERR_ALIAS
+
+
+KC, VC, TB, SL, WS = 0x60000000, 0x70000000, 0x80000000, 0x90000000, 0xA0000000
+PG = dict(B=2, Hq=8, Hkv=2, N_q=1, d=128, num_blocks=64, block_size=16, mbps=32, scale=0.125,
+          causal=0, dtype=fa.FA_BF16, splits=4)
+
+
+def paged(q=Q, kc=KC, vc=VC, tb=TB, sl=SL, o=O, lse=L, ws=WS, ws_bytes=1 << 20, **kw):
+    a = dict(PG)
+    a.update(kw)
+    return fa.fa_fwd_paged(q, kc, vc, tb, sl, o, lse, a["B"], a["Hq"], a["Hkv"], a["N_q"], a["d"],
+                           a["num_blocks"], a["block_size"], a["mbps"], a["scale"], a["causal"],
+                           a["dtype"], a["splits"], ws, ws_bytes, None)
+
+
+def test_paged_rejects_on_host(lib):
+    for name in ("q", "kc", "vc", "tb", "sl", "o", "lse", "ws"):
+        assert paged(**{name: 0}) == fa.FA_ERR_NULL_PTR, name
+    assert paged(dtype=fa.FA_F32) == fa.FA_ERR_DTYPE
+    assert paged(d=96) == fa.FA_ERR_HEAD_DIM
+    assert paged(Hq=7) == fa.FA_ERR_HEAD_GROUP
+    for bs in (8, 24, 0, -16, 1 << 17):
+        assert paged(block_size=bs) == fa.FA_ERR_BAD_DIM, bs
+    assert paged(num_blocks=0) == fa.FA_ERR_BAD_DIM
+    assert paged(mbps=0) == fa.FA_ERR_BAD_DIM
+    assert paged(num_blocks=1 << 20, block_size=256) == fa.FA_ERR_BAD_DIM   # cache >= 4 GiB
+    assert paged(splits=0) == fa.FA_ERR_BAD_DIM
+    assert paged(splits=17) == fa.FA_ERR_BAD_DIM       # 32 blocks x 16 keys = 16 tiles
+    assert paged(scale=math.nan) == fa.FA_ERR_SCALE
+    assert paged(ws_bytes=64) == fa.FA_ERR_WORKSPACE
+    assert paged(kc=KC + 8) == fa.FA_ERR_ALIGN
+    assert paged(tb=TB + 2) == fa.FA_ERR_ALIGN
+    assert paged(sl=SL + 1) == fa.FA_ERR_ALIGN
+    assert paged(o=KC + 64) == fa.FA_ERR_ALIAS          # output inside a cache
+    assert paged(ws=TB) == fa.FA_ERR_ALIAS              # workspace over the block table
+    assert paged(lse=O + 16) == fa.FA_ERR_ALIAS         # outputs over each other

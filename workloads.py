@@ -14,8 +14,10 @@ sequence against a 32768-key cache, batch 8), the case the same page (§3,
 where the method helps and where it does not) sends to the split-KV
 FlashDecoding variant.  Workload 7 is workload 3's shape with 8-bit E4M3
 inputs (the FP8 direction the pages name for FlashAttention-3), quantised from
-the same kind of draws by ``make_inputs_fp8``.  No public dataset is
-involved; nothing is read from disk.
+the same kind of draws by ``make_inputs_fp8``.  Workload 8 is workload 6
+with its K/V cache scattered into 16-key blocks of a paged cache
+(``paginate``), the form a serving engine keeps a cache in.  No public
+dataset is involved; nothing is read from disk.
 
 Recipe (all workloads): ``numpy.random.default_rng(seed)`` (PCG64), draw Q,
 then K, then (for outlier workloads) the outlier rows of K, then V, each as
@@ -52,6 +54,7 @@ class Workload:
     sigma: float = 1.0
     outlier_frac: float = 0.0
     outlier_mult: float = 8.0
+    block_size: int = 0          # > 0: K/V held in a paged cache of blocks of this many keys
 
     @property
     def seed(self) -> int:
@@ -90,6 +93,8 @@ WORKLOADS = {
                 True, sigma=0.5, outlier_frac=0.01, outlier_mult=8.0),
     6: Workload(6, "decode_gqa_7b_b8_n32768", 8, 28, 4, 1, 32768, 128, "bf16", False),
     7: Workload(7, "long_noncausal_e4m3_n8192_d128", 2, 32, 32, 8192, 8192, 128, "e4m3", False),
+    8: Workload(8, "decode_gqa_7b_b8_n32768_paged_bs16", 8, 28, 4, 1, 32768, 128, "bf16", False,
+                block_size=16),
 }
 
 
@@ -148,6 +153,43 @@ def workload_inputs_fp8(w: Workload):
     codes, ds = make_inputs_fp8(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, w.seed, w.sigma,
                                 w.outlier_frac, w.outlier_mult)
     return codes, ds, w.scale
+
+
+def paginate(k: torch.Tensor, v: torch.Tensor, seqlens, block_size: int, seed: int = 0,
+             spare_blocks: int = 2):
+    """Scatter dense K/V [B, Hkv, N, D] into paged caches, as a serving engine would hold them.
+
+    Returns (k_cache, v_cache, block_table, seqlens): caches
+    [num_blocks, block_size, Hkv, D] (the layout vLLM's flash-attention backend
+    passes to its kernel), int32 block_table [B, max_blocks] and int32
+    seqlens [B].  Sequence b's keys 0..seqlens[b]-1 go to blocks drawn from a
+    seeded permutation of the pool; table entries past a sequence's blocks are
+    -1.  Every slot that holds no key (spare blocks, the tail of a sequence's
+    last block) is NaN, so a read outside the table's keys shows in results.
+    """
+    B, Hkv, N, D = k.shape
+    lens = [int(x) for x in seqlens]
+    assert len(lens) == B and all(0 <= n <= N for n in lens)
+    nblk = [(n + block_size - 1) // block_size for n in lens]
+    total = sum(nblk) + spare_blocks
+    perm = np.random.default_rng(seed).permutation(total)
+    kc = torch.full((total, block_size, Hkv, D), float("nan"), dtype=k.dtype)
+    vc = torch.full((total, block_size, Hkv, D), float("nan"), dtype=v.dtype)
+    table = torch.full((B, max(1, max(nblk))), -1, dtype=torch.int32)
+    nxt = 0
+    for b in range(B):
+        ids = torch.from_numpy(perm[nxt:nxt + nblk[b]].astype(np.int64))
+        nxt += nblk[b]
+        table[b, :nblk[b]] = ids.to(torch.int32)
+        full = lens[b] // block_size
+        if full:
+            kc[ids[:full]] = k[b, :, :full * block_size].reshape(Hkv, full, block_size, D).permute(1, 2, 0, 3)
+            vc[ids[:full]] = v[b, :, :full * block_size].reshape(Hkv, full, block_size, D).permute(1, 2, 0, 3)
+        rest = lens[b] - full * block_size
+        if rest:
+            kc[ids[full], :rest] = k[b, :, full * block_size:lens[b]].permute(1, 0, 2)
+            vc[ids[full], :rest] = v[b, :, full * block_size:lens[b]].permute(1, 0, 2)
+    return kc.contiguous(), vc.contiguous(), table, torch.tensor(lens, dtype=torch.int32)
 
 
 def codes_of(t: torch.Tensor) -> np.ndarray:
