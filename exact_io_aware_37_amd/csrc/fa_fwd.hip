@@ -1109,7 +1109,18 @@ __device__ __forceinline__ void attn_splitkv_body(const SplitParams& p) {
   if (CAUSAL) c1 = min(c1, qi_max + coff + 1);
   const int t_all = c1 > 0 ? (c1 + C::BC - 1) / C::BC : 0;
   const int n_tiles = s < t_all ? (t_all - s + p.S - 1) / p.S : 0;
-  auto tile_key0 = [&](int t) { return (s + t * p.S) * C::BC; };
+  // Dense layout: each (batch, key/value head) starts its sequence of tiles
+  // at a different position (and wraps around).  The heads' K/V blocks are
+  // equally aligned, so without it all heads would stream the same offsets
+  // at the same time.  The paged layout keeps the plain order: the key/value
+  // heads of a sequence share each pool block, and reading it together is
+  // faster.
+  const int rot = (n_tiles > 0 && !PAGED) ? (b * p.Hkv + g) % n_tiles : 0;
+  auto tile_key0 = [&](int t) {
+    int u = t + rot;
+    u -= (u >= n_tiles) ? n_tiles : 0;
+    return (s + u * p.S) * C::BC;
+  };
 
   const size_t kvhead = (size_t)(b * p.Hkv + g) * p.Nkv;
   const rsrc_t rk = PAGED ? make_rsrc(p.k, p.pool_bytes)
@@ -1311,9 +1322,12 @@ attn_splitkv_mfma16(SplitParams p) {
 
 // Merge of the chunk results of every row: lse = ln sum_s exp(lse_s) and
 // O = sum_s exp(lse_s - lse) O_s, rounded once to the output type.  One
-// workgroup per row: the chunk weights are formed in parallel, then G groups
-// of D/4 threads (4 head dimensions each) sum a strided subset of the chunks
-// with independent loads, and LDS adds the G partial sums.
+// workgroup per row.  The kernel is a chain of dependent steps on a small
+// amount of data, so its time is latency: the chunk partials are loaded
+// before the weights are known (they do not depend on them), the max and
+// the sum of the weights are wave butterflies with one barrier each, then
+// G groups of D/4 threads (4 head dimensions each) sum a strided subset of
+// the chunks and LDS adds the G partial sums.
 template <typename T, int D>
 __global__ void __launch_bounds__(256) attn_splitkv_combine(const float* __restrict__ ows,
                                                              const float* __restrict__ lws,
@@ -1321,37 +1335,53 @@ __global__ void __launch_bounds__(256) attn_splitkv_combine(const float* __restr
                                                              long long rows, int S) {
   constexpr int LPR = D / 4;            // threads per dimension sweep
   constexpr int G = 256 / LPR;          // chunk groups
+  constexpr int PRE = 8;                // chunk partials per thread loaded ahead of the weights
   __shared__ float w_s[FA_SPLITKV_MAX_SPLITS];
-  __shared__ float red[256];
+  __shared__ float red[2][4];
   __shared__ f32x4 part[G][LPR];
   const long long row = blockIdx.x;
   const int tid = threadIdx.x;
+  const int wv_id = tid >> 6;
+  const int c = tid % LPR, grp = tid / LPR;
 
-  // Largest chunk lse (S <= 256: one value per thread).
+  // Every load that does not depend on the weights is issued first: this
+  // thread's chunk lse and its first PRE chunk partials.
   const float lv = tid < S ? lws[(size_t)tid * rows + row] : -INFINITY;
-  red[tid] = lv;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
-    __syncthreads();
+  f32x4 pre[PRE];
+#pragma unroll
+  for (int u = 0; u < PRE; ++u) {
+    const int s = grp + u * G;
+    pre[u] = s < S ? *reinterpret_cast<const f32x4*>(ows + ((size_t)s * rows + row) * D + c * 4)
+                   : f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const float mx = red[0];
+
+  // Largest chunk lse: a butterfly within each wave, then the four waves.
+  float m = lv;
+#pragma unroll
+  for (int w = 32; w > 0; w >>= 1) m = fmaxf(m, __shfl_xor(m, w));
+  if ((tid & 63) == 0) red[0][wv_id] = m;
   __syncthreads();
+  const float mx = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
   // Weights exp(lse_s - max); empty chunks (lse_s = -inf) get 0.
   const float wv = (tid < S && lv != -INFINITY) ? fast_exp2((lv - mx) * kLog2e) : 0.f;
   if (tid < S) w_s[tid] = wv;
-  red[tid] = wv;
+  float sm = wv;
+#pragma unroll
+  for (int w = 32; w > 0; w >>= 1) sm += __shfl_xor(sm, w);
+  if ((tid & 63) == 0) red[1][wv_id] = sm;
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) red[tid] += red[tid + w];
-    __syncthreads();
-  }
-  const float wsum = red[0];
+  const float wsum = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
 
-  const int c = tid % LPR, grp = tid / LPR;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int s = grp; s < S; s += G) {
+#pragma unroll
+  for (int u = 0; u < PRE; ++u) {
+    const int s = grp + u * G;
+    if (s < S) {
+      const float w = w_s[s];
+      if (w != 0.f) acc += w * pre[u];
+    }
+  }
+  for (int s = grp + PRE * G; s < S; s += G) {
     const float w = w_s[s];
     if (w != 0.f) acc += w * *reinterpret_cast<const f32x4*>(ows + ((size_t)s * rows + row) * D + c * 4);
   }
