@@ -170,3 +170,55 @@ def test_invalid_call_on_gpu_returns_status():
     with pytest.raises(fa.FAError) as e:
         fa.attention(q, q, q)
     assert e.value.status == fa.FA_ERR_HEAD_DIM
+
+
+def test_longest_key_sequence_the_host_accepts():
+    """Maximum size.  One key/value head whose K and V each fill the 2 GiB that
+    the kernels' 32-bit offsets inside a head allow: N_kv = 2^31 / (2 * 128) - 257
+    keys at d = 128 in bf16, the largest value fa_check_args accepts (its last
+    64-key tile is ragged).  Two query heads share it (GQA) with 300 query rows
+    each (one full and one ragged 256-row tile), non-causal, through fa_fwd;
+    then a 4:1 decoding step (N_q = 1) over the same K/V through the split-KV
+    entry point.  Inputs are seeded N(0, 1) draws cast to bf16; the oracle
+    evaluates 12 query rows of each head of the first call and every row of the
+    second.  So that a wrong offset anywhere in the 2 GiB cannot hide in the
+    average over 8.4M keys, one key row per checked row of head 0 and of the
+    decoding step is replaced by 16 times that query row's unit vector: its
+    score (about 16) carries roughly half of the row's softmax mass, so the
+    output is of order one and depends on that key's V row.  These keys sit at
+    the first and last keys, both sides of tile and 256-key boundaries, the
+    middle, and the last (ragged) tile."""
+    from test_gpu_splitkv import run_split
+
+    n_kv = (1 << 31) // (128 * 2) - 257
+    rng = np.random.default_rng(4242)
+    to_bf16 = lambda a: torch.from_numpy(a).to(torch.bfloat16)
+    q = to_bf16(rng.standard_normal((1, 2, 300, 128), dtype=np.float32))
+    k = to_bf16(rng.standard_normal((1, 1, n_kv, 128), dtype=np.float32))
+    v = to_bf16(rng.standard_normal((1, 1, n_kv, 128), dtype=np.float32))
+    q1 = to_bf16(rng.standard_normal((1, 4, 1, 128), dtype=np.float32))
+    scale = workloads.default_scale(128)
+    rows = np.array([0, 1, 63, 64, 255, 256, 257, 270, 290, 297, 298, 299])
+    hot = [n_kv - 1, 0, n_kv - 64, n_kv - 65, 1 << 22, (1 << 22) - 1, n_kv // 2, 4096,
+           n_kv - 200, 8388095, 8388096, 12345, n_kv - 2, 255, 256, 8388288]
+    plant = [q[0, 0, i] for i in rows] + [q1[0, h, 0] for h in range(4)]
+    for j, qr in zip(hot, plant):
+        x = qr.double()
+        k[0, 0, j] = (16.0 * x / x.norm()).to(torch.bfloat16)
+    far = [1 << 40, 2 << 40, 3 << 40, 4 << 40, 5 << 40]   # argument check only, never dereferenced
+    st = fa.fa_check_args(*far, 1, 2, 1, 300, n_kv, 128, scale, 0, fa.FA_BF16)
+    assert st == fa.FA_OK, fa.fa_status_string(st)
+    st = fa.fa_check_args(*far, 1, 2, 1, 300, n_kv + 2, 128, scale, 0, fa.FA_BF16)
+    assert st == fa.FA_ERR_BAD_DIM
+    o_g, _ = compare("longest accepted N_kv", q, k, v, False, scale, "bf16", rows=rows)
+    say(f"    max|O| over the checked rows: head 0 (planted keys) "
+        f"{float(o_g[0, 0, rows].abs().max()):.3f}, head 1 {float(o_g[0, 1, rows].abs().max()):.4f}")
+
+    k64, v64 = workloads.to_f64(k), workloads.to_f64(v)
+    say(f"[case] longest accepted N_kv, split-KV decode q{tuple(q1.shape)} k{tuple(k.shape)}")
+    o_g, l_g, _, S = run_split(q1, k, v, False, scale)
+    ref_o, ref_l = attention_fp64(workloads.to_f64(q1), k64, v64, scale, False)
+    err_o = float(np.max(np.abs(workloads.to_f64(o_g) - ref_o)))
+    err_l = float(np.max(np.abs(l_g.double().numpy() - ref_l)))
+    say(f"    splits={S} max|dO|={err_o:.3e} max|dlse|={err_l:.3e} max|O|={float(o_g.abs().max()):.3f}")
+    assert err_o <= TOL["bf16"] and err_l <= TOL["bf16"], (err_o, err_l)
