@@ -159,3 +159,46 @@ def test_full_workload5_sampled_rows():
                                   workloads.to_f64(v[:, hk]), workloads.to_f64(do[:, hq]), scale,
                                   w.causal, rows, rows)
     compare_slice("w5", (dq[:, hq][:, :, rows], dk[:, hk][:, :, rows], dv[:, hk][:, :, rows]), ref)
+
+
+def test_longest_key_sequence_the_host_accepts():
+    """Maximum size for fa_bwd: one key/value head of N_kv = 2^31 / (2 * 128) - 257 keys at
+    d = 128 in bf16 (2 GiB of K and of V, the most the 32-bit offsets inside a head allow),
+    two query heads of 16 rows each, non-causal.  Like the forward's maximum-size case, one key
+    row per query row of head 0 is replaced by 16 times that row's unit vector (≈ 20% of the
+    row's softmax mass), at the first and last keys, tile and 256-key boundaries, the middle and
+    the ragged last tile, so that the checked gradients are of order one.  Checked: every dQ
+    row, and dK/dV at the planted keys plus 16 random keys."""
+    from oracle import attention_bwd_fp64_rows
+
+    n_kv = (1 << 31) // (128 * 2) - 257
+    rng = np.random.default_rng(4343)
+    to_bf16 = lambda a: torch.from_numpy(a).to(torch.bfloat16)
+    q = to_bf16(rng.standard_normal((1, 2, 16, 128), dtype=np.float32))
+    k = to_bf16(rng.standard_normal((1, 1, n_kv, 128), dtype=np.float32))
+    v = to_bf16(rng.standard_normal((1, 1, n_kv, 128), dtype=np.float32))
+    do = to_bf16(rng.standard_normal((1, 2, 16, 128), dtype=np.float32))
+    hot = [n_kv - 1, 0, n_kv - 64, n_kv - 65, 1 << 22, (1 << 22) - 1, n_kv // 2, 4096,
+           n_kv - 200, 8388095, 8388096, 12345, n_kv - 2, 255, 256, 8388288]
+    for j, i in zip(hot, range(16)):
+        x = q[0, 0, i].double()
+        k[0, 0, j] = (16.0 * x / x.norm()).to(torch.bfloat16)
+    scale = workloads.default_scale(128)
+    say(f"[case] longest accepted N_kv backward: q{tuple(q.shape)} k{tuple(k.shape)}")
+    qd, kd, vd, dod = (x.to(DEV) for x in (q, k, v, do))
+    o, lse = fa.attention(qd, kd, vd, causal=False, scale=scale)
+    dq = torch.full_like(qd, float("nan"))
+    dk = torch.full_like(kd, float("nan"))
+    dv = torch.full_like(vd, float("nan"))
+    fa.attention_backward(qd, kd, vd, o, lse, dod, causal=False, scale=scale, dq=dq, dk=dk,
+                          dv=dv)
+    torch.cuda.synchronize()
+    keys = np.unique(np.concatenate([np.array(hot), rng.choice(n_kv, 16, replace=False)]))
+    rows = np.arange(16)
+    dq_g = dq.cpu()
+    dk_g = dk[:, :, torch.from_numpy(keys).to(DEV)].cpu()
+    dv_g = dv[:, :, torch.from_numpy(keys).to(DEV)].cpu()
+    del qd, kd, vd, dod, o, lse, dq, dk, dv
+    ref = attention_bwd_fp64_rows(workloads.to_f64(q), workloads.to_f64(k), workloads.to_f64(v),
+                                  workloads.to_f64(do), scale, False, rows, keys)
+    compare_slice("max N_kv", (dq_g, dk_g, dv_g), ref)
