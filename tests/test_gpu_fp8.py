@@ -168,3 +168,32 @@ def test_full_workload7_sampled_rows():
     rows = np.unique(np.concatenate([np.arange(3), np.arange(w.Nq - 3, w.Nq), [255, 256, 4095, 4096],
                                      rng.choice(w.Nq, 20, replace=False)]))
     compare(w.name, o, l, codes, ds, w.causal, scale, rows=rows)
+
+
+
+def test_longest_key_sequence_the_host_accepts():
+    """Maximum size for fa_fwd_fp8: the longest key sequence the host accepts at d = 128,
+    N_kv = 2^31 / (2 * 128) - 257 (the limit is shared with the 16-bit path; here K and V
+    are 1 GiB of E4M3 codes each), one query head of 300 rows (one full and one ragged
+    256-row tile), non-causal.  For each of 3 checked rows one key row is replaced by the
+    E4M3 codes of 32 times that row's unit vector, in the last key, at key 2^22 and at the
+    start of the ragged last tile: its score (about 30) exceeds the log of the other keys'
+    summed weight (about 16.4) by so much that the exact output is that key's V row to ~1e-6,
+    and a wrong offset changes it at order one.  (With a score near 16, where that key holds
+    ~20% of the mass, the other keys' probabilities lie below E4M3's smallest subnormal
+    relative to the reference and round to zero; the output then follows the planted key
+    alone, which the rounding model bounds but which says little about the addressing.)"""
+    n_kv = (1 << 31) // (128 * 2) - 257
+    codes, ds = workloads.make_inputs_fp8(1, 1, 1, 300, n_kv, 128, seed=4444)
+    q8, k8, v8 = codes
+    rows = np.array([0, 256, 299])
+    hot = [n_kv - 1, 1 << 22, 8388288]
+    for j, i in zip(hot, rows):
+        x = q8[0, 0, i].to(torch.float64) * ds[0]
+        y = (32.0 * x / x.norm() / ds[1]).clamp(-448.0, 448.0)
+        k8[0, 0, j] = y.to(torch.float32).to(torch.float8_e4m3fn)
+    scale = workloads.default_scale(128)
+    say(f"[case] longest accepted N_kv (E4M3): q{tuple(q8.shape)} k{tuple(k8.shape)}")
+    o, l = run_gpu((q8, k8, v8), ds, False, scale)
+    say(f"    max|O| over the checked rows {float(o[0, 0, rows].float().abs().max()):.3f}")
+    compare("longest accepted N_kv (E4M3)", o, l, (q8, k8, v8), ds, False, scale, rows=rows)
