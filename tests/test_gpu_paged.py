@@ -135,3 +135,68 @@ def test_full_workload8_against_oracle():
     el = float(np.max(np.abs(lse.double().numpy() - rl)))
     say(f"    splits={S} max|dO|={eo:.3e} max|dlse|={el:.3e}")
     assert eo <= TOL and el <= TOL
+
+
+@pytest.mark.parametrize("causal, Nq", [(False, 1), (True, 4)])
+def test_largest_pool_the_host_accepts(causal, Nq):
+    """Maximum size for fa_fwd_paged: block offsets inside a pool are 32-bit, so the host
+    accepts pools of at most 2^32 - 4097 bytes.  With 16-key blocks, Hkv = 2 and d = 128 in
+    bf16 (8 KiB per block) that is 524287 blocks (4 GiB per pool); one block more is rejected.
+    Two sequences (5000 and 3001 keys, GQA 4:1) live in that pool: the first in the last 313
+    blocks, the second in block 0, blocks from the middle and the pool's last-but-313 region,
+    with a ragged last block.  Every other slot of both pools is NaN, so a read outside the
+    sequences shows.  In each sequence one key per key/value head (the last key, key 0, or one
+    in the middle) is replaced by 16 times a query row's unit vector: it outweighs the other
+    keys (score about 16 against a log-sum of about 9.5), so the output is of order one and
+    tracks that key's V row.  The oracle sees the referenced blocks only, with the table
+    renumbered accordingly (the same keys in the same order)."""
+    bs, Hkv, Hq, d = 16, 2, 8, 128
+    nb = (2 ** 32 - 4097) // (bs * Hkv * d * 2)
+    assert nb == 524287
+    lens = [5000, 3001]
+    mb = max((n + bs - 1) // bs for n in lens)
+    scale = workloads.default_scale(d)
+    st = fa.fa_fwd_paged(1 << 40, 2 << 40, 3 << 40, 4 << 40, 5 << 40, 6 << 40, 7 << 40, 2, Hq, Hkv,
+                         Nq, d, nb + 1, bs, mb, scale, int(causal), fa.FA_BF16, 4, 8 << 40,
+                         1 << 30, None)
+    assert st == fa.FA_ERR_BAD_DIM   # rejected before any memory is touched
+    rng = np.random.default_rng(4545 + Nq)
+    n0 = (lens[0] + bs - 1) // bs
+    n1 = (lens[1] + bs - 1) // bs
+    tab = np.full((2, mb), -1, dtype=np.int32)
+    tab[0, :n0] = np.arange(nb - n0, nb)                                   # the pool's last blocks
+    mid = rng.choice(np.arange(1, nb - n0 - 200), n1 - 2, replace=False)
+    tab[1, :n1] = np.concatenate([[0], mid, [nb - n0 - 1]])               # first, middle, high
+    q = torch.from_numpy(rng.standard_normal((2, Hq, Nq, d), dtype=np.float32)).to(torch.bfloat16)
+    kc = torch.full((nb, bs, Hkv, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    vc = torch.full((nb, bs, Hkv, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    plant = {0: [(lens[0] - 1, 0, 0), (0, 1, 4)], 1: [(lens[1] - 1, 0, 1), (1600, 1, 7)]}
+    for b, n in enumerate(lens):
+        kb = torch.from_numpy(rng.standard_normal((n, Hkv, d), dtype=np.float32)).to(torch.bfloat16)
+        vb = torch.from_numpy(rng.standard_normal((n, Hkv, d), dtype=np.float32)).to(torch.bfloat16)
+        for key, g, h in plant[b]:   # key row of kv head g aligned with query head h, last row
+            x = q[b, h, Nq - 1].double()
+            kb[key, g] = (16.0 * x / x.norm()).to(torch.bfloat16)
+        t = np.arange(n)
+        slots = torch.from_numpy(tab[b, t // bs].astype(np.int64) * bs + t % bs).to(DEV)
+        kc.view(nb * bs, Hkv, d)[slots] = kb.to(DEV)
+        vc.view(nb * bs, Hkv, d)[slots] = vb.to(DEV)
+    tabd = torch.from_numpy(tab)
+    sl = torch.tensor(lens, dtype=torch.int32)
+    say(f"[case] largest accepted pool: {nb} blocks of {bs} keys, Hkv={Hkv}, d={d}, lens={lens}, "
+        f"Nq={Nq}, causal={causal}")
+    o, lse, S = run_paged(q, kc, vc, tabd, sl, causal, scale)
+    used = np.unique(tab[tab >= 0])
+    remap = np.full(nb, -1, dtype=np.int64)
+    remap[used] = np.arange(used.size)
+    tab_c = np.where(tab >= 0, remap[np.maximum(tab, 0)], -1).astype(np.int32)
+    idx = torch.from_numpy(used).to(DEV)
+    kcc, vcc = kc[idx].cpu(), vc[idx].cpu()
+    del kc, vc
+    ro, rl = attention_fp64_paged(workloads.to_f64(q), workloads.to_f64(kcc), workloads.to_f64(vcc),
+                                  tab_c, np.array(lens), scale, causal)
+    og, lg = workloads.to_f64(o), lse.double().numpy()
+    assert np.all(np.isfinite(og)) and np.all(np.isfinite(lg)), "unwritten or NaN output"
+    eo, el = float(np.max(np.abs(og - ro))), float(np.max(np.abs(lg - rl)))
+    say(f"    splits={S} max|dO|={eo:.3e} max|dlse|={el:.3e} max|O|={float(np.abs(og).max()):.3f}")
+    assert eo <= TOL and el <= TOL, (eo, el)
