@@ -78,7 +78,10 @@ typedef enum fa_dtype {
 /*
  * Exact attention forward, launched on the null (default) stream.
  * scale is applied as given (callers usually pass 1/sqrt(d)); any finite
- * value is accepted, including 0 and negative values.
+ * value is accepted, including 0 and negative values.  Scores are formed in
+ * fp32 as |scale| * log2(e) * (q . k), so every such product must stay
+ * finite in fp32 (|scale * q . k| below about 2.3e38); beyond that the
+ * outputs are undefined (the inputs decide it, so it is not checked).
  * Size limits (FA_ERR_BAD_DIM beyond them): one head of q or k/v, plus 256
  * rows, must stay below 2 GiB ((max(N_q, N_kv) + 256) * d * elem_size <
  * 2^31), B*Hq and B*Hkv below 2^31, and the grid below 2^31 workgroups.
