@@ -1504,10 +1504,14 @@ __device__ __forceinline__ void attn_bwd_dkdv_body(const BwdParams& p) {
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
-  // Work item: (b, kv head, head share, key tile), key tiles fastest.  Head
-  // share hs takes the query heads hs, hs + hsplit, ... of the group.
-  const int kt = blockIdx.x % p.n_tiles;
-  const int r1 = blockIdx.x / p.n_tiles;
+  // Work item: (b, kv head, head share, key tile).  Head share hs takes the
+  // query heads hs, hs + hsplit, ... of the group.  Non-causal: key tiles
+  // fastest.  Causal: the first key tiles see the most queries, so they are
+  // listed first, (b, kv head, share) fastest, and the longest items start in
+  // the first round of workgroups.
+  const int n_r1 = gridDim.x / p.n_tiles;
+  const int kt = CAUSAL ? (int)(blockIdx.x / n_r1) : (int)(blockIdx.x % p.n_tiles);
+  const int r1 = CAUSAL ? (int)(blockIdx.x % n_r1) : (int)(blockIdx.x / p.n_tiles);
   const int hs = r1 % p.hsplit;
   const int bg = r1 / p.hsplit;
   const int g = bg % p.Hkv;
@@ -1772,8 +1776,12 @@ __device__ __forceinline__ void attn_bwd_dq_body(const BwdParams& p) {
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
-  const int qt = blockIdx.x % p.n_tiles;
-  const int bh = blockIdx.x / p.n_tiles;
+  // Work item: (b, query head, query tile).  Non-causal: query tiles fastest.
+  // Causal: the last query tiles see the most keys; they are listed first,
+  // (b, head) fastest.
+  const int n_bh = gridDim.x / p.n_tiles;
+  const int qt = CAUSAL ? p.n_tiles - 1 - (int)(blockIdx.x / n_bh) : (int)(blockIdx.x % p.n_tiles);
+  const int bh = CAUSAL ? (int)(blockIdx.x % n_bh) : (int)(blockIdx.x / p.n_tiles);
   const int hq = bh % p.Hq;
   const int b = bh / p.Hq;
   const int hkv = hq / p.group;
