@@ -102,6 +102,14 @@ __device__ __forceinline__ void map_block(const Params& p, bool causal, int& b, 
   hq = hl - b * p.Hq;
 }
 
+// Block index renumbered so that each XCD (dispatch is round-robin: block i
+// runs on XCD i % 8) receives one contiguous range of logical indices.
+__device__ __forceinline__ int xcd_local(int bid, int nb) {
+  const int xcd = bid & 7, slot = bid >> 3;
+  const int per = nb >> 3, rem = nb & 7;
+  return xcd * per + (xcd < rem ? xcd : rem) + slot;
+}
+
 // ----------------------------------------------- 16-bit (bf16 / f16) path
 //
 // Workgroup: 8 waves x 32 query rows = 256 rows.  K/V tiles of 64 keys move
@@ -1510,8 +1518,9 @@ __device__ __forceinline__ void attn_bwd_dkdv_body(const BwdParams& p) {
   // listed first, (b, kv head, share) fastest, and the longest items start in
   // the first round of workgroups.
   const int n_r1 = gridDim.x / p.n_tiles;
-  const int kt = CAUSAL ? (int)(blockIdx.x / n_r1) : (int)(blockIdx.x % p.n_tiles);
-  const int r1 = CAUSAL ? (int)(blockIdx.x % n_r1) : (int)(blockIdx.x / p.n_tiles);
+  const int xl = xcd_local((int)blockIdx.x, (int)gridDim.x);
+  const int kt = CAUSAL ? (int)(blockIdx.x / n_r1) : xl % p.n_tiles;
+  const int r1 = CAUSAL ? (int)(blockIdx.x % n_r1) : xl / p.n_tiles;
   const int hs = r1 % p.hsplit;
   const int bg = r1 / p.hsplit;
   const int g = bg % p.Hkv;
@@ -1780,8 +1789,9 @@ __device__ __forceinline__ void attn_bwd_dq_body(const BwdParams& p) {
   // Causal: the last query tiles see the most keys; they are listed first,
   // (b, head) fastest.
   const int n_bh = gridDim.x / p.n_tiles;
-  const int qt = CAUSAL ? p.n_tiles - 1 - (int)(blockIdx.x / n_bh) : (int)(blockIdx.x % p.n_tiles);
-  const int bh = CAUSAL ? (int)(blockIdx.x % n_bh) : (int)(blockIdx.x / p.n_tiles);
+  const int xl = xcd_local((int)blockIdx.x, (int)gridDim.x);
+  const int qt = CAUSAL ? p.n_tiles - 1 - (int)(blockIdx.x / n_bh) : xl % p.n_tiles;
+  const int bh = CAUSAL ? (int)(blockIdx.x % n_bh) : xl / p.n_tiles;
   const int hq = bh % p.Hq;
   const int b = bh / p.Hq;
   const int hkv = hq / p.group;
