@@ -206,10 +206,10 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None, out=Non
     B, Hq, Hkv, Nq, Nkv, d = _check_tensors(q, k, v)
     if scale is None:
         scale = 1.0 / float(d) ** 0.5
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    out = torch.empty_like(q) if out is None else \
+        _check_out(out, "out", q.shape, q.dtype, q.device)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else \
+        _check_out(lse, "lse", (B, Hq, Nq), torch.float32, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     st = fa_fwd_stream(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, d, float(scale), causal,
@@ -217,6 +217,17 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None, out=Non
     if st != FA_OK:
         raise FAError(st, fa_status_string(st))
     return out, lse
+
+
+def fwd(q, k, v, *, causal: bool = False, scale: float | None = None):
+    """(o, lse) = the exact attention forward of q [B,Hq,N_q,d] over k, v [B,Hkv,N_kv,d].
+
+    o has q's dtype and shape; lse [B,Hq,N_q] is fp32, the natural-log
+    logsumexp of each row's scaled scores.  ``scale`` defaults to 1/sqrt(d).
+    Both are allocated by torch on q's device; the call launches fa_fwd_stream
+    on torch's current stream and returns without synchronising.
+    """
+    return attention(q, k, v, causal=causal, scale=scale)
 
 
 def _check_tensors(q, k, v):
@@ -227,12 +238,43 @@ def _check_tensors(q, k, v):
             raise FAError(FA_ERR_BAD_DIM, f"{name} must be a contiguous 4-D tensor")
     if not (q.dtype == k.dtype == v.dtype):
         raise FAError(FA_ERR_DTYPE, "q, k and v must share one dtype")
+    if not (q.device == k.device == v.device):
+        raise FAError(FA_ERR_NULL_PTR, "q, k and v must be on one GPU")
     B, Hq, Nq, d = q.shape
     Bk, Hkv, Nkv, dk = k.shape
     if tuple(v.shape) != tuple(k.shape) or Bk != B or dk != d:
         raise FAError(FA_ERR_BAD_DIM, f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} "
                                       f"v{tuple(v.shape)}")
     return B, Hq, Hkv, Nq, Nkv, d
+
+
+def _check_out(t, name: str, shape, dtype, device):
+    """Raise unless a caller-supplied output buffer is exactly what the kernels write.
+
+    The C ABI sizes every store from the input dimensions, so a buffer on
+    another device, of another dtype or shape, or not contiguous would be
+    written out of bounds (or through a host address).  Checked before any
+    launch."""
+    if not getattr(t, "is_cuda", False) or t.device != device:
+        raise FAError(FA_ERR_NULL_PTR, f"{name} must be a GPU tensor on {device}")
+    if t.dtype != dtype:
+        raise FAError(FA_ERR_DTYPE, f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise FAError(FA_ERR_BAD_DIM, f"{name} must have shape {tuple(shape)}, got "
+                                      f"{tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise FAError(FA_ERR_BAD_DIM, f"{name} must be contiguous")
+    return t
+
+
+def _check_workspace(t, device):
+    """A caller-supplied workspace: a contiguous tensor on the inputs' GPU (its byte
+    size is passed to the C ABI, which rejects one that is too small)."""
+    if not getattr(t, "is_cuda", False) or t.device != device:
+        raise FAError(FA_ERR_NULL_PTR, f"workspace must be a GPU tensor on {device}")
+    if not t.is_contiguous():
+        raise FAError(FA_ERR_BAD_DIM, "workspace must be contiguous")
+    return t
 
 
 def attention_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
@@ -256,11 +298,13 @@ def attention_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
     need = fa_splitkv_workspace_bytes(B, Hq, Nq, d, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    else:
+        _check_workspace(workspace, q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    out = torch.empty_like(q) if out is None else \
+        _check_out(out, "out", q.shape, q.dtype, q.device)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else \
+        _check_out(lse, "lse", (B, Hq, Nq), torch.float32, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     st = fa_fwd_splitkv(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, d, float(scale), causal, dt,
@@ -282,13 +326,10 @@ def attention_fp8(q, k, v, descale_q: float, descale_k: float, descale_v: float,
     B, Hq, Hkv, Nq, Nkv, d = _check_tensors(q, k, v)
     if scale is None:
         scale = 1.0 / float(d) ** 0.5
-    if out is None:
-        out = torch.empty((B, Hq, Nq, d), dtype=torch.bfloat16, device=q.device)
-    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (B, Hq, Nq, d) or \
-            not out.is_contiguous():
-        raise FAError(FA_ERR_BAD_DIM, "out must be a contiguous bf16 tensor shaped like q")
-    if lse is None:
-        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    out = torch.empty((B, Hq, Nq, d), dtype=torch.bfloat16, device=q.device) if out is None \
+        else _check_out(out, "out", (B, Hq, Nq, d), torch.bfloat16, q.device)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else \
+        _check_out(lse, "lse", (B, Hq, Nq), torch.float32, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     st = fa_fwd_fp8(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, d, float(scale), causal,
@@ -311,8 +352,8 @@ def attention_paged(q, k_cache, v_cache, block_table, seqlens_k, causal: bool = 
     import torch
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache),
                     ("block_table", block_table), ("seqlens_k", seqlens_k)):
-        if not t.is_cuda or not t.is_contiguous():
-            raise FAError(FA_ERR_NULL_PTR, f"{name} must be a contiguous GPU tensor")
+        if not t.is_cuda or not t.is_contiguous() or t.device != q.device:
+            raise FAError(FA_ERR_NULL_PTR, f"{name} must be a contiguous tensor on q's GPU")
     if block_table.dtype != torch.int32 or seqlens_k.dtype != torch.int32:
         raise FAError(FA_ERR_DTYPE, "block_table and seqlens_k must be int32")
     if q.dtype != k_cache.dtype or q.dtype != v_cache.dtype or k_cache.shape != v_cache.shape:
@@ -332,10 +373,12 @@ def attention_paged(q, k_cache, v_cache, block_table, seqlens_k, causal: bool = 
     need = fa_splitkv_workspace_bytes(B, Hq, Nq, d, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    else:
+        _check_workspace(workspace, q.device)
+    out = torch.empty_like(q) if out is None else \
+        _check_out(out, "out", q.shape, q.dtype, q.device)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else \
+        _check_out(lse, "lse", (B, Hq, Nq), torch.float32, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     st = fa_fwd_paged(q, k_cache, v_cache, block_table, seqlens_k, out, lse, B, Hq, Hkv, Nq, d,
@@ -356,17 +399,18 @@ def attention_backward(q, k, v, o, lse, dout, causal: bool = False, scale: float
     import torch
     B, Hq, Hkv, Nq, Nkv, d = _check_tensors(q, k, v)
     for name, t in (("o", o), ("dout", dout)):
-        if not t.is_cuda or tuple(t.shape) != tuple(q.shape) or t.dtype != q.dtype or \
-                not t.is_contiguous():
-            raise FAError(FA_ERR_BAD_DIM, f"{name} must be a contiguous GPU tensor like q")
+        _check_out(t, name, q.shape, q.dtype, q.device)
+    _check_out(lse, "lse", (B, Hq, Nq), torch.float32, q.device)
     if scale is None:
         scale = 1.0 / float(d) ** 0.5
     need = fa_bwd_workspace_bytes(B, Hq, Hkv, Nq, Nkv, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    else:
+        _check_workspace(workspace, q.device)
+    dq = torch.empty_like(q) if dq is None else _check_out(dq, "dq", q.shape, q.dtype, q.device)
+    dk = torch.empty_like(k) if dk is None else _check_out(dk, "dk", k.shape, k.dtype, q.device)
+    dv = torch.empty_like(v) if dv is None else _check_out(dv, "dv", v.shape, v.dtype, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     st = fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, d, float(scale), causal,
@@ -379,6 +423,6 @@ def attention_backward(q, k, v, o, lse, dout, causal: bool = False, scale: float
 __all__ = ["fa_fwd", "fa_fwd_stream", "fa_check_args", "fa_status_string", "fa_launch_info",
            "fa_splitkv_workspace_bytes", "fa_splitkv_default_splits", "fa_fwd_splitkv",
            "fa_bwd_workspace_bytes", "fa_bwd", "fa_fwd_fp8", "fa_fwd_paged",
-           "attention", "attention_splitkv", "attention_backward", "attention_fp8",
+           "fwd", "attention", "attention_splitkv", "attention_backward", "attention_fp8",
            "attention_paged", "load_library", "header_functions", "FAError", "dtype_code",
            "FA_F32", "FA_F16", "FA_BF16"]

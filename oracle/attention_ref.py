@@ -89,7 +89,8 @@ def attention_fp64(q, k, v, scale: float, causal: bool = False,
     S = sigma * Q_chunk K^T ([P1] §3.1, [P3] standard attention step 1),
     applies the causal mask, then takes the safe softmax of each row: subtract
     the row maximum, exponentiate, divide by the row sum ([P3] "Safe
-    Softmax"; [P1] §4 ``full_attention``), and forms O = P V ([P3] step 3).
+    Softmax"; [P1] §3.1, P = softmax(S) row by row), and forms O = P V
+    ([P3] step 3).
     lse = m + ln(l).
 
     Chunking over query rows only bounds memory (a 32768-key row block is
@@ -311,12 +312,17 @@ def probabilities_fp64(q, k, scale: float, causal: bool = False):
 
 
 def attention_bruteforce(q, k, v, scale: float, causal: bool = False):
-    """Pure-Python element-by-element attention with compensated sums.
+    """Pure-Python element-by-element attention, straight from the softmax definition.
 
-    Each dot product, row sum and output sum is a ``math.fsum`` over Python
-    floats, so the only rounding is one per exp/log and per term product.
-    Intended for N <= 16.  Follows [P1] §4 ``full_attention`` (max, exp,
-    normaliser, weighted V) extended with masking and head grouping.
+    [P1] §3.1 defines P = softmax(S) row by row, p_ij = e^(s_ij) / sum_k e^(s_ik),
+    and O = P V.  Dividing numerator and denominator by e^(s_ij) gives
+    p_ij = 1 / sum_k e^(s_ik - s_ij), which is evaluated here for every pair
+    (O(N^2) exponentials per row, no running or row maximum, no separate
+    normaliser); a term e^(s_ik - s_ij) beyond the float range makes p_ij
+    smaller than 1e-300, taken as 0.  Then o_i = sum_j p_ij v_j and, since
+    lse_i = ln sum_k e^(s_ik) = s_ij - ln p_ij for any j, lse_i is read off the
+    key with the largest score.  Every sum is a ``math.fsum`` over Python
+    floats.  Intended for N <= 16; used only to check ``attention_fp64``.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -333,13 +339,16 @@ def attention_bruteforce(q, k, v, scale: float, causal: bool = False):
                 keys = list(allowed_keys(i, Nkv, causal))
                 s = [sigma * math.fsum(qi[t] * float(k[b, g, j, t]) for t in range(D))
                      for j in keys]
-                m = max(s)
-                e = [math.exp(x - m) for x in s]
-                l = math.fsum(e)
+                p = []
+                for sj in s:
+                    gaps = [sk - sj for sk in s]
+                    p.append(0.0 if max(gaps) > 700.0
+                             else 1.0 / math.fsum(math.exp(x) for x in gaps))
                 for t in range(D):
-                    o[b, h, i, t] = math.fsum(e[n] * float(v[b, g, j, t])
-                                              for n, j in enumerate(keys)) / l
-                lse[b, h, i] = m + math.log(l)
+                    o[b, h, i, t] = math.fsum(p[n] * float(v[b, g, j, t])
+                                              for n, j in enumerate(keys))
+                top = max(range(len(keys)), key=lambda n: s[n])
+                lse[b, h, i] = s[top] - math.log(p[top])
     return o, lse
 
 

@@ -58,26 +58,72 @@ def case_inputs(B, Hq, Hkv, Nq, Nkv, D, dtype, seed, sigma=1.0):
     return workloads.make_inputs(B, Hq, Hkv, Nq, Nkv, D, dtype, seed, sigma)
 
 
-@pytest.mark.parametrize("idx", [1, 2, 3, 4])
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
 def test_named_workload_full_tensor(idx):
+    """Every element of O and lse of each of the five named workloads (for the
+    N=32768 causal GQA workload with outlier keys, 28 x 32768 rows) against the
+    oracle, which evaluates every row whole."""
     w = workloads.WORKLOADS[idx]
     q, k, v, scale = workloads.workload_inputs(w)
     compare(w.name, q, k, v, w.causal, scale, w.dtype)
 
 
-def test_long_causal_outlier_workload_sampled_rows():
-    """N=32768 causal GQA with outlier keys: every head, ~900 rows per head
-    (the first and last 128, both sides of every 4096-row boundary, 512 at
-    random); the oracle evaluates exactly those rows."""
-    w = workloads.WORKLOADS[5]
-    q, k, v, scale = workloads.workload_inputs(w)
-    N = w.Nq
-    rng = np.random.default_rng(77)
-    picks = [np.arange(128), np.arange(N - 128, N), rng.choice(N, 512, replace=False)]
-    for b in range(4096, N, 4096):
-        picks.append(np.arange(b - 8, b + 8))
-    rows = np.unique(np.concatenate(picks))
-    compare(w.name, q, k, v, w.causal, scale, w.dtype, rows=rows)
+def test_fwd_entry_matches_attention():
+    """fwd(q, k, v, causal=, scale=) is the allocating form of the same launch."""
+    q, k, v = case_inputs(1, 4, 2, 300, 300, 128, "bf16", seed=12)
+    qd, kd, vd = (x.to(DEV) for x in (q, k, v))
+    say("[case] fwd entry point")
+    o1, l1 = fa.fwd(qd, kd, vd, causal=True, scale=0.1)
+    o2, l2 = fa.attention(qd, kd, vd, causal=True, scale=0.1)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_bad_output_buffers_raise_before_launch():
+    """A supplied out/lse/workspace/gradient buffer of the wrong device, dtype,
+    shape or layout raises FAError and nothing is written."""
+    q, k, v = case_inputs(1, 4, 2, 64, 64, 128, "bf16", seed=14)
+    qd, kd, vd = (x.to(DEV) for x in (q, k, v))
+    say("[case] bad output buffers")
+    good_o = torch.empty_like(qd)
+    good_l = torch.empty(qd.shape[:3], dtype=torch.float32, device=DEV)
+    bad_outs = [torch.empty_like(q),                                  # host memory
+                torch.empty_like(qd, dtype=torch.float16),            # dtype
+                torch.empty(1, 4, 63, 128, dtype=torch.bfloat16, device=DEV),   # shape
+                torch.empty(1, 4, 128, 64, dtype=torch.bfloat16, device=DEV).transpose(2, 3)]
+    bad_lses = [torch.empty(qd.shape[:3], dtype=torch.bfloat16, device=DEV),
+                torch.empty(qd.shape[:3]),
+                torch.empty(1, 4, 32, dtype=torch.float32, device=DEV)]
+    for bo in bad_outs:
+        for fn in (fa.attention, fa.attention_splitkv):
+            sentinel = good_l.fill_(7.0).clone()
+            with pytest.raises(fa.FAError):
+                fn(qd, kd, vd, out=bo, lse=good_l)
+            torch.cuda.synchronize()
+            assert torch.equal(good_l, sentinel)
+    for bl in bad_lses:
+        for fn in (fa.attention, fa.attention_splitkv):
+            sentinel = good_o.fill_(3.0).clone()
+            with pytest.raises(fa.FAError):
+                fn(qd, kd, vd, out=good_o, lse=bl)
+            torch.cuda.synchronize()
+            assert torch.equal(good_o, sentinel)
+    with pytest.raises(fa.FAError):
+        fa.attention_splitkv(qd, kd, vd, num_splits=1, workspace=torch.empty(1 << 20, dtype=torch.uint8))
+    o, lse = fa.attention(qd, kd, vd)
+    dout = torch.ones_like(qd)
+    for name, bad in (("dq", torch.empty_like(kd)), ("dk", torch.empty_like(qd)),
+                      ("dv", torch.empty_like(vd, dtype=torch.float16))):
+        with pytest.raises(fa.FAError):
+            fa.attention_backward(qd, kd, vd, o, lse, dout, **{name: bad})
+    with pytest.raises(fa.FAError):
+        fa.attention_backward(qd, kd, vd, o, lse.to(torch.bfloat16), dout)
+    q8, k8, v8 = (x.to(torch.float8_e4m3fn) for x in (qd, kd, vd))
+    with pytest.raises(fa.FAError):
+        fa.attention_fp8(q8, k8, v8, 1.0, 1.0, 1.0, lse=bad_lses[0])
+    with pytest.raises(fa.FAError):
+        fa.attention_fp8(q8, k8, v8, 1.0, 1.0, 1.0, out=good_o.to(torch.float16))
+    torch.cuda.synchronize()
 
 
 ODD = [
