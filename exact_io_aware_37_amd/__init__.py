@@ -33,6 +33,7 @@ FA_ERR_HIP = 8
 FA_ERR_ALIAS = 9
 FA_ERR_WORKSPACE = 10
 FA_SPLITKV_MAX_SPLITS = 256
+FA_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 FA_F32 = 0
 FA_F16 = 1
@@ -79,6 +80,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_splitkv_default_splits.restype = _I
     lib.fa_fwd_splitkv.argtypes = list(_FWD_ARGS) + [_I, _VP, ctypes.c_size_t, _VP]
     lib.fa_fwd_splitkv.restype = _I
+    lib.fa_fwd_splitkv_noalloc.argtypes = list(_FWD_ARGS) + [_I, _VP]
+    lib.fa_fwd_splitkv_noalloc.restype = _I
     lib.fa_bwd_workspace_bytes.argtypes = [_I] * 6
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_bwd.argtypes = [_VP] * 9 + [_I] * 6 + [_F, _I, _I, _VP, ctypes.c_size_t, _VP]
@@ -153,6 +156,14 @@ def fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, N_q, N_kv, d, scale, causal, dty
     return load_library().fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq,
                                          Hkv, N_q, N_kv, d, scale, int(causal), dtype,
                                          num_splits, _ptr(workspace), workspace_bytes, s)
+
+
+def fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, Hq, Hkv, N_q, N_kv, d, scale, causal, dtype,
+                           num_splits, stream) -> int:
+    s = stream if (stream is None or isinstance(stream, int)) else stream.cuda_stream
+    return load_library().fa_fwd_splitkv_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                                 B, Hq, Hkv, N_q, N_kv, d, scale, int(causal),
+                                                 dtype, num_splits, s)
 
 
 def fa_bwd_workspace_bytes(B, Hq, Hkv, N_q, N_kv, d) -> int:
@@ -314,6 +325,34 @@ def attention_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
     return out, lse
 
 
+def attention_splitkv_noalloc(q, k, v, out, lse, causal: bool = False,
+                              scale: float | None = None, num_splits: int | None = None,
+                              stream=None):
+    """``attention_splitkv`` through the allocation-free entry point: the chunk
+    results live in the library's per-GPU scratch array, and ``out``/``lse``
+    are caller-owned (nothing is allocated here or in the library).  Calls
+    that overlap on one GPU race on the scratch array; order them on one
+    stream.  Returns (out, lse)."""
+    import torch
+    B, Hq, Hkv, Nq, Nkv, d = _check_tensors(q, k, v)
+    dt = dtype_code(q.dtype)
+    _check_out(out, "out", q.shape, q.dtype, q.device)
+    _check_out(lse, "lse", (B, Hq, Nq), torch.float32, q.device)
+    if scale is None:
+        scale = 1.0 / float(d) ** 0.5
+    if num_splits is None:
+        num_splits = fa_splitkv_default_splits(B, Hq, Hkv, Nq, Nkv, d, dt)
+        if num_splits < 1:
+            raise FAError(FA_ERR_BAD_DIM, "no valid split count for these sizes")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = fa_fwd_splitkv_noalloc(q, k, v, out, lse, B, Hq, Hkv, Nq, Nkv, d, float(scale), causal,
+                                dt, num_splits, stream)
+    if st != FA_OK:
+        raise FAError(st, fa_status_string(st))
+    return out, lse
+
+
 def attention_fp8(q, k, v, descale_q: float, descale_k: float, descale_v: float,
                   causal: bool = False, scale: float | None = None, out=None, lse=None,
                   stream=None):
@@ -422,6 +461,7 @@ def attention_backward(q, k, v, o, lse, dout, causal: bool = False, scale: float
 
 __all__ = ["fa_fwd", "fa_fwd_stream", "fa_check_args", "fa_status_string", "fa_launch_info",
            "fa_splitkv_workspace_bytes", "fa_splitkv_default_splits", "fa_fwd_splitkv",
+           "fa_fwd_splitkv_noalloc", "attention_splitkv_noalloc",
            "fa_bwd_workspace_bytes", "fa_bwd", "fa_fwd_fp8", "fa_fwd_paged",
            "fwd", "attention", "attention_splitkv", "attention_backward", "attention_fp8",
            "attention_paged", "load_library", "header_functions", "FAError", "dtype_code",

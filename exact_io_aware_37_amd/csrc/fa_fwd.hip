@@ -34,6 +34,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "fa.h"
 
 namespace {
@@ -2292,6 +2294,49 @@ int dispatch_split(const SplitParams& sp, void* o, float* lse, int d, bool causa
   return causal ? run_split<T, 128, true, PAGED>(sp, ot, lse, s) : run_split<T, 128, false, PAGED>(sp, ot, lse, s);
 }
 
+// Both launches of the split-KV forward once every argument has been checked;
+// `workspace` holds fa_splitkv_workspace_bytes(B, Hq, N_q, d, num_splits) bytes.
+int launch_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                   int Hq, int Hkv, int N_q, int N_kv, int d, float scale, int causal, int dtype,
+                   int num_splits, void* workspace, void* stream) {
+  const SplitGeometry g = split_geometry(Hq, Hkv, N_q, N_kv);
+  SplitParams sp;
+  sp.q = q;
+  sp.k = k;
+  sp.v = v;
+  sp.rows = (long long)B * Hq * N_q;
+  sp.ows = static_cast<float*>(workspace);
+  sp.lws = sp.ows + (size_t)num_splits * sp.rows * d;
+  sp.B = B;
+  sp.Hq = Hq;
+  sp.Hkv = Hkv;
+  sp.Nq = N_q;
+  sp.Nkv = N_kv;
+  sp.group = Hq / Hkv;
+  sp.R = g.R;
+  sp.nrb = g.nrb;
+  sp.S = num_splits;
+  sp.items = (long long)B * Hkv * g.nrb * num_splits;
+  if (scale > 0.f) {
+    sp.sl2 = scale * kLog2e;
+    sp.qmode = 0;
+  } else if (scale < 0.f) {
+    sp.sl2 = -scale * kLog2e;
+    sp.qmode = 1;
+  } else {
+    sp.sl2 = 1.f;
+    sp.qmode = 2;
+  }
+  sp.btab = nullptr;
+  sp.seqlens = nullptr;
+  sp.mbps = sp.lbs = sp.nblocks = 0;
+  sp.pool_bytes = 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool c = causal != 0;
+  if (dtype == FA_BF16) return dispatch_split<__bf16>(sp, o, lse, d, c, s);
+  return dispatch_split<_Float16>(sp, o, lse, d, c, s);
+}
+
 template <typename T, int D, bool CAUSAL>
 int run_bwd(BwdParams p, long long rows, hipStream_t stream) {
   (void)hipGetLastError();
@@ -2325,6 +2370,52 @@ template <typename T>
 int dispatch_bwd(const BwdParams& p, long long rows, int d, bool causal, hipStream_t s) {
   if (d == 64) return causal ? run_bwd<T, 64, true>(p, rows, s) : run_bwd<T, 64, false>(p, rows, s);
   return causal ? run_bwd<T, 128, true>(p, rows, s) : run_bwd<T, 128, false>(p, rows, s);
+}
+
+}  // namespace
+
+// Device-resident workspace of the allocation-free split-KV entry point
+// (fa_fwd_splitkv_noalloc): one copy per GPU, loaded with the library's code
+// object and kept until the process ends.  Host code never uses this name as
+// an address: it stands for the array only on the device side.  The device
+// address of each GPU's copy comes from hipGetSymbolAddress, once per device
+// (scratch_address below), and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on device `dev`, looked up on that device's
+// first use (with `dev` made current for the lookup, then restored).
+int scratch_address(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) {
+    snprintf(g_hip_error, sizeof g_hip_error, "HIP error: device %d beyond the %d supported", dev,
+             kMaxDevices);
+    return FA_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    void* ptr = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur >= 0 && cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess || ptr == nullptr) {
+      snprintf(g_hip_error, sizeof g_hip_error, "HIP error: %s (%s) looking up the scratch array",
+               hipGetErrorName(e), hipGetErrorString(e));
+      return FA_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
 }
 
 }  // namespace
@@ -2500,42 +2591,32 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
       overlaps(pw, need, (uintptr_t)lse, nl))
     return FA_ERR_ALIAS;
 
-  const SplitGeometry g = split_geometry(Hq, Hkv, N_q, N_kv);
-  SplitParams sp;
-  sp.q = q;
-  sp.k = k;
-  sp.v = v;
-  sp.rows = (long long)B * Hq * N_q;
-  sp.ows = static_cast<float*>(workspace);
-  sp.lws = sp.ows + (size_t)num_splits * sp.rows * d;
-  sp.B = B;
-  sp.Hq = Hq;
-  sp.Hkv = Hkv;
-  sp.Nq = N_q;
-  sp.Nkv = N_kv;
-  sp.group = Hq / Hkv;
-  sp.R = g.R;
-  sp.nrb = g.nrb;
-  sp.S = num_splits;
-  sp.items = (long long)B * Hkv * g.nrb * num_splits;
-  if (scale > 0.f) {
-    sp.sl2 = scale * kLog2e;
-    sp.qmode = 0;
-  } else if (scale < 0.f) {
-    sp.sl2 = -scale * kLog2e;
-    sp.qmode = 1;
-  } else {
-    sp.sl2 = 1.f;
-    sp.qmode = 2;
-  }
-  sp.btab = nullptr;
-  sp.seqlens = nullptr;
-  sp.mbps = sp.lbs = sp.nblocks = 0;
-  sp.pool_bytes = 0;
+  return launch_splitkv(q, k, v, o, lse, B, Hq, Hkv, N_q, N_kv, d, scale, causal, dtype,
+                        num_splits, workspace, stream);
+}
+
+int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int Hq, int Hkv, int N_q, int N_kv, int d, float scale,
+                           int causal, int dtype, int num_splits, void* stream) {
+  int st = fa_check_args(q, k, v, o, lse, B, Hq, Hkv, N_q, N_kv, d, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  st = check_split_dims(B, Hq, Hkv, N_q, N_kv, d, dtype, num_splits);
+  if (st != FA_OK) return st;
+  const size_t need = fa_splitkv_workspace_bytes(B, Hq, N_q, d, num_splits);
+  if (need == 0 || need > (size_t)FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool c = causal != 0;
-  if (dtype == FA_BF16) return dispatch_split<__bf16>(sp, o, lse, d, c, s);
-  return dispatch_split<_Float16>(sp, o, lse, d, c, s);
+  int dev = -1;
+  const hipError_t e = hipStreamGetDevice(s, &dev);
+  if (e != hipSuccess) {
+    snprintf(g_hip_error, sizeof g_hip_error, "HIP error: %s (%s)", hipGetErrorName(e),
+             hipGetErrorString(e));
+    return FA_ERR_HIP;
+  }
+  void* ws = nullptr;
+  st = scratch_address(dev, &ws);
+  if (st != FA_OK) return st;
+  return launch_splitkv(q, k, v, o, lse, B, Hq, Hkv, N_q, N_kv, d, scale, causal, dtype,
+                        num_splits, ws, stream);
 }
 
 int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache, const int* block_table,
@@ -2721,7 +2802,9 @@ const char* fa_status_string(int status) {
     case FA_ERR_SCALE: return "scale must be finite";
     case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
     case FA_ERR_ALIAS: return "o, lse or the workspace overlaps an input or each other";
-    case FA_ERR_WORKSPACE: return "workspace smaller than fa_splitkv_workspace_bytes";
+    case FA_ERR_WORKSPACE:
+      return "workspace smaller than needed (or, for the allocation-free entry point, more than "
+             "FA_NOALLOC_SCRATCH_BYTES needed)";
     case FA_ERR_HIP: return g_hip_error[0] ? g_hip_error : "HIP runtime error";
     default: return "unknown status";
   }

@@ -66,7 +66,7 @@ typedef enum fa_status {
     FA_ERR_ALIGN = 7,      /* a pointer is misaligned                            */
     FA_ERR_HIP = 8,        /* the HIP runtime reported an error                  */
     FA_ERR_ALIAS = 9,      /* o, lse or a workspace overlaps an input or another */
-    FA_ERR_WORKSPACE = 10  /* workspace smaller than fa_splitkv_workspace_bytes  */
+    FA_ERR_WORKSPACE = 10  /* workspace too small (or scratch too small: _noalloc) */
 } fa_status;
 
 typedef enum fa_dtype {
@@ -202,6 +202,37 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    int B, int Hq, int Hkv, int N_q, int N_kv, int d,
                    float scale, int causal, int dtype, int num_splits,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Allocation-free form of fa_fwd_splitkv, for callers that cannot allocate
+ * or hand over device memory at call time: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same operation,
+ * arguments (minus the workspace), checks, kernels and result as
+ * fa_fwd_splitkv: for the same inputs and num_splits the outputs are
+ * bitwise identical.
+ *
+ * The chunk results go to a device array inside the library instead of a
+ * caller workspace: FA_NOALLOC_SCRATCH_BYTES (16 MiB) per GPU, part of the
+ * library's code object, held until the process ends.  The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine); its first
+ * call on a device looks up that device's copy of the array once.  Sizes
+ * whose fa_splitkv_workspace_bytes(B, Hq, N_q, d, num_splits) exceeds
+ * FA_NOALLOC_SCRATCH_BYTES return FA_ERR_WORKSPACE before any HIP call (e.g.
+ * a decoding step of B = 8, Hq = 28, N_q = 1, d = 128 fits up to 145 splits).
+ *
+ * The array belongs to the GPU that `stream` runs on (NULL: the current
+ * device); q, k, v, o and lse must be on that GPU.  Every call on one GPU
+ * shares its array, which keeps the last call's contents; each call rewrites
+ * every part it later reads, so nothing needs clearing.  Calls that overlap
+ * in time on one GPU (different streams, or different host threads without
+ * ordering) race on the array and give wrong results: order them on one
+ * stream.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (16 << 20)
+
+int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int Hq, int Hkv, int N_q, int N_kv, int d,
+                           float scale, int causal, int dtype, int num_splits, void* stream);
 
 /*
  * Split-KV forward over paged K/V caches, for serving.  The course page

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
                           "fa_launch_info", "fa_splitkv_workspace_bytes",
                           "fa_splitkv_default_splits", "fa_fwd_splitkv",
                           "fa_bwd_workspace_bytes", "fa_bwd", "fa_fwd_fp8",
-                          "fa_fwd_paged"}
+                          "fa_fwd_paged", "fa_fwd_splitkv_noalloc"}
     for n in names:
         assert hasattr(lib, n), n
         assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
@@ -308,3 +308,21 @@ def test_paged_rejects_on_host(lib):
     assert paged(o=KC + 64) == fa.FA_ERR_ALIAS          # output inside a cache
     assert paged(ws=TB) == fa.FA_ERR_ALIAS              # workspace over the block table
     assert paged(lse=O + 16) == fa.FA_ERR_ALIAS         # outputs over each other
+
+
+def test_noalloc_rejects_on_host(lib):
+    """fa_fwd_splitkv_noalloc checks everything on the host first: invalid
+    arguments and sizes whose chunk results exceed its scratch array return
+    before any HIP call (no GPU in this process: reaching HIP would give
+    FA_ERR_HIP)."""
+    f = lib.fa_fwd_splitkv_noalloc
+    # B=8 Hq=28 N_q=1 d=128: 115584 bytes per split; 145 splits fit in 16 MiB, 146 do not.
+    per = fa.fa_splitkv_workspace_bytes(8, 28, 1, 128, 1)
+    assert per == 8 * 28 * 129 * 4
+    assert 145 * per <= fa.FA_NOALLOC_SCRATCH_BYTES < 146 * per
+    st = f(Q, K, V, O, L, 8, 28, 4, 1, 32768, 128, 0.1, 0, fa.FA_BF16, 146, None)
+    assert st == fa.FA_ERR_WORKSPACE
+    assert f(Q, K, V, O, L, 8, 28, 4, 1, 1000, 128, 0.1, 0, fa.FA_F32, 8, None) == fa.FA_ERR_DTYPE
+    assert f(0, K, V, O, L, 8, 28, 4, 1, 32768, 128, 0.1, 0, fa.FA_BF16, 8, None) == fa.FA_ERR_NULL_PTR
+    assert f(Q, K, V, O, L, 8, 28, 4, 1, 100, 128, 0.1, 0, fa.FA_BF16, 5, None) == fa.FA_ERR_BAD_DIM
+    assert f(Q, K, V, Q, L, 8, 28, 4, 1, 100, 128, 0.1, 0, fa.FA_BF16, 2, None) == fa.FA_ERR_ALIAS
