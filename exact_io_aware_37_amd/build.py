@@ -2,7 +2,9 @@
 
     python -m exact_io_aware_37_amd.build
 
-compiles csrc/fa_fwd.hip for gfx950 into exact_io_aware_37_amd/libfa.so.
+runs csrc/gen_fwd_w64.py (which writes csrc/fa_fwd_w64.inc, the assembly
+body of the 64-row forward kernel) and compiles csrc/fa_fwd.hip for gfx950
+into exact_io_aware_37_amd/libfa.so.
 Every HIP source is built with packed-fp32 instruction selection disabled
 (``-Xclang -target-feature -Xclang -packed-fp32-ops``); hipcc's host pass
 warns that it does not know that feature, which is harmless.
@@ -30,8 +32,19 @@ def hipcc() -> str:
     return exe
 
 
+def generate() -> str:
+    """Write csrc/fa_fwd_w64.inc (the 64-row forward body) from its generator."""
+    sys.path.insert(0, os.path.join(PKG_DIR, "csrc"))
+    try:
+        import gen_fwd_w64
+    finally:
+        sys.path.pop(0)
+    return gen_fwd_w64.write_inc()
+
+
 def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile the library; returns the path of the built shared object."""
+    """Generate the asm body, compile the library; returns the built shared object's path."""
+    generate()
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-shared",
            "-Wall", "-Wno-unused-result", f"-I{INCLUDE}",

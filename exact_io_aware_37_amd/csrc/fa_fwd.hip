@@ -606,6 +606,130 @@ attn_fwd_mfma16(Params p) {
   attn_fwd_mfma16_body<T, D, CAUSAL>(p);
 }
 
+// ------------------------------------ 64 rows per wave (bf16 / f16, d = 128)
+//
+// The same computation as attn_fwd_mfma16 with each wave owning 64 query
+// rows instead of 32, one wave per SIMD (4 waves, 256 rows per workgroup):
+// every K and V fragment read from LDS feeds two matrix instructions, half
+// the LDS traffic per FLOP.  O and Q live in accumulation registers, scores
+// and probabilities in vector registers; that split, the register
+// assignment and the instruction schedule are written out by
+// gen_fwd_w64.py, whose header describes them, into fa_fwd_w64.inc, and the
+// whole per-workgroup computation (Q load, the K/V DMA ring of 4 stages
+// issued 3 tiles ahead, one barrier per tile, masking of ragged and
+// causal-diagonal tiles, the lazy exponent reference, the epilogue with
+// O staged through LDS for whole-row stores) runs in one inline-asm statement.
+// This function computes the statement's operands: buffer descriptors and
+// the per-lane LDS and memory offsets of the layouts below.
+
+#include "fa_fwd_w64.inc"
+
+typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor words (stride 0, bounds `bytes`): loads past the end
+// return zero, stores past it are dropped.
+__device__ __forceinline__ u32x4s raw_desc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4s{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+
+template <typename T, bool CAUSAL>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+attn_fwd_w64(Params p) {
+  constexpr int D = 128;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[8 * 16384];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_t*)lds;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, half = lane >> 5;
+
+  int b, hq, qt;
+  map_block(p, CAUSAL, b, hq, qt);
+  const int hkv = hq / p.group;
+  const int q0 = qt * 256;
+  const int q0w = q0 + 64 * wave;
+  const size_t qhead = (size_t)(b * p.Hq + hq) * p.Nq;
+  const size_t kvhead = (size_t)(b * p.Hkv + hkv) * p.Nkv;
+  const u32x4s rq = raw_desc(static_cast<const uint16_t*>(p.q) + qhead * D, (uint32_t)p.Nq * 256u);
+  const u32x4s rk = raw_desc(static_cast<const uint16_t*>(p.k) + kvhead * D, (uint32_t)p.Nkv * 256u);
+  const u32x4s rv = raw_desc(static_cast<const uint16_t*>(p.v) + kvhead * D, (uint32_t)p.Nkv * 256u);
+  const u32x4s ro = raw_desc(static_cast<uint16_t*>(p.o) + qhead * D, (uint32_t)p.Nq * 256u);
+  const u32x4s rl = raw_desc(p.lse + qhead, (uint32_t)p.Nq * 4u);
+
+  // DMA share: wave w moves 1 KiB chunks 8w .. 8w+7 of each 32 KiB stage
+  // (K tile = chunks 0-15, V tile = 16-31); chunk c, lane l writes 16 bytes
+  // of row 4c + l/16 at logical 16-byte column l % 16, stored at column
+  // (l % 16) ^ swizzle(row): K rows swizzle by row % 16 (the 16 lanes that
+  // read one logical column of 16 rows hit 16 distinct bank groups), V rows by
+  // 4 * (row % 4) (a transposed read touches 4 rows x 4 columns).
+  const bool isv = wave >= 2;
+  const u32x4s rdma = isv ? rv : rk;
+  const int ci0 = (8 * wave) & 15;
+  const uint32_t dmabase = lds0 + (isv ? 65536u : 0u) + (uint32_t)ci0 * 1024u;
+  uint32_t dmaoff[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int row = (ci0 + u) * 4 + (lane >> 4);
+    const int sw = isv ? ((row & 3) << 2) : (row & 15);
+    dmaoff[u] = (uint32_t)(row * 256 + (((lane & 15) ^ sw) * 16));
+  }
+  // K fragment (A operand of S^T = K Q^T): key row l32 of a 32-key block,
+  // logical column 2cd + half, physical column ^ (row % 16).
+  const int swz = l32 & 15;
+  const uint32_t kbase = (uint32_t)(l32 * 256 + ((half ^ (swz & 1)) * 16) + ((swz >> 1) * 32));
+  // V^T fragment (A operand of O^T += V^T P^T) by ds_read_b64_tr_b16: lane
+  // (g, s) of its 16-lane group addresses key row 4*(g/2) + s/4 and 4
+  // dimensions at 16*(g%2) + 4*(s%4); the read hands lane r of the group the
+  // 4 keys of dimension 16*(g%2) + r.
+  const int g16 = lane >> 4, s16 = lane & 15;
+  const int vrow = (g16 >> 1) * 4 + (s16 >> 2);
+  const uint32_t vbase = (uint32_t)(vrow * 256 + (vrow & 3) * 64 + (g16 & 1) * 32 +
+                                    ((s16 & 3) >> 1) * 16 + (s16 & 1) * 8);
+  const uint32_t kaddr0 = lds0 + (kbase ^ 0u), kaddr1 = lds0 + (kbase ^ 32u),
+                 kaddr2 = lds0 + (kbase ^ 64u), kaddr3 = lds0 + (kbase ^ 96u),
+                 kaddr4 = lds0 + (kbase ^ 128u), kaddr5 = lds0 + (kbase ^ 160u),
+                 kaddr6 = lds0 + (kbase ^ 192u), kaddr7 = lds0 + (kbase ^ 224u);
+  const uint32_t vaddr0 = lds0 + 65536u + (vbase ^ 0u), vaddr1 = lds0 + 65536u + (vbase ^ 64u),
+                 vaddr2 = lds0 + 65536u + (vbase ^ 128u), vaddr3 = lds0 + 65536u + (vbase ^ 192u);
+  // Q rows q0w + 32h + l32, dimensions 16cd + 8*half (+ 8192 bytes for h = 1)
+  const uint32_t qoff = (uint32_t)((q0w + l32) * 256 + half * 16);
+  // Mask limit: key j of row i is kept iff j <= min(N_kv - 1, causal ? i : inf)
+  const int big = 0x3fffffff;
+  const int lim0 = min(p.Nkv - 1, CAUSAL ? q0w + l32 : big);
+  const int lim1 = min(p.Nkv - 1, CAUSAL ? q0w + 32 + l32 : big);
+  // Epilogue: row q0w + 4i + lane/16, 16-byte column lane % 16; lse of row q0w + 32h + l32
+  const uint32_t ooff = (uint32_t)((q0w + (lane >> 4)) * 256 + (lane & 15) * 16);
+  const uint32_t lseoff = (uint32_t)((q0w + l32) * 4);
+  const uint32_t obase = lds0 + (uint32_t)wave * 16384u;
+
+  const int kv_end = CAUSAL ? min(p.Nkv, q0 + 256) : p.Nkv;
+  const uint32_t ntiles = (uint32_t)((kv_end + 63) / 64);
+  const uint32_t nmain = (uint32_t)(CAUSAL ? min((q0 + 1) / 64, p.Nkv / 64) : p.Nkv / 64);
+  const uint32_t sl2 = __float_as_uint(p.sl2);
+  const uint32_t qxor = p.qmode == 1 ? 0x80008000u : 0u;
+  const uint32_t qand = p.qmode == 2 ? 0u : 0xffffffffu;
+
+#define FA_W64_OPERANDS                                                                     \
+  [rq] "s"(rq), [rdma] "s"(rdma), [ro] "s"(ro), [rl] "s"(rl), [dmabase] "s"(dmabase),       \
+      [sl2] "s"(sl2), [qxor] "s"(qxor), [qand] "s"(qand), [ntiles] "s"(ntiles),             \
+      [nmain] "s"(nmain), [obase] "s"(obase), [kaddr0] "v"(kaddr0), [kaddr1] "v"(kaddr1),  \
+      [kaddr2] "v"(kaddr2), [kaddr3] "v"(kaddr3), [kaddr4] "v"(kaddr4), [kaddr5] "v"(kaddr5), \
+      [kaddr6] "v"(kaddr6), [kaddr7] "v"(kaddr7), [vaddr0] "v"(vaddr0), [vaddr1] "v"(vaddr1), \
+      [vaddr2] "v"(vaddr2), [vaddr3] "v"(vaddr3), [dmaoff0] "v"(dmaoff[0]),                 \
+      [dmaoff1] "v"(dmaoff[1]), [dmaoff2] "v"(dmaoff[2]), [dmaoff3] "v"(dmaoff[3]),         \
+      [qoff] "v"(qoff), [lim0] "v"(lim0), [lim1] "v"(lim1), [ooff] "v"(ooff),              \
+      [lseoff] "v"(lseoff)
+  if constexpr (sizeof(T) == 2 && __is_same(T, __bf16)) {
+    if constexpr (CAUSAL) asm volatile(FA_W64_BF16_CAUSAL : : FA_W64_OPERANDS : FA_W64_CLOBBERS);
+    else asm volatile(FA_W64_BF16_FULL : : FA_W64_OPERANDS : FA_W64_CLOBBERS);
+  } else {
+    if constexpr (CAUSAL) asm volatile(FA_W64_F16_CAUSAL : : FA_W64_OPERANDS : FA_W64_CLOBBERS);
+    else asm volatile(FA_W64_F16_FULL : : FA_W64_OPERANDS : FA_W64_CLOBBERS);
+  }
+#undef FA_W64_OPERANDS
+}
+
 // ----------------------------------------------------- FP8 (e4m3) path
 //
 // The FlashAttention-3 direction the course page "FlashAttention:
@@ -2205,10 +2329,15 @@ int run32(const Params& p, long long blocks, hipStream_t stream) {
   return launch(attn_fwd_mfma_f32<D, CAUSAL>, C::LDS_BYTES, p, blocks, C::NT, stream);
 }
 
+template <typename T, bool CAUSAL>
+int run_w64(const Params& p, long long blocks, hipStream_t stream) {
+  return launch(attn_fwd_w64<T, CAUSAL>, 0, p, blocks, 256, stream);
+}
+
 template <typename T>
 int dispatch16(const Params& p, int d, bool causal, long long blocks, hipStream_t s) {
   if (d == 64) return causal ? run16<T, 64, true>(p, blocks, s) : run16<T, 64, false>(p, blocks, s);
-  return causal ? run16<T, 128, true>(p, blocks, s) : run16<T, 128, false>(p, blocks, s);
+  return causal ? run_w64<T, true>(p, blocks, s) : run_w64<T, false>(p, blocks, s);
 }
 
 template <int D, bool CAUSAL>

@@ -1,0 +1,815 @@
+"""Generator of the 64-row-per-wave attention forward body for gfx950.
+
+    python -m exact_io_aware_37_amd.csrc.gen_fwd_w64      (run by the build)
+
+writes ``fa_fwd_w64.inc`` beside this file: one string constant per kernel
+variant (bf16 / f16 inputs, causal or not, head dimension 128) holding the
+whole per-workgroup computation as gfx950 assembly, which the kernel in
+``fa_fwd.hip`` runs in one inline-asm statement after computing addresses and
+buffer descriptors in C++.
+
+What the body computes is the recurrence of the course page "FlashAttention:
+IO-aware attention kernel" (section 3.2: new row maximum, rescale the old sum
+and accumulator by exp(m_old - m_new), add the tile's exponentials; divide by
+the sum once at the end) inside the query-tile-outer, key-tile-inner loop of
+its sections 2 and 3.3, for the 64 query rows of one wave, with the lazy
+exponent reference of the 16-bit kernel (the reference moves only when the
+row maximum passes it by more than 2^8; O / l and lse do not depend on where
+it sits).
+
+Why assembly.  A wave that owns 64 query rows reads every K and V fragment
+from LDS once for two matrix instructions, half the LDS bytes per FLOP of the
+32-row layout.  Its live state is O (128 registers), Q (64), two score tiles
+(128) and P (32): more than the 256 vector registers of a wave, so O and Q sit
+in accumulation registers (AGPRs), which only the matrix instructions and
+moves touch, while scores and probabilities stay in VGPRs for the vector
+units.  The compiler picks one register form per function for every matrix
+instruction and cannot express that split; here every register is assigned
+by hand, and the matrix instructions, LDS reads, DMA transfers and vector
+instructions of a tile are interleaved by the list scheduler below, which
+also inserts the wait states gfx950 needs between dependent instructions
+(the hardware does not check them for matrix results).
+
+Register map (per wave; one wave per SIMD, 512 registers):
+  a[0:127]    O^T accumulators, block (h, db): a[16*(4h+db) : +16]
+  a[128:191]  Q^T operand, (h, cd): a[128 + 4*(8h+cd) : +4]
+  v[0:127]    two score buffers; buffer b, block (h, kt): v[64b + 16*(2h+kt) : +16]
+  v[128:159]  P, (h, kt, cc): v[128 + 4*(4h+2kt+cc) : +4]
+  v[160:175]  K fragment ring (4 slots), v[176:191] V fragment ring (4 slots)
+  v[192:229]  row statistics and temporaries
+  v230..v255  left to the compiler for the statement's operands
+h: which 32-row half of the wave's rows; kt: which 32 keys of a 64-key tile;
+cd: which 16 head dimensions; db: which 32 output dimensions; cc: which 16
+keys of a 32-key block.  Lane layouts are those of v_mfma_f32_32x32x16:
+lane l of a 16-register accumulator holds column l % 32 and rows
+8*(r/4) + 4*(l/32) + r%4 in register r.
+"""
+
+from __future__ import annotations
+
+import os
+import re
+import sys
+
+D = 128
+BC = 64
+ROWB = 2 * D
+KSTAGE = BC * ROWB          # bytes of one K (or V) tile in LDS
+VRING = 4 * KSTAGE          # the V ring starts after the 4-stage K ring
+NSTAGE = 4
+MFMA_CYCLES = 32            # v_mfma_f32_32x32x16: 8 passes of 4 cycles
+SLOT_BUDGET = 28            # issue cycles for other instructions per matrix instruction
+
+# ----------------------------------------------------------------- registers
+
+
+def O(h, db):
+    b = 16 * (4 * h + db)
+    return f"a[{b}:{b + 15}]"
+
+
+def Q(h, cd):
+    b = 128 + 4 * (8 * h + cd)
+    return f"a[{b}:{b + 3}]"
+
+
+def S(buf, h, kt):
+    b = 64 * buf + 16 * (2 * h + kt)
+    return f"v[{b}:{b + 15}]"
+
+
+def s1(buf, h, kt, r):
+    return f"v{64 * buf + 16 * (2 * h + kt) + r}"
+
+
+def P(h, kt, cc):
+    b = 128 + 4 * (4 * h + 2 * kt + cc)
+    return f"v[{b}:{b + 3}]"
+
+
+def p1(h, kt, cc, w):
+    return f"v{128 + 4 * (4 * h + 2 * kt + cc) + w}"
+
+
+def KF(slot):
+    b = 160 + 4 * slot
+    return f"v[{b}:{b + 3}]"
+
+
+def VF(slot):
+    b = 176 + 4 * slot
+    return f"v[{b}:{b + 3}]"
+
+
+def VFlo(slot):
+    b = 176 + 4 * slot
+    return f"v[{b}:{b + 1}]"
+
+
+def VFhi(slot):
+    b = 178 + 4 * slot
+    return f"v[{b}:{b + 1}]"
+
+
+MRUN = ["v192", "v193"]      # exponent reference per half (log2 units)
+LRUN = ["v194", "v195"]      # this lane's part of the row sum
+MX = ["v196", "v197"]        # tile row maximum
+MXS = ["v198", "v199"]       # its partner-half copy
+MNEW = ["v200", "v201"]
+ALPHA = ["v202", "v203"]
+TMP = ["v204", "v205"]
+LIMR = ["v206", "v207"]      # mask limit relative to the tile's first key (+4*half)
+LIMH = ["v208", "v209"]      # mask limit minus 4*half (per lane, per half)
+NEGINF = "v210"
+HALF4 = "v211"
+ETMP = [f"v{212 + i}" for i in range(18)]   # v212..v229: epilogue / rescale temporaries
+
+# SGPR temporaries (clobbered by the statement)
+S_TOFF = "s72"       # byte offset of the tile being transferred (tile index * 16 KiB)
+S_TOFF2 = "s73"      # S_TOFF + 4 KiB
+S_T = "s74"          # index of the tile whose scores are being formed
+S_KV0 = "s75"        # its first key
+S_TMP = "s76"
+S_M0 = "s77"         # saved M0
+S_H8K = "s78"        # 8192 (row offset of the second query half)
+S_T2 = "s79"         # tile index mod 4
+MASKS = ["s[80:81]", "s[82:83]", "s[84:85]"]
+S_ANY = "s[86:87]"
+SGPR_CLOBBERS = [f"s{i}" for i in range(72, 88)]
+
+# ---------------------------------------------------------------- instructions
+
+
+class Ins:
+    """One instruction with what the scheduler and the checker need to know.
+
+    kind: 'mfma', 'valu', 'trans' (v_exp/v_log/v_rcp), 'lds', 'vmem', 'salu',
+    'nop', 'wait', 'barrier', 'label', 'branch', 'cmp' (VALU writing an SGPR
+    mask).  reads / writes: register names (single 32-bit registers)."""
+
+    __slots__ = ("text", "kind", "reads", "writes", "cost", "srcab")
+
+    def __init__(self, text, kind, reads=(), writes=(), cost=4, srcab=()):
+        self.text = text
+        self.kind = kind
+        self.reads = tuple(reads)
+        self.writes = tuple(writes)
+        self.cost = cost
+        self.srcab = tuple(srcab)
+
+
+def regs(spec):
+    """Expand 'v[4:7]' / 'a[0:15]' / 'v12' / 's[80:81]' into single registers."""
+    out = []
+    for part in spec if isinstance(spec, (list, tuple)) else [spec]:
+        m = re.fullmatch(r"([vas])\[(\d+):(\d+)\]", part)
+        if m:
+            out += [f"{m.group(1)}{i}" for i in range(int(m.group(2)), int(m.group(3)) + 1)]
+        elif re.fullmatch(r"[vas]\d+", part):
+            out.append(part)
+        elif part in ("vcc", "m0"):
+            out.append(part)
+    return out
+
+
+def mfma(op, dst, a, b, c):
+    reads = regs(a) + regs(b) + (regs(c) if c != "0" else [])
+    return Ins(f"{op} {dst}, {a}, {b}, {c}", "mfma", reads, regs(dst), cost=4,
+               srcab=regs(a) + regs(b))
+
+
+def valu(text, reads, writes, kind="valu", cost=4):
+    return Ins(text, kind, regs(list(reads)), regs(list(writes)), cost)
+
+
+def raw(text, kind="salu", cost=4, reads=(), writes=()):
+    return Ins(text, kind, regs(list(reads)), regs(list(writes)), cost)
+
+
+# --------------------------------------------------------------- the scheduler
+#
+# Wait states (instruction slots; s_nop N counts N + 1) required between a
+# producer and a consumer, the rules the compiler applies on gfx950 (read
+# off its own output for these instruction pairs):
+#   matrix result (VGPR or AGPR)  -> vector read or accvgpr read : 12 (18 used)
+#   vector write                  -> matrix operand read         : 2
+#   transcendental result         -> vector read                 : 1
+#   vector write of an SGPR mask  -> vector or scalar read        : 2 (4 used)
+#   vector write                  -> v_permlane32_swap operand   : 2
+#   SALU write of M0              -> LDS DMA                     : 1
+# A matrix instruction's A/B operands are not rewritten within 8 slots of it.
+
+WS_MFMA_VALU = 18
+WS_VALU_MFMA = 2
+WS_TRANS = 1
+WS_MASK = 4
+WS_PERM = 2
+WS_WAR = 8
+
+
+class Stream:
+    def __init__(self, ins, start=0, name=""):
+        self.ins = list(ins)
+        self.pos = 0
+        self.start = start      # earliest matrix-instruction index after which it may run
+        self.name = name
+
+    def done(self):
+        return self.pos >= len(self.ins)
+
+    def peek(self):
+        return self.ins[self.pos]
+
+
+class Block:
+    """Linear instruction list with hazard-aware emission.
+
+    Tracks, per register, the wait-state counter value from which a matrix
+    consumer, a vector consumer or v_permlane32_swap may read it, and from
+    which a vector instruction may overwrite a matrix A/B operand; pads with
+    s_nop where needed and inserts s_waitcnt lgkmcnt for LDS results."""
+
+    def __init__(self):
+        self.out = []          # list of Ins
+        self.slot = 0          # running wait-state counter
+        self.rdy_m = {}        # reg -> first slot a matrix instruction may read it
+        self.rdy_v = {}        # reg -> first slot a vector/scalar instruction may read it
+        self.rdy_p = {}        # reg -> first slot v_permlane32_swap may read it
+        self.war = {}          # reg -> first slot a vector write to it may issue
+        self.m0 = 0            # first slot an LDS DMA may issue after an M0 write
+        self.lgkm = []         # outstanding LDS reads: list of register sets, oldest first
+
+    def need(self, ins):
+        """Wait states still needed before `ins` may issue."""
+        t = 0
+        k = ins.kind
+        for r in ins.reads:
+            if k == "mfma":
+                t = max(t, self.rdy_m.get(r, 0))
+            elif k == "perm":
+                t = max(t, self.rdy_v.get(r, 0), self.rdy_p.get(r, 0))
+            else:
+                t = max(t, self.rdy_v.get(r, 0))
+        if k in ("valu", "trans", "cmp", "perm", "accw", "accr"):
+            for r in ins.writes:
+                t = max(t, self.war.get(r, 0))
+        if k == "lds_dma":
+            t = max(t, self.m0)
+        return max(0, t - self.slot)
+
+    def lds_pending(self, ins):
+        rw = set(ins.reads) | set(ins.writes)
+        return any(group & rw for group in self.lgkm)
+
+    def waitcnt_for(self, ins):
+        """Emit s_waitcnt lgkmcnt(n) so that every LDS read `ins` depends on has returned."""
+        rw = set(ins.reads) | set(ins.writes)
+        idx = -1
+        for i, group in enumerate(self.lgkm):
+            if group & rw:
+                idx = i
+        if idx >= 0:
+            keep = len(self.lgkm) - idx - 1
+            assert keep <= 15
+            self._append(Ins(f"s_waitcnt lgkmcnt({keep})", "wait"))
+            self.lgkm = self.lgkm[idx + 1:]
+
+    def pad(self, n):
+        while n > 0:
+            k = min(n, 16)
+            self._append(Ins(f"s_nop {k - 1}", "nop", cost=k))
+            n -= k
+
+    def _append(self, ins):
+        self.out.append(ins)
+        start = self.slot
+        self.slot += int(ins.text.split()[1]) + 1 if ins.kind == "nop" else 1
+        return start
+
+    def put(self, ins):
+        if ins.kind not in ("label", "branch", "wait", "barrier", "nop"):
+            self.waitcnt_for(ins)
+            self.pad(self.need(ins))
+        start = self._append(ins)
+        k = ins.kind
+        for r in ins.writes:
+            if k == "mfma":
+                self.rdy_m[r] = start + 1                     # accumulation chains forward
+                self.rdy_v[r] = start + 1 + WS_MFMA_VALU
+            elif k == "trans":
+                self.rdy_v[r] = start + 1 + WS_TRANS
+                self.rdy_m[r] = start + 1 + WS_VALU_MFMA
+                self.rdy_p[r] = start + 1 + WS_PERM
+            elif k == "cmp":
+                self.rdy_v[r] = start + 1 + WS_MASK
+            elif k in ("valu", "perm", "accr"):
+                self.rdy_v[r] = start + 1
+                self.rdy_m[r] = start + 1 + WS_VALU_MFMA
+                self.rdy_p[r] = start + 1 + WS_PERM
+            elif k == "accw":
+                self.rdy_m[r] = start + 1 + 4
+                self.rdy_v[r] = start + 1 + 4
+            elif k == "salu":
+                self.rdy_v[r] = start + 1
+            elif k in ("lds", "vmem"):
+                pass
+        if k == "salu" and "m0" in ins.writes:
+            self.m0 = start + 2
+        if k == "mfma":
+            for r in ins.srcab:
+                self.war[r] = max(self.war.get(r, 0), start + 1 + WS_WAR)
+        if k == "lds":
+            self.lgkm.append(set(ins.writes))
+        return ins
+
+    def text(self):
+        return "\n".join(i.text for i in self.out)
+
+
+def schedule(block, mfmas, streams, lds_plan, budget=SLOT_BUDGET):
+    """Interleave `mfmas` (in order) with vector streams and LDS reads.
+
+    lds_plan: list of (first consuming matrix index, matrix index from which
+    the ring slot is free, [Ins ...]), issued before the first matrix
+    instruction at or after the free index.  After each matrix instruction,
+    ready stream instructions fill up to `budget` issue cycles (streams in
+    priority order, each in program order).  A matrix instruction whose
+    operands a stream still has to produce first pulls those producers in."""
+    li = 0
+    plan = sorted(lds_plan, key=lambda x: (x[1], x[0]))
+    for m, mi in enumerate(mfmas):
+        while li < len(plan) and plan[li][1] <= m:
+            for ins in plan[li][2]:
+                block.put(ins)
+            li += 1
+        need = set(mi.reads)
+        for st in streams:
+            last = -1
+            for i in range(st.pos, len(st.ins)):
+                if set(st.ins[i].writes) & need:
+                    last = i
+            while st.pos <= last:
+                block.put(st.peek())
+                st.pos += 1
+        block.put(mi)
+        spent = 0
+        progress = True
+        while spent < budget and progress:
+            progress = False
+            for st in streams:
+                if st.done() or st.start > m:
+                    continue
+                ins = st.peek()
+                if block.lds_pending(ins) or block.need(ins) > 0:
+                    continue
+                block.put(ins)
+                st.pos += 1
+                spent += ins.cost
+                progress = True
+                break
+    while li < len(plan):
+        for ins in plan[li][2]:
+            block.put(ins)
+        li += 1
+    for st in streams:
+        while not st.done():
+            block.put(st.peek())
+            st.pos += 1
+
+
+# --------------------------------------------------------------- tile pieces
+
+
+def mfma_op(dt):
+    return "v_mfma_f32_32x32x16_bf16" if dt == "bf16" else "v_mfma_f32_32x32x16_f16"
+
+
+def cvt_op(dt):
+    return "v_cvt_pk_bf16_f32" if dt == "bf16" else "v_cvt_pk_f16_f32"
+
+
+def dot_op(dt):
+    return ("v_dot2c_f32_bf16", "0x3f803f80") if dt == "bf16" else ("v_dot2c_f32_f16", "0x3c003c00")
+
+
+def s_mfmas_and_reads(dt, buf, kstage):
+    """Matrix instructions of S(buf) = K Q^T for the 64 rows, and the K reads.
+
+    Fragment f = 2*cd + kt goes to ring slot f % 4; it feeds two matrix
+    instructions (h = 0, 1)."""
+    ms = []
+    reads = []
+    for cd in range(8):
+        for kt in range(2):
+            f = 2 * cd + kt
+            off = kstage * KSTAGE + kt * (32 * ROWB)
+            rd = Ins(f"ds_read_b128 {KF(f % 4)}, {{kaddr{cd}}} offset:{off}", "lds",
+                     reads=(), writes=regs(KF(f % 4)))
+            # slot f%4 is free once fragment f-4's second matrix instruction has issued
+            reads.append((2 * f, max(0, 2 * (f - 4) + 2) if f >= 4 else 0, [rd]))
+            for h in range(2):
+                c = "0" if cd == 0 else S(buf, h, kt)
+                ms.append(mfma(mfma_op(dt), S(buf, h, kt), KF(f % 4), Q(h, cd), c))
+    return ms, reads
+
+
+def pv_mfmas_and_reads(dt, vstage, base_index):
+    """Matrix instructions of O += V^T P^T and the transposed V reads.
+
+    Fragment g = 8*kt + 4*cc + db (two ds_read_b64_tr_b16 each) goes to ring
+    slot g % 4 and feeds h = 0, 1."""
+    ms = []
+    reads = []
+    g = 0
+    for kt in range(2):
+        for cc in range(2):
+            for db in range(4):
+                off = vstage * KSTAGE + (kt * 32 + cc * 16) * ROWB
+                lo = Ins(f"ds_read_b64_tr_b16 {VFlo(g % 4)}, {{vaddr{db}}} offset:{off}", "lds",
+                         writes=regs(VFlo(g % 4)))
+                hi = Ins(f"ds_read_b64_tr_b16 {VFhi(g % 4)}, {{vaddr{db}}} offset:{off + 8 * ROWB}",
+                         "lds", writes=regs(VFhi(g % 4)))
+                free = base_index + 2 * (g - 4) + 2 if g >= 4 else 0
+                reads.append((base_index + 2 * g, free, [lo, hi]))
+                for h in range(2):
+                    ms.append(mfma(mfma_op(dt), O(h, db), VF(g % 4), P(h, kt, cc), O(h, db)))
+                g += 1
+    return ms, reads
+
+
+def exp_stream(dt, buf, hk_order):
+    """P(buf) = exp2(s * sl2 - m), packed to the input type; row sums of the packed values."""
+    dot, one = dot_op(dt)
+    ins = []
+    for (h, kt) in hk_order:
+        for cc in range(2):
+            for w in range(4):
+                r0, r1 = cc * 8 + 2 * w, cc * 8 + 2 * w + 1
+                a, b = s1(buf, h, kt, r0), s1(buf, h, kt, r1)
+                ins.append(valu(f"v_fma_f32 {a}, {a}, {{sl2}}, -{MRUN[h]}", [a, MRUN[h]], [a]))
+                ins.append(valu(f"v_fma_f32 {b}, {b}, {{sl2}}, -{MRUN[h]}", [b, MRUN[h]], [b]))
+                ins.append(valu(f"v_exp_f32 {a}, {a}", [a], [a], kind="trans", cost=8))
+                ins.append(valu(f"v_exp_f32 {b}, {b}", [b], [b], kind="trans", cost=8))
+                p = p1(h, kt, cc, w)
+                ins.append(valu(f"{cvt_op(dt)} {p}, {a}, {b}", [a, b], [p]))
+                ins.append(valu(f"{dot} {LRUN[h]}, {one}, {p}", [p, LRUN[h]], [LRUN[h]]))
+    return ins
+
+
+def mask_stream(buf, h):
+    """Scores of keys past the row's limit (tail, causal) -> -inf, for half h."""
+    ins = [valu(f"v_sub_u32_e64 {LIMR[h]}, {LIMH[h]}, {S_KV0}", [LIMH[h]], [LIMR[h]])]
+    k = 0
+    for kt in range(2):
+        for r in range(16):
+            off = kt * 32 + (r >> 2) * 8 + (r & 3)
+            m = MASKS[k % 3]
+            ins.append(valu(f"v_cmp_gt_i32 {m}, {off}, {LIMR[h]}", [LIMR[h]], [m], kind="cmp"))
+            a = s1(buf, h, kt, r)
+            ins.append(valu(f"v_cndmask_b32 {a}, {a}, {NEGINF}, {m}", [a, NEGINF, m], [a]))
+            k += 1
+    return ins
+
+
+def max_stream(buf, h, first=False):
+    """New exponent reference of half h from S(buf); alpha moves the old sums to it."""
+    vals = [s1(buf, h, kt, r) for kt in range(2) for r in range(16)]
+    ins = [valu(f"v_max3_f32 {MX[h]}, {vals[0]}, {vals[1]}, {vals[2]}", vals[:3], [MX[h]])]
+    rest = vals[3:]
+    while rest:
+        if len(rest) >= 2:
+            ins.append(valu(f"v_max3_f32 {MX[h]}, {MX[h]}, {rest[0]}, {rest[1]}",
+                            [MX[h], rest[0], rest[1]], [MX[h]]))
+            rest = rest[2:]
+        else:
+            ins.append(valu(f"v_max_f32 {MX[h]}, {MX[h]}, {rest[0]}", [MX[h], rest[0]], [MX[h]]))
+            rest = rest[1:]
+    # combine the two half-waves (lanes l and l^32 hold the same query)
+    ins.append(valu(f"v_mov_b32 {MXS[h]}, {MX[h]}", [MX[h]], [MXS[h]]))
+    ins.append(Ins(f"v_permlane32_swap_b32 {MX[h]}, {MXS[h]}", "perm", regs([MX[h], MXS[h]]),
+                   regs([MX[h], MXS[h]])))
+    ins.append(valu(f"v_max_f32 {MX[h]}, {MX[h]}, {MXS[h]}", [MX[h], MXS[h]], [MX[h]]))
+    ins.append(valu(f"v_mul_f32 {MX[h]}, {{sl2}}, {MX[h]}", [MX[h]], [MX[h]]))
+    if first:
+        # first tile: the reference is the tile maximum itself; nothing to rescale
+        ins.append(valu(f"v_mov_b32 {MRUN[h]}, {MX[h]}", [MX[h]], [MRUN[h]]))
+        return ins
+    ins.append(valu(f"v_add_f32 {TMP[h]}, 0x41000000, {MRUN[h]}", [MRUN[h]], [TMP[h]]))
+    m = MASKS[h]
+    ins.append(valu(f"v_cmp_gt_f32 {m}, {MX[h]}, {TMP[h]}", [MX[h], TMP[h]], [m], kind="cmp"))
+    ins.append(valu(f"v_cndmask_b32 {MNEW[h]}, {MRUN[h]}, {MX[h]}, {m}", [MRUN[h], MX[h], m],
+                    [MNEW[h]]))
+    ins.append(valu(f"v_sub_f32 {TMP[h]}, {MRUN[h]}, {MNEW[h]}", [MRUN[h], MNEW[h]], [TMP[h]]))
+    ins.append(valu(f"v_exp_f32 {ALPHA[h]}, {TMP[h]}", [TMP[h]], [ALPHA[h]], kind="trans", cost=8))
+    return ins
+
+
+def dma_issue(stage):
+    """The wave's 8 KiB share of the next-but-two tile: 8 x 1 KiB LDS DMA."""
+    ins = []
+    for u in range(8):
+        m0 = stage * KSTAGE + u * 1024
+        ins.append(raw(f"s_add_u32 m0, {{dmabase}}, {m0}", "salu", writes=["m0"]))
+        soff = S_TOFF if u < 4 else S_TOFF2
+        ins.append(Ins(f"buffer_load_dwordx4 {{dmaoff{u % 4}}}, {{rdma}}, {soff} offen lds",
+                       "lds_dma", cost=4))
+    ins.append(raw(f"s_add_u32 {S_TOFF}, {S_TOFF}, {KSTAGE}"))
+    ins.append(raw(f"s_add_u32 {S_TOFF2}, {S_TOFF2}, {KSTAGE}"))
+    return ins
+
+
+# ------------------------------------------------------------------ the body
+
+
+def rescale_block():
+    """O moves to the new reference (rare: lazy reference); then on to the next tile."""
+    b = Block()
+    b.pad(48)   # the last P*V products have written their AGPRs
+    t = ETMP
+    k = 0
+    for h in range(2):
+        for db in range(4):
+            for r in range(16):
+                a = 16 * (4 * h + db) + r
+                x = t[k % 16]
+                b.out.append(Ins(f"v_accvgpr_read_b32 {x}, a{a}", "accr"))
+                b.out.append(Ins(f"v_mul_f32 {x}, {x}, {ALPHA[h]}", "valu"))
+                b.out.append(Ins(f"v_accvgpr_write_b32 a{a}, {x}", "accw"))
+                k += 1
+    b.pad(8)
+    return b
+
+
+def tile_step(dt, j_parity, masked, causal, uid):
+    """Steady step j: wait for tile j+1, DMA tile j+3, S(j+1) || exp S(j), P(j)V(j) || max S(j+1).
+
+    j_parity = j % 4 selects the ring stages and score buffers."""
+    kst = (j_parity + 1) % 4
+    vst = j_parity % 4
+    dst = (j_parity + 3) % 4
+    cur, nxt = j_parity % 2, (j_parity + 1) % 2
+    b = Block()
+    b.put(Ins("s_waitcnt vmcnt(8) lgkmcnt(0)", "wait", cost=4))
+    b.put(Ins("s_barrier", "barrier", cost=4))
+    dma = dma_issue(dst)
+    ms_s, rd_s = s_mfmas_and_reads(dt, nxt, kst)
+    ms_pv, rd_pv = pv_mfmas_and_reads(dt, vst, len(ms_s))
+    # V reads of the first fragments may start during the S phase (V(j) landed long ago)
+    lds_plan = []
+    for x in rd_s:
+        lds_plan.append(x)
+    for (use, free, ins) in rd_pv:
+        lds_plan.append((use, max(free, use - 8), ins))
+    lds_plan.sort(key=lambda x: (x[1], x[0]))
+    streams = [
+        Stream(dma, 0, "dma"),
+        Stream(exp_stream(dt, cur, [(0, 0), (1, 0), (0, 1), (1, 1)]), 0, "exp"),
+    ]
+    tail = []
+    if masked:
+        tail += [raw(f"s_add_u32 {S_KV0}, {S_KV0}, {BC}")]
+        tail += mask_stream(nxt, 0) + mask_stream(nxt, 1)
+    tail += max_stream(nxt, 0) + max_stream(nxt, 1)
+    streams.append(Stream(tail, len(ms_s), "max"))
+    schedule(b, ms_s + ms_pv, streams, lds_plan)
+    if not masked:
+        b.put(raw(f"s_add_u32 {S_KV0}, {S_KV0}, {BC}"))
+    # the new reference (only now: the exponentials of S(j) above read the old one), sums, rescale
+    for h in range(2):
+        b.put(valu(f"v_mov_b32 {MRUN[h]}, {MNEW[h]}", [MNEW[h]], [MRUN[h]]))
+        b.put(valu(f"v_mul_f32 {LRUN[h]}, {LRUN[h]}, {ALPHA[h]}", [LRUN[h], ALPHA[h]], [LRUN[h]]))
+    b.put(valu(f"v_cmp_neq_f32 vcc, 1.0, {ALPHA[0]}", [ALPHA[0]], ["vcc"], kind="cmp"))
+    b.put(valu(f"v_cmp_neq_f32 {S_ANY}, 1.0, {ALPHA[1]}", [ALPHA[1]], [S_ANY], kind="cmp"))
+    b.pad(4)
+    b.put(raw(f"s_or_b64 vcc, vcc, {S_ANY}"))
+    b.put(raw("s_cbranch_vccnz .Lrescale", "branch"))
+    b.put(raw("s_branch .Lnext", "branch"))
+    return b
+
+
+def first_tile(dt, masked_first):
+    """Prologue: Q to AGPRs, zero O, DMA tiles 0-2, S(0) and its reference."""
+    b = Block()
+    b.put(raw(f"s_mov_b32 {S_M0}, m0"))
+    b.put(raw(f"s_movk_i32 {S_H8K}, 0x2000"))
+    b.put(raw(f"s_mov_b32 {S_TOFF}, 0"))
+    b.put(raw(f"s_movk_i32 {S_TOFF2}, 0x1000"))
+    b.put(raw(f"s_mov_b32 {S_KV0}, 0"))
+    # Q rows: 16 loads of 16 bytes per lane into v[0:63], then to AGPRs
+    for h in range(2):
+        for cd in range(8):
+            dst = f"v[{4 * (8 * h + cd)}:{4 * (8 * h + cd) + 3}]"
+            soff = "0" if h == 0 else S_H8K
+            b.put(Ins(f"buffer_load_dwordx4 {dst}, {{qoff}}, {{rq}}, {soff} offen offset:{cd * 32}",
+                      "vmem", writes=regs(dst)))
+    for stage in range(3):
+        for ins in dma_issue(stage):
+            b.put(ins)
+    # O = 0 while the loads are in flight
+    for i in range(128):
+        b.put(Ins(f"v_accvgpr_write_b32 a{i}, 0", "accw"))
+    b.put(valu(f"v_mov_b32 {NEGINF}, 0xff800000", [], [NEGINF]))
+    b.put(valu(f"v_mbcnt_lo_u32_b32 {HALF4}, -1, 0", [], [HALF4]))
+    b.put(valu(f"v_mbcnt_hi_u32_b32 {HALF4}, -1, {HALF4}", [HALF4], [HALF4]))
+    b.put(valu(f"v_lshrrev_b32 {HALF4}, 5, {HALF4}", [HALF4], [HALF4]))
+    b.put(valu(f"v_lshlrev_b32 {HALF4}, 2, {HALF4}", [HALF4], [HALF4]))
+    for h in range(2):
+        b.put(valu(f"v_sub_u32 {LIMH[h]}, {{lim{h}}}, {HALF4}", [HALF4], [LIMH[h]]))
+        b.put(valu(f"v_mov_b32 {LRUN[h]}, 0", [], [LRUN[h]]))
+        b.put(valu(f"v_mov_b32 {ALPHA[h]}, 1.0", [], [ALPHA[h]]))
+    b.put(Ins("s_waitcnt vmcnt(24)", "wait"))
+    for i in range(64):
+        b.put(valu(f"v_xor_b32 v{i}, {{qxor}}, v{i}", [f"v{i}"], [f"v{i}"]))
+        b.put(valu(f"v_and_b32 v{i}, {{qand}}, v{i}", [f"v{i}"], [f"v{i}"]))
+    for i in range(64):
+        b.put(Ins(f"v_accvgpr_write_b32 a{128 + i}, v{i}", "accw", reads=[f"v{i}"]))
+    b.pad(4)
+    b.put(Ins("s_waitcnt vmcnt(16)", "wait"))
+    b.put(Ins("s_barrier", "barrier"))
+    ms, rd = s_mfmas_and_reads(dt, 0, 0)
+    tail = []
+    if masked_first:
+        tail += mask_stream(0, 0) + mask_stream(0, 1)
+    tail += max_stream(0, 0, first=True) + max_stream(0, 1, first=True)
+    schedule(b, ms, [Stream(tail, len(ms), "max")], rd)
+    return b
+
+
+def drain(dt, parity):
+    """Last tile T-1 (T-1 % 4 == parity): exp S(T-1), then P V with nothing left to overlap."""
+    b = Block()
+    cur = parity % 2
+    ms_pv, rd_pv = pv_mfmas_and_reads(dt, parity % 4, 0)
+    schedule(b, ms_pv, [Stream(exp_stream(dt, cur, [(0, 0), (1, 0), (0, 1), (1, 1)]), 0, "exp")],
+             rd_pv)
+    b.put(Ins("s_branch .Lepi", "branch"))
+    return b
+
+
+def epilogue(dt):
+    """O / l through LDS to whole-row stores; lse = (m + log2 l) ln 2."""
+    b = Block()
+    b.put(Ins("s_waitcnt vmcnt(0) lgkmcnt(0)", "wait"))
+    b.put(Ins("s_barrier", "barrier"))   # every wave is done with the ring
+    t = ETMP
+    for h in range(2):
+        # l of the row = both half-waves' parts
+        b.put(valu(f"v_mov_b32 {TMP[h]}, {LRUN[h]}", [LRUN[h]], [TMP[h]]))
+        b.put(Ins(f"v_permlane32_swap_b32 {LRUN[h]}, {TMP[h]}", "perm", regs([LRUN[h], TMP[h]]),
+                  regs([LRUN[h], TMP[h]])))
+        b.put(valu(f"v_add_f32 {LRUN[h]}, {LRUN[h]}, {TMP[h]}", [LRUN[h], TMP[h]], [LRUN[h]]))
+        b.put(valu(f"v_rcp_f32 {ALPHA[h]}, {LRUN[h]}", [LRUN[h]], [ALPHA[h]], kind="trans"))
+        b.put(valu(f"v_log_f32 {TMP[h]}, {LRUN[h]}", [LRUN[h]], [TMP[h]], kind="trans"))
+        b.put(valu(f"v_add_f32 {TMP[h]}, {MRUN[h]}, {TMP[h]}", [MRUN[h], TMP[h]], [TMP[h]]))
+        b.put(valu(f"v_mul_f32 {TMP[h]}, 0x3f317218, {TMP[h]}", [TMP[h]], [TMP[h]]))
+        b.put(Ins(f"buffer_store_dword {TMP[h]}, {{lseoff}}, {{rl}}, 0 offen offset:{h * 128}",
+                  "vmem", reads=[TMP[h]]))
+    # the wave's O tile (64 rows x 256 bytes) into its own 16 KiB of LDS, row-swizzled
+    # lane (l32, half) of block (h, db) holds row 32h + l32, columns db*32 + 8g + 4*half + (0..3)
+    # byte address: row*256 + ((chunk ^ (row & 15)) * 16) + half*8, chunk = 4*db + g
+    b.put(valu(f"v_mbcnt_lo_u32_b32 {t[16]}, -1, 0", [], [t[16]]))
+    b.put(valu(f"v_mbcnt_hi_u32_b32 {t[16]}, -1, {t[16]}", [t[16]], [t[16]]))
+    b.put(valu(f"v_and_b32 {t[17]}, 31, {t[16]}", [t[16]], [t[17]]))           # l32
+    b.pad(18)
+    for h in range(2):
+        # row = 32h + l32 -> (row & 15) = l32 & 15; base = lds + row*256 + half*8
+        b.put(valu(f"v_lshlrev_b32 {t[14]}, 8, {t[17]}", [t[17]], [t[14]]))     # l32*256
+        b.put(valu(f"v_add_u32 {t[14]}, {{obase}}, {t[14]}", [t[14]], [t[14]]))
+        b.put(valu(f"v_add_u32 {t[14]}, {h * 32 * 256}, {t[14]}", [t[14]], [t[14]]))
+        b.put(valu(f"v_lshrrev_b32 {t[15]}, 2, {HALF4}", [HALF4], [t[15]]))      # half
+        b.put(valu(f"v_lshlrev_b32 {t[15]}, 3, {t[15]}", [t[15]], [t[15]]))      # half*8
+        b.put(valu(f"v_add_u32 {t[14]}, {t[14]}, {t[15]}", [t[14], t[15]], [t[14]]))
+        b.put(valu(f"v_and_b32 {t[13]}, 15, {t[17]}", [t[17]], [t[13]]))         # row & 15
+        for db in range(4):
+            for g in range(4):
+                base = 16 * (4 * h + db) + 4 * g
+                x = [t[(4 * (db * 4 + g) + i) % 12] for i in range(4)]
+                for i in range(4):
+                    b.put(Ins(f"v_accvgpr_read_b32 {x[i]}, a{base + i}", "accr", writes=[x[i]]))
+                for i in range(4):
+                    b.put(valu(f"v_mul_f32 {x[i]}, {x[i]}, {ALPHA[h]}", [x[i], ALPHA[h]], [x[i]]))
+                b.put(valu(f"{cvt_op(dt)} {x[0]}, {x[0]}, {x[1]}", [x[0], x[1]], [x[0]]))
+                b.put(valu(f"{cvt_op(dt)} {x[1]}, {x[2]}, {x[3]}", [x[2], x[3]], [x[1]]))
+                # address: base + ((4db+g) ^ (row&15)) * 16
+                b.put(valu(f"v_xor_b32 {t[12]}, {4 * db + g}, {t[13]}", [t[13]], [t[12]]))
+                b.put(valu(f"v_lshl_add_u32 {t[12]}, {t[12]}, 4, {t[14]}", [t[12], t[14]], [t[12]]))
+                b.put(Ins(f"ds_write_b64 {t[12]}, v[{x[0][1:]}:{int(x[0][1:]) + 1}]", "lds_w",
+                          reads=[t[12], x[0], x[1]]))
+    b.put(Ins("s_waitcnt lgkmcnt(0)", "wait"))
+    # read back whole rows: read i covers rows 4i .. 4i+3, lane -> row 4i + (lane >> 4),
+    # logical chunk lane & 15 at physical chunk (lane & 15) ^ (row & 15)
+    b.put(valu(f"v_lshrrev_b32 {t[15]}, 4, {t[16]}", [t[16]], [t[15]]))         # lane >> 4
+    b.put(valu(f"v_and_b32 {t[13]}, 15, {t[16]}", [t[16]], [t[13]]))            # lane & 15
+    for i in range(16):
+        row_lo = (4 * i) & 15
+        y = f"v[{int(t[0][1:]) + 4 * (i % 3)}:{int(t[0][1:]) + 4 * (i % 3) + 3}]"
+        b.put(valu(f"v_add_u32 {t[12]}, {4 * i}, {t[15]}", [t[15]], [t[12]]))    # row
+        b.put(valu(f"v_and_b32 {t[14]}, 15, {t[12]}", [t[12]], [t[14]]))
+        b.put(valu(f"v_xor_b32 {t[14]}, {t[14]}, {t[13]}", [t[14], t[13]], [t[14]]))
+        b.put(valu(f"v_lshlrev_b32 {t[12]}, 8, {t[12]}", [t[12]], [t[12]]))
+        b.put(valu(f"v_lshl_add_u32 {t[12]}, {t[14]}, 4, {t[12]}", [t[12], t[14]], [t[12]]))
+        b.put(valu(f"v_add_u32 {t[12]}, {{obase}}, {t[12]}", [t[12]], [t[12]]))
+        b.put(Ins(f"ds_read_b128 {y}, {t[12]}", "lds", writes=regs(y)))
+        b.put(Ins("s_waitcnt lgkmcnt(0)", "wait"))
+        b.lgkm = []
+        b.put(Ins(f"buffer_store_dwordx4 {y}, {{ooff}}, {{ro}}, 0 offen offset:{0}" if i == 0 else
+                  f"buffer_store_dwordx4 {y}, {{ooff}}, {{ro}}, {S_TMP} offen", "vmem",
+                  reads=regs(y)))
+        if i < 15:
+            b.put(raw(f"s_mov_b32 {S_TMP}, {(4 * (i + 1)) * 256}"))
+    b.put(raw(f"s_mov_b32 m0, {S_M0}"))
+    return b
+
+
+def body(dt, causal):
+    """The whole per-workgroup asm body as text with {operand} placeholders.
+
+    Control flow: prologue (tile 0), then one block per tile j chosen by the
+    dispatcher from j % 4 (ring stages, score buffer) and from whether tile
+    j + 1 needs a mask or does not exist (then the drain of tile j), then the
+    epilogue."""
+    # s_nop: wait states for any vector write of an operand (SGPR or VGPR) made
+    # by the compiled code just before the statement
+    parts = ["s_nop 7"]
+    pm = first_tile(dt, True)
+    pu = first_tile(dt, False)
+    parts += ["s_cmp_eq_u32 {nmain}, 0", "s_cbranch_scc1 .Lpro_m", pu.text(),
+              "s_branch .Lpro_done", ".Lpro_m:", pm.text(), ".Lpro_done:",
+              f"s_mov_b32 {S_T}, 0", "s_branch .Ldisp"]
+    parts += [".Lrescale:", rescale_block().text(),
+              ".Lnext:", f"s_add_u32 {S_T}, {S_T}, 1",
+              ".Ldisp:",
+              f"s_add_u32 {S_TMP}, {S_T}, 1",
+              f"s_and_b32 {S_T2}, {S_T}, 3",
+              f"s_cmp_ge_u32 {S_TMP}, {{ntiles}}",
+              "s_cbranch_scc1 .Ldd",
+              f"s_cmp_ge_u32 {S_TMP}, {{nmain}}",
+              "s_cbranch_scc1 .Ldm"]
+    for kind in ("u", "m", "d"):
+        if kind != "u":
+            parts.append(f".Ld{kind}:")
+        for p in range(3):
+            parts += [f"s_cmp_eq_u32 {S_T2}, {p}", f"s_cbranch_scc1 .L{kind}_{p}"]
+        parts.append(f"s_branch .L{kind}_3")
+    for p in range(4):
+        for masked in (False, True):
+            tag = f"{'m' if masked else 'u'}_{p}"
+            parts += [f".L{tag}:", tile_step(dt, p, masked, causal, tag).text()]
+        parts += [f".Ld_{p}:", drain(dt, p).text()]
+    parts += [".Lepi:", epilogue(dt).text()]
+    return "\n".join(parts) + "\n"
+
+
+OPERANDS = {
+    # name: (constraint, C++ expression supplied by the kernel)
+    "rq": "s", "rdma": "s", "ro": "s", "rl": "s",
+    "dmabase": "s", "sl2": "s", "qxor": "s", "qand": "s", "ntiles": "s", "nmain": "s",
+    "obase": "s",
+    "kaddr0": "v", "kaddr1": "v", "kaddr2": "v", "kaddr3": "v",
+    "kaddr4": "v", "kaddr5": "v", "kaddr6": "v", "kaddr7": "v",
+    "vaddr0": "v", "vaddr1": "v", "vaddr2": "v", "vaddr3": "v",
+    "dmaoff0": "v", "dmaoff1": "v", "dmaoff2": "v", "dmaoff3": "v",
+    "qoff": "v", "lim0": "v", "lim1": "v", "ooff": "v", "lseoff": "v",
+}
+
+
+def asm_text(dt, causal):
+    """Body with placeholders turned into named inline-asm operands, labels made unique."""
+    t = body(dt, causal)
+    t = re.sub(r"\{(\w+)\}", lambda m: "%[" + m.group(1) + "]", t)
+    t = t.replace(".L", ".Lfw%=_")
+    return t
+
+
+def clobbers():
+    c = [f"v{i}" for i in range(230)] + [f"a{i}" for i in range(256)]
+    return c + SGPR_CLOBBERS + ["vcc", "scc", "memory"]
+
+
+def c_macro(name, text):
+    lines = [l for l in text.split("\n") if l]
+    body = " \\\n".join('  "' + l.replace("\\", "\\\\").replace('"', '\\"') + '\\n"'
+                          for l in lines)
+    return f"#define {name} \\\n{body}\n"
+
+
+def write_inc(path=None):
+    """Write the asm bodies as string-literal macros (inline asm needs a literal)."""
+    path = path or os.path.join(os.path.dirname(os.path.abspath(__file__)), "fa_fwd_w64.inc")
+    out = ["// Generated by gen_fwd_w64.py (run by the library build): do not edit.", ""]
+    for dt in ("bf16", "f16"):
+        for causal in (False, True):
+            name = f"FA_W64_{dt.upper()}_{'CAUSAL' if causal else 'FULL'}"
+            out.append(c_macro(name, asm_text(dt, causal)))
+    out.append("#define FA_W64_CLOBBERS " + ", ".join(f'"{c}"' for c in clobbers()))
+    out.append("")
+    text = "\n".join(out)
+    old = open(path).read() if os.path.exists(path) else None
+    if old != text:
+        with open(path, "w") as f:
+            f.write(text)
+    return path
+
+
+if __name__ == "__main__":
+    print(write_inc(sys.argv[1] if len(sys.argv) > 1 else None))
