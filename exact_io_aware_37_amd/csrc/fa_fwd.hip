@@ -702,6 +702,11 @@ attn_fwd_w64(Params p) {
   const uint32_t ooff = (uint32_t)((q0w + (lane >> 4)) * 256 + (lane & 15) * 16);
   const uint32_t lseoff = (uint32_t)((q0w + l32) * 4);
   const uint32_t obase = lds0 + (uint32_t)wave * 16384u;
+  // Selector of the row-sum instruction (v_mfma_f32_16x16x32 reading P as B):
+  // lane 16g + c holds A row c, columns 8g .. 8g+7; 1.0 in rows 0 and 8 for
+  // g = 0, 2 and rows 4 and 12 for g = 1, 3, i.e. where lane % 8 == 4 * (g % 2).
+  const uint32_t one2 = __is_same(T, __bf16) ? 0x3f803f80u : 0x3c003c00u;
+  const uint32_t selv = ((lane & 7) == ((lane >> 2) & 4)) ? one2 : 0u;
 
   const int kv_end = CAUSAL ? min(p.Nkv, q0 + 256) : p.Nkv;
   const uint32_t ntiles = (uint32_t)((kv_end + 63) / 64);
@@ -719,7 +724,7 @@ attn_fwd_w64(Params p) {
       [vaddr2] "v"(vaddr2), [vaddr3] "v"(vaddr3), [dmaoff0] "v"(dmaoff[0]),                 \
       [dmaoff1] "v"(dmaoff[1]), [dmaoff2] "v"(dmaoff[2]), [dmaoff3] "v"(dmaoff[3]),         \
       [qoff] "v"(qoff), [lim0] "v"(lim0), [lim1] "v"(lim1), [ooff] "v"(ooff),              \
-      [lseoff] "v"(lseoff)
+      [lseoff] "v"(lseoff), [selv] "v"(selv)
   if constexpr (sizeof(T) == 2 && __is_same(T, __bf16)) {
     if constexpr (CAUSAL) asm volatile(FA_W64_BF16_CAUSAL : : FA_W64_OPERANDS : FA_W64_CLOBBERS);
     else asm volatile(FA_W64_BF16_FULL : : FA_W64_OPERANDS : FA_W64_CLOBBERS);

@@ -112,7 +112,6 @@ def VFhi(slot):
 
 
 MRUN = ["v192", "v193"]      # exponent reference per half (log2 units)
-LRUN = ["v194", "v195"]      # this lane's part of the row sum
 MX = ["v196", "v197"]        # tile row maximum
 MXS = ["v198", "v199"]       # its partner-half copy
 MNEW = ["v200", "v201"]
@@ -122,7 +121,12 @@ LIMR = ["v206", "v207"]      # mask limit relative to the tile's first key (+4*h
 LIMH = ["v208", "v209"]      # mask limit minus 4*half (per lane, per half)
 NEGINF = "v210"
 HALF4 = "v211"
-ETMP = [f"v{212 + i}" for i in range(18)]   # v212..v229: epilogue / rescale temporaries
+LRUN = ["v194", "v195"]      # running row sum per half (both half-waves hold all of it)
+LACC = ["v[212:215]", "v[216:219]"]   # a tile's row sums per half (register 0; the others stay 0)
+LACC0 = ["v212", "v216"]
+SEL = "v[220:223]"                     # 0/1 selector of the row-sum instruction
+ETMP = [f"v{i}" for i in range(64)]    # epilogue temporaries: score buffer 0, dead by then
+RTMP = [f"v{128 + i}" for i in range(16)]   # rescale temporaries: P, dead by then
 
 # SGPR temporaries (clobbered by the statement)
 S_TOFF = "s72"       # byte offset of the tile being transferred (tile index * 16 KiB)
@@ -172,9 +176,10 @@ def regs(spec):
     return out
 
 
-def mfma(op, dst, a, b, c):
+def mfma(op, dst, a, b, c, cycles=MFMA_CYCLES):
+    """A matrix instruction; `cost` holds the cycles it keeps the matrix pipe busy."""
     reads = regs(a) + regs(b) + (regs(c) if c != "0" else [])
-    return Ins(f"{op} {dst}, {a}, {b}, {c}", "mfma", reads, regs(dst), cost=4,
+    return Ins(f"{op} {dst}, {a}, {b}, {c}", "mfma", reads, regs(dst), cost=cycles,
                srcab=regs(a) + regs(b))
 
 
@@ -292,6 +297,8 @@ class Block:
             self.pad(self.need(ins))
         start = self._append(ins)
         k = ins.kind
+        if k == "wait" and "lgkmcnt(0)" in ins.text:
+            self.lgkm = []
         for r in ins.writes:
             if k == "mfma":
                 self.rdy_m[r] = start + 1                     # accumulation chains forward
@@ -326,24 +333,35 @@ class Block:
         return "\n".join(i.text for i in self.out)
 
 
-def schedule(block, mfmas, streams, lds_plan, budget=SLOT_BUDGET):
+def schedule(block, mfmas, streams, lds_plan, budget=SLOT_BUDGET, inserts=()):
     """Interleave `mfmas` (in order) with vector streams and LDS reads.
 
     lds_plan: list of (first consuming matrix index, matrix index from which
     the ring slot is free, [Ins ...]), issued before the first matrix
-    instruction at or after the free index.  After each matrix instruction,
-    ready stream instructions fill up to `budget` issue cycles (streams in
-    priority order, each in program order).  A matrix instruction whose
-    operands a stream still has to produce first pulls those producers in."""
+    instruction at or after the free index; `inserts`: (matrix index, [Ins])
+    emitted right before that matrix instruction.  After each matrix
+    instruction, ready stream instructions (streams in priority order, each
+    in program order) fill its shadow: the remaining stream work spread evenly
+    over the remaining matrix time, at most `budget` cycles per 32-cycle
+    instruction.  A matrix instruction whose operands a stream still has to
+    produce first pulls those producers in."""
     li = 0
     plan = sorted(lds_plan, key=lambda x: (x[1], x[0]))
+    at = {}
+    for idx, ins in inserts:
+        at.setdefault(idx, []).extend(ins)
+    mtime = [mi.cost for mi in mfmas]
     for m, mi in enumerate(mfmas):
         while li < len(plan) and plan[li][1] <= m:
             for ins in plan[li][2]:
                 block.put(ins)
             li += 1
+        for ins in at.get(m, []):
+            block.put(ins)
         need = set(mi.reads)
         for st in streams:
+            if st.start > m:
+                continue          # not yet allowed to run: it produces nothing this one reads
             last = -1
             for i in range(st.pos, len(st.ins)):
                 if set(st.ins[i].writes) & need:
@@ -352,9 +370,15 @@ def schedule(block, mfmas, streams, lds_plan, budget=SLOT_BUDGET):
                 block.put(st.peek())
                 st.pos += 1
         block.put(mi)
+        # even spread: work still queued in streams that may run from here on,
+        # over the matrix time left (this instruction's included)
+        left = sum(ins.cost for st in streams if st.start <= m for ins in st.ins[st.pos:])
+        time_left = sum(mtime[m:])
+        room = min(budget * mi.cost / MFMA_CYCLES,
+                   max(8.0, left * mi.cost / max(time_left, 1)) + 4)
         spent = 0
         progress = True
-        while spent < budget and progress:
+        while spent < room and progress:
             progress = False
             for st in streams:
                 if st.done() or st.start > m:
@@ -392,7 +416,14 @@ def dot_op(dt):
     return ("v_dot2c_f32_bf16", "0x3f803f80") if dt == "bf16" else ("v_dot2c_f32_f16", "0x3c003c00")
 
 
-def s_mfmas_and_reads(dt, buf, kstage):
+def k_read(f, kstage):
+    cd, kt = f // 2, f % 2
+    off = kstage * KSTAGE + kt * (32 * ROWB)
+    return Ins(f"ds_read_b128 {KF(f % 4)}, {{kaddr{cd}}} offset:{off}", "lds",
+               reads=(), writes=regs(KF(f % 4)))
+
+
+def s_mfmas_and_reads(dt, buf, kstage, skip=0):
     """Matrix instructions of S(buf) = K Q^T for the 64 rows, and the K reads.
 
     Fragment f = 2*cd + kt goes to ring slot f % 4; it feeds two matrix
@@ -403,10 +434,10 @@ def s_mfmas_and_reads(dt, buf, kstage):
         for kt in range(2):
             f = 2 * cd + kt
             off = kstage * KSTAGE + kt * (32 * ROWB)
-            rd = Ins(f"ds_read_b128 {KF(f % 4)}, {{kaddr{cd}}} offset:{off}", "lds",
-                     reads=(), writes=regs(KF(f % 4)))
+            rd = k_read(f, kstage)
             # slot f%4 is free once fragment f-4's second matrix instruction has issued
-            reads.append((2 * f, max(0, 2 * (f - 4) + 2) if f >= 4 else 0, [rd]))
+            if f >= skip:
+                reads.append((2 * f, max(0, 2 * (f - 4) + 2) if f >= 4 else 0, [rd]))
             for h in range(2):
                 c = "0" if cd == 0 else S(buf, h, kt)
                 ms.append(mfma(mfma_op(dt), S(buf, h, kt), KF(f % 4), Q(h, cd), c))
@@ -414,12 +445,14 @@ def s_mfmas_and_reads(dt, buf, kstage):
 
 
 def pv_mfmas_and_reads(dt, vstage, base_index):
-    """Matrix instructions of O += V^T P^T and the transposed V reads.
+    """Matrix instructions of O += V^T P^T, then the row sums of P, and the V reads.
 
     Fragment g = 8*kt + 4*cc + db (two ds_read_b64_tr_b16 each) goes to ring
     slot g % 4 and feeds h = 0, 1."""
     ms = []
     reads = []
+    first = {}
+    last = {}
     g = 0
     for kt in range(2):
         for cc in range(2):
@@ -429,17 +462,23 @@ def pv_mfmas_and_reads(dt, vstage, base_index):
                          writes=regs(VFlo(g % 4)))
                 hi = Ins(f"ds_read_b64_tr_b16 {VFhi(g % 4)}, {{vaddr{db}}} offset:{off + 8 * ROWB}",
                          "lds", writes=regs(VFhi(g % 4)))
-                free = base_index + 2 * (g - 4) + 2 if g >= 4 else 0
-                reads.append((base_index + 2 * g, free, [lo, hi]))
+                first[g] = base_index + len(ms)
                 for h in range(2):
                     ms.append(mfma(mfma_op(dt), O(h, db), VF(g % 4), P(h, kt, cc), O(h, db)))
+                last[g] = base_index + len(ms)
+                free = last[g - 4] if g >= 4 else 0
+                reads.append((first[g], free, [lo, hi]))
                 g += 1
+    # the row sums need P only: they run last, under the tile's barrier and transfers
+    for kt in range(2):
+        for cc in range(2):
+            for h in range(2):
+                ms.append(sum_mfma(dt, h, kt, cc))
     return ms, reads
 
 
 def exp_stream(dt, buf, hk_order):
-    """P(buf) = exp2(s * sl2 - m), packed to the input type; row sums of the packed values."""
-    dot, one = dot_op(dt)
+    """P(buf) = exp2(s * sl2 - m), rounded to the input type and packed as the P*V operand."""
     ins = []
     for (h, kt) in hk_order:
         for cc in range(2):
@@ -452,8 +491,22 @@ def exp_stream(dt, buf, hk_order):
                 ins.append(valu(f"v_exp_f32 {b}, {b}", [b], [b], kind="trans", cost=8))
                 p = p1(h, kt, cc, w)
                 ins.append(valu(f"{cvt_op(dt)} {p}, {a}, {b}", [a, b], [p]))
-                ins.append(valu(f"{dot} {LRUN[h]}, {one}, {p}", [p, LRUN[h]], [LRUN[h]]))
     return ins
+
+
+def sum_mfma(dt, h, kt, cc):
+    """Row sums of the rounded P of group (h, kt, cc), added to LACC[h] on the matrix pipe.
+
+    v_mfma_f32_16x16x32 reads the P operand with lane 16g + c as column c and
+    k = 8g .. 8g+7: column c holds query c (g = 0, 2: the two half-waves) and
+    query c + 16 (g = 1, 3).  The selector A is 1 at (row 0 or 8, g = 0 or 2)
+    and (row 4 or 12, g = 1 or 3), so row 0 and 8 sum query c, rows 4 and 12
+    query c + 16; register 0 of lane l is row 4 (l/16) (mod 16), column
+    l % 16: the sum of query l % 32 in both half-waves.  Summing the rounded
+    values makes O a convex combination of V rows with the weights used."""
+    op = "v_mfma_f32_16x16x32_bf16" if dt == "bf16" else "v_mfma_f32_16x16x32_f16"
+    c = "0" if (kt, cc) == (0, 0) else LACC[h]
+    return mfma(op, LACC[h], SEL, P(h, kt, cc), c, cycles=16)
 
 
 def mask_stream(buf, h):
@@ -505,7 +558,10 @@ def max_stream(buf, h, first=False):
 
 
 def dma_issue(stage):
-    """The wave's 8 KiB share of the next-but-two tile: 8 x 1 KiB LDS DMA."""
+    """The wave's 8 KiB share of a K/V tile into ring stage `stage`: 8 x 1 KiB LDS DMA.
+
+    The tile's byte offset is S_TOFF (S_TOFF2 = S_TOFF + 4 KiB for the second
+    four pieces); both advance by one tile after the issue."""
     ins = []
     for u in range(8):
         m0 = stage * KSTAGE + u * 1024
@@ -525,7 +581,7 @@ def rescale_block():
     """O moves to the new reference (rare: lazy reference); then on to the next tile."""
     b = Block()
     b.pad(48)   # the last P*V products have written their AGPRs
-    t = ETMP
+    t = RTMP
     k = 0
     for h in range(2):
         for db in range(4):
@@ -540,29 +596,55 @@ def rescale_block():
     return b
 
 
-def tile_step(dt, j_parity, masked, causal, uid):
-    """Steady step j: wait for tile j+1, DMA tile j+3, S(j+1) || exp S(j), P(j)V(j) || max S(j+1).
+def prefetch_k(b, kstage):
+    """The first 4 K fragment reads of the next tile's scores (ring slots 0-3)."""
+    for f in range(4):
+        b.put(k_read(f, kstage))
 
+
+def fold_stream():
+    """l = (l + the previous tile's sums) * alpha, both against the reference of this tile.
+
+    Runs early in a step, long after the previous tile's row-sum
+    instructions, and before this step's new alpha is formed."""
+    ins = []
+    for h in range(2):
+        ins.append(valu(f"v_add_f32 {LRUN[h]}, {LRUN[h]}, {LACC0[h]}", [LRUN[h], LACC0[h]], [LRUN[h]]))
+        ins.append(valu(f"v_mul_f32 {LRUN[h]}, {LRUN[h]}, {ALPHA[h]}", [LRUN[h], ALPHA[h]], [LRUN[h]]))
+    return ins
+
+
+def tile_step(dt, j_parity, masked, causal, uid):
+    """Steady step j: S(j+1) || exp S(j), then P(j)V(j) || max S(j+1), then row sums of P(j).
+
+    During the S phase this wave sends its share of tile j+3 into ring stage
+    (j+3) % 4 = (j-1) % 4, which every wave finished reading before the
+    previous step's barrier.  The first 4 K reads of S(j+1) were issued at the
+    end of the previous step.  Inside the P*V phase, once this wave's last V(j)
+    read has returned: wait for this wave's share of tile j+2, barrier (every
+    wave's share has landed and every wave is done with V(j)), then the first
+    K reads of S(j+2); the last matrix instructions of the tile (the row
+    sums) run while other waves reach the barrier.
     j_parity = j % 4 selects the ring stages and score buffers."""
     kst = (j_parity + 1) % 4
     vst = j_parity % 4
-    dst = (j_parity + 3) % 4
     cur, nxt = j_parity % 2, (j_parity + 1) % 2
     b = Block()
-    b.put(Ins("s_waitcnt vmcnt(8) lgkmcnt(0)", "wait", cost=4))
-    b.put(Ins("s_barrier", "barrier", cost=4))
-    dma = dma_issue(dst)
-    ms_s, rd_s = s_mfmas_and_reads(dt, nxt, kst)
+    b.lgkm = [set(regs(KF(f))) for f in range(4)]
+    ms_s, rd_s = s_mfmas_and_reads(dt, nxt, kst, skip=4)
     ms_pv, rd_pv = pv_mfmas_and_reads(dt, vst, len(ms_s))
-    # V reads of the first fragments may start during the S phase (V(j) landed long ago)
-    lds_plan = []
-    for x in rd_s:
-        lds_plan.append(x)
+    lds_plan = list(rd_s)
     for (use, free, ins) in rd_pv:
         lds_plan.append((use, max(free, use - 8), ins))
-    lds_plan.sort(key=lambda x: (x[1], x[0]))
+    # the sync point: the matrix instruction that first uses the last V fragment
+    # (so every V(j) read of this wave has been issued; the wait returns them)
+    sync_at = rd_pv[-1][0]
+    sync = [Ins("s_waitcnt vmcnt(8) lgkmcnt(0)", "wait"), Ins("s_barrier", "barrier")]
+    nextk = [k_read(f, (j_parity + 2) % 4) for f in range(4)]
     streams = [
-        Stream(dma, 0, "dma"),
+        Stream(nextk, sync_at, "nextk"),
+        Stream(dma_issue((j_parity + 3) % 4), 2, "dma"),
+        Stream(fold_stream(), 8, "fold"),
         Stream(exp_stream(dt, cur, [(0, 0), (1, 0), (0, 1), (1, 1)]), 0, "exp"),
     ]
     tail = []
@@ -570,20 +652,28 @@ def tile_step(dt, j_parity, masked, causal, uid):
         tail += [raw(f"s_add_u32 {S_KV0}, {S_KV0}, {BC}")]
         tail += mask_stream(nxt, 0) + mask_stream(nxt, 1)
     tail += max_stream(nxt, 0) + max_stream(nxt, 1)
+    # does any lane's reference move (O must then be rescaled before the next P*V)?
+    tail.append(valu(f"v_cmp_neq_f32 vcc, 1.0, {ALPHA[0]}", [ALPHA[0]], ["vcc"], kind="cmp"))
+    tail.append(valu(f"v_cmp_neq_f32 {S_ANY}, 1.0, {ALPHA[1]}", [ALPHA[1]], [S_ANY], kind="cmp"))
     streams.append(Stream(tail, len(ms_s), "max"))
-    schedule(b, ms_s + ms_pv, streams, lds_plan)
+    schedule(b, ms_s + ms_pv, streams, lds_plan, inserts=[(sync_at, sync)])
     if not masked:
         b.put(raw(f"s_add_u32 {S_KV0}, {S_KV0}, {BC}"))
-    # the new reference (only now: the exponentials of S(j) above read the old one), sums, rescale
+    # the new reference (only now: the exponentials of S(j) above read the old one)
     for h in range(2):
         b.put(valu(f"v_mov_b32 {MRUN[h]}, {MNEW[h]}", [MNEW[h]], [MRUN[h]]))
-        b.put(valu(f"v_mul_f32 {LRUN[h]}, {LRUN[h]}, {ALPHA[h]}", [LRUN[h], ALPHA[h]], [LRUN[h]]))
-    b.put(valu(f"v_cmp_neq_f32 vcc, 1.0, {ALPHA[0]}", [ALPHA[0]], ["vcc"], kind="cmp"))
-    b.put(valu(f"v_cmp_neq_f32 {S_ANY}, 1.0, {ALPHA[1]}", [ALPHA[1]], [S_ANY], kind="cmp"))
-    b.pad(4)
-    b.put(raw(f"s_or_b64 vcc, vcc, {S_ANY}"))
+    b.put(raw(f"s_or_b64 vcc, vcc, {S_ANY}", reads=["vcc", S_ANY], writes=["vcc"]))
     b.put(raw("s_cbranch_vccnz .Lrescale", "branch"))
-    b.put(raw("s_branch .Lnext", "branch"))
+    b.put(raw(f"s_add_u32 {S_T}, {S_T}, 1"))
+    if masked:
+        b.put(raw("s_branch .Ldisp", "branch"))
+    else:
+        # fast path: the next step is unmasked too -> straight on (blocks u_0..u_3 are laid out in order)
+        b.put(raw(f"s_add_u32 {S_TMP}, {S_T}, 1"))
+        b.put(raw(f"s_cmp_lt_u32 {S_TMP}, {{nmain}}"))
+        b.put(raw("s_cbranch_scc0 .Ldisp", "branch"))
+        if j_parity == 3:
+            b.put(raw("s_branch .Lu_0", "branch"))
     return b
 
 
@@ -609,13 +699,16 @@ def first_tile(dt, masked_first):
     for i in range(128):
         b.put(Ins(f"v_accvgpr_write_b32 a{i}, 0", "accw"))
     b.put(valu(f"v_mov_b32 {NEGINF}, 0xff800000", [], [NEGINF]))
+    for r in regs(SEL):
+        b.put(valu(f"v_mov_b32 {r}, {{selv}}", [], [r]))
     b.put(valu(f"v_mbcnt_lo_u32_b32 {HALF4}, -1, 0", [], [HALF4]))
     b.put(valu(f"v_mbcnt_hi_u32_b32 {HALF4}, -1, {HALF4}", [HALF4], [HALF4]))
     b.put(valu(f"v_lshrrev_b32 {HALF4}, 5, {HALF4}", [HALF4], [HALF4]))
     b.put(valu(f"v_lshlrev_b32 {HALF4}, 2, {HALF4}", [HALF4], [HALF4]))
     for h in range(2):
         b.put(valu(f"v_sub_u32 {LIMH[h]}, {{lim{h}}}, {HALF4}", [HALF4], [LIMH[h]]))
-        b.put(valu(f"v_mov_b32 {LRUN[h]}, 0", [], [LRUN[h]]))
+        for r in regs(LACC[h]) + [LRUN[h]]:
+            b.put(valu(f"v_mov_b32 {r}, 0", [], [r]))
         b.put(valu(f"v_mov_b32 {ALPHA[h]}, 1.0", [], [ALPHA[h]]))
     b.put(Ins("s_waitcnt vmcnt(24)", "wait"))
     for i in range(64):
@@ -632,15 +725,22 @@ def first_tile(dt, masked_first):
         tail += mask_stream(0, 0) + mask_stream(0, 1)
     tail += max_stream(0, 0, first=True) + max_stream(0, 1, first=True)
     schedule(b, ms, [Stream(tail, len(ms), "max")], rd)
+    # tile 1 visible to every wave, then the first K reads of S(1)
+    b.put(Ins("s_waitcnt vmcnt(8) lgkmcnt(0)", "wait"))
+    b.put(Ins("s_barrier", "barrier"))
+    b.lgkm = []
+    prefetch_k(b, 1)
     return b
 
 
 def drain(dt, parity):
     """Last tile T-1 (T-1 % 4 == parity): exp S(T-1), then P V with nothing left to overlap."""
     b = Block()
+    b.lgkm = [set(regs(KF(f))) for f in range(4)]   # the K reads issued for a next tile
     cur = parity % 2
     ms_pv, rd_pv = pv_mfmas_and_reads(dt, parity % 4, 0)
-    schedule(b, ms_pv, [Stream(exp_stream(dt, cur, [(0, 0), (1, 0), (0, 1), (1, 1)]), 0, "exp")],
+    schedule(b, ms_pv, [Stream(fold_stream(), 0, "fold"),
+                        Stream(exp_stream(dt, cur, [(0, 0), (1, 0), (0, 1), (1, 1)]), 0, "exp")],
              rd_pv)
     b.put(Ins("s_branch .Lepi", "branch"))
     return b
@@ -653,13 +753,13 @@ def epilogue(dt):
     b.put(Ins("s_barrier", "barrier"))   # every wave is done with the ring
     t = ETMP
     for h in range(2):
-        # l of the row = both half-waves' parts
-        b.put(valu(f"v_mov_b32 {TMP[h]}, {LRUN[h]}", [LRUN[h]], [TMP[h]]))
-        b.put(Ins(f"v_permlane32_swap_b32 {LRUN[h]}, {TMP[h]}", "perm", regs([LRUN[h], TMP[h]]),
-                  regs([LRUN[h], TMP[h]])))
-        b.put(valu(f"v_add_f32 {LRUN[h]}, {LRUN[h]}, {TMP[h]}", [LRUN[h], TMP[h]], [LRUN[h]]))
-        b.put(valu(f"v_rcp_f32 {ALPHA[h]}, {LRUN[h]}", [LRUN[h]], [ALPHA[h]], kind="trans"))
-        b.put(valu(f"v_log_f32 {TMP[h]}, {LRUN[h]}", [LRUN[h]], [TMP[h]], kind="trans"))
+        # l of the row (both half-waves hold the whole sum), the last tile's sums added
+        lr = LRUN[h]
+        if h == 0:
+            b.pad(18)
+        b.put(valu(f"v_add_f32 {lr}, {lr}, {LACC0[h]}", [lr, LACC0[h]], [lr]))
+        b.put(valu(f"v_rcp_f32 {ALPHA[h]}, {lr}", [lr], [ALPHA[h]], kind="trans"))
+        b.put(valu(f"v_log_f32 {TMP[h]}, {lr}", [lr], [TMP[h]], kind="trans"))
         b.put(valu(f"v_add_f32 {TMP[h]}, {MRUN[h]}, {TMP[h]}", [MRUN[h], TMP[h]], [TMP[h]]))
         b.put(valu(f"v_mul_f32 {TMP[h]}, 0x3f317218, {TMP[h]}", [TMP[h]], [TMP[h]]))
         b.put(Ins(f"buffer_store_dword {TMP[h]}, {{lseoff}}, {{rl}}, 0 offen offset:{h * 128}",
@@ -752,9 +852,9 @@ def body(dt, causal):
             parts += [f"s_cmp_eq_u32 {S_T2}, {p}", f"s_cbranch_scc1 .L{kind}_{p}"]
         parts.append(f"s_branch .L{kind}_3")
     for p in range(4):
-        for masked in (False, True):
-            tag = f"{'m' if masked else 'u'}_{p}"
-            parts += [f".L{tag}:", tile_step(dt, p, masked, causal, tag).text()]
+        parts += [f".Lu_{p}:", tile_step(dt, p, False, causal, f"u_{p}").text()]
+    for p in range(4):
+        parts += [f".Lm_{p}:", tile_step(dt, p, True, causal, f"m_{p}").text()]
         parts += [f".Ld_{p}:", drain(dt, p).text()]
     parts += [".Lepi:", epilogue(dt).text()]
     return "\n".join(parts) + "\n"
@@ -769,7 +869,7 @@ OPERANDS = {
     "kaddr4": "v", "kaddr5": "v", "kaddr6": "v", "kaddr7": "v",
     "vaddr0": "v", "vaddr1": "v", "vaddr2": "v", "vaddr3": "v",
     "dmaoff0": "v", "dmaoff1": "v", "dmaoff2": "v", "dmaoff3": "v",
-    "qoff": "v", "lim0": "v", "lim1": "v", "ooff": "v", "lseoff": "v",
+    "qoff": "v", "lim0": "v", "lim1": "v", "ooff": "v", "lseoff": "v", "selv": "v",
 }
 
 

@@ -283,6 +283,12 @@ class Emu:
     def op_s_cmp_ge_u32(self, w, a, line):
         w.scc = int(self.sread(w, a[0]) >= self.sread(w, a[1]))
 
+    def op_s_cmp_lt_u32(self, w, a, line):
+        w.scc = int(self.sread(w, a[0]) < self.sread(w, a[1]))
+
+    def op_s_cbranch_scc0(self, w, a, line):
+        return self.labels[a[0]] if not w.scc else None
+
     def op_s_branch(self, w, a, line):
         return self.labels[a[0]]
 
@@ -415,6 +421,32 @@ class Emu:
             out.append(u32((c + prod[rows, lanes % 32]).astype(np.float32)))
         for r in range(16):
             self.vwrite(w, D, out[r], r)
+
+    def _mfma16(self, w, a, conv):
+        """v_mfma_f32_16x16x32: lane l holds A[l % 16][8*(l/16) + e], B[8*(l/16) + e][l % 16]
+        and D[4*(l/16) + r][l % 16] in register r."""
+        D, A, B, C = a
+        lanes = np.arange(L)
+        av = np.stack([self.vread(w, A, k) for k in range(4)])
+        bv = np.stack([self.vread(w, B, k) for k in range(4)])
+        A_m = np.zeros((16, 32), np.float64)
+        B_m = np.zeros((32, 16), np.float64)
+        for e in range(8):
+            A_m[lanes % 16, 8 * (lanes // 16) + e] = conv((av[e // 2] >> (16 * (e % 2))) & 0xFFFF)
+            B_m[8 * (lanes // 16) + e, lanes % 16] = conv((bv[e // 2] >> (16 * (e % 2))) & 0xFFFF)
+        prod = A_m @ B_m
+        out = []
+        for r in range(4):
+            c = np.zeros(L, np.float64) if C == "0" else f32(self.vread(w, C, r)).astype(np.float64)
+            out.append(u32((c + prod[4 * (lanes // 16) + r, lanes % 16]).astype(np.float32)))
+        for r in range(4):
+            self.vwrite(w, D, out[r], r)
+
+    def op_v_mfma_f32_16x16x32_bf16(self, w, a, line):
+        self._mfma16(w, a, lambda b: bf16_val(b).astype(np.float64))
+
+    def op_v_mfma_f32_16x16x32_f16(self, w, a, line):
+        self._mfma16(w, a, lambda b: f16_val(b).astype(np.float64))
 
     def op_v_mfma_f32_32x32x16_bf16(self, w, a, line):
         self._mfma(w, a, lambda b: bf16_val(b).astype(np.float64))

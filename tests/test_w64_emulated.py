@@ -29,7 +29,7 @@ TOL = 2e-2
 KBUF, VBUF, QBUF, OBUF, LBUF = 1, 2, 3, 4, 5
 
 
-def operands(wave, q0, Nq, Nkv, causal, scale, qhead_bytes=0, kvhead_bytes=0):
+def operands(wave, q0, Nq, Nkv, causal, scale, dt="bf16", qhead_bytes=0, kvhead_bytes=0):
     """Inline-asm operands of one wave: register name -> value (per lane or scalar)."""
     lane = np.arange(64)
     l32, half = lane & 31, lane >> 5
@@ -77,6 +77,8 @@ def operands(wave, q0, Nq, Nkv, causal, scale, qhead_bytes=0, kvhead_bytes=0):
     vv["lim0"], vv["lim1"] = lim
     vv["ooff"] = (q0w + (lane >> 4)) * 256 + (lane & 15) * 16
     vv["lseoff"] = (q0w + l32) * 4
+    one = 0x3F803F80 if dt == "bf16" else 0x3C003C00
+    vv["selv"] = np.where((lane & 7) == ((lane >> 2) & 4), one, 0)
     return sv, vv
 
 
@@ -109,7 +111,7 @@ def run_workgroup(text, q, k, v, q0, causal, scale, dt, order):
             OBUF: np.full(Nq * 256, 0xFF, np.uint8), LBUF: np.full(Nq * 4, 0xFF, np.uint8)}
     emu = Emu(body, bufs, order=order)
     for w in range(4):
-        sv, vv = operands(w, q0, Nq, Nkv, causal, scale)
+        sv, vv = operands(w, q0, Nq, Nkv, causal, scale, dt)
         wave = emu.waves[w]
         for n, val in sv.items():
             r = gen.regs(sreg[n])
