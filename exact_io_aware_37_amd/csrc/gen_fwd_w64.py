@@ -82,51 +82,58 @@ def s1(buf, h, kt, r):
     return f"v{64 * buf + 16 * (2 * h + kt) + r}"
 
 
-def P(h, kt, cc):
-    b = 128 + 4 * (4 * h + 2 * kt + cc)
+def P(buf, h, kt, cc):
+    """P of group (h, kt, cc), packed in place over the first 4 of its 8 scores."""
+    b = 64 * buf + 16 * (2 * h + kt) + 8 * cc
     return f"v[{b}:{b + 3}]"
 
 
-def p1(h, kt, cc, w):
-    return f"v{128 + 4 * (4 * h + 2 * kt + cc) + w}"
+def p1(buf, h, kt, cc, w):
+    return s1(buf, h, kt, 8 * cc + w)
+
+
+KSLOTS = 6    # K fragment ring depth
+VLEAD = 12    # V reads may start this many matrix instructions before their use
+MAX_FIRST = False  # True: the row-maximum work of S(j+1) outranks the remaining exponentials of S(j)
+VSLOTS = 6    # V fragment ring depth
 
 
 def KF(slot):
-    b = 160 + 4 * slot
+    b = 128 + 4 * slot
     return f"v[{b}:{b + 3}]"
 
 
 def VF(slot):
-    b = 176 + 4 * slot
+    b = 128 + 4 * KSLOTS + 4 * slot
     return f"v[{b}:{b + 3}]"
 
 
 def VFlo(slot):
-    b = 176 + 4 * slot
+    b = 128 + 4 * KSLOTS + 4 * slot
     return f"v[{b}:{b + 1}]"
 
 
 def VFhi(slot):
-    b = 178 + 4 * slot
+    b = 130 + 4 * KSLOTS + 4 * slot
     return f"v[{b}:{b + 1}]"
 
 
-MRUN = ["v192", "v193"]      # exponent reference per half (log2 units)
-MX = ["v196", "v197"]        # tile row maximum
-MXS = ["v198", "v199"]       # its partner-half copy
-MNEW = ["v200", "v201"]
-ALPHA = ["v202", "v203"]
-TMP = ["v204", "v205"]
-LIMR = ["v206", "v207"]      # mask limit relative to the tile's first key (+4*half)
-LIMH = ["v208", "v209"]      # mask limit minus 4*half (per lane, per half)
-NEGINF = "v210"
-HALF4 = "v211"
+MRUN = ["v176", "v177"]      # exponent reference per half (log2 units)
+MX = ["v178", "v179"]        # tile row maximum
+MXS = ["v180", "v181"]       # its partner-half copy
+MNEW = ["v182", "v183"]
+ALPHA = ["v184", "v185"]
+TMP = ["v186", "v187"]
+LIMR = ["v188", "v189"]      # mask limit relative to the tile's first key (+4*half)
+LIMH = ["v190", "v191"]      # mask limit minus 4*half (per lane, per half)
+NEGINF = "v192"
+HALF4 = "v193"
 LRUN = ["v194", "v195"]      # running row sum per half (both half-waves hold all of it)
-LACC = ["v[212:215]", "v[216:219]"]   # a tile's row sums per half (register 0; the others stay 0)
-LACC0 = ["v212", "v216"]
-SEL = "v[220:223]"                     # 0/1 selector of the row-sum instruction
+SEL = "v[196:199]"           # 0/1 selector of the row-sum instruction
+LACC = ["v[200:203]", "v[204:207]"]   # a tile's row sums per half (register 0; the others stay 0)
+LACC0 = ["v200", "v204"]
+RTMP = [f"v{208 + i}" for i in range(16)]   # rescale temporaries
 ETMP = [f"v{i}" for i in range(64)]    # epilogue temporaries: score buffer 0, dead by then
-RTMP = [f"v{128 + i}" for i in range(16)]   # rescale temporaries: P, dead by then
 
 # SGPR temporaries (clobbered by the statement)
 S_TOFF = "s72"       # byte offset of the tile being transferred (tile index * 16 KiB)
@@ -419,14 +426,14 @@ def dot_op(dt):
 def k_read(f, kstage):
     cd, kt = f // 2, f % 2
     off = kstage * KSTAGE + kt * (32 * ROWB)
-    return Ins(f"ds_read_b128 {KF(f % 4)}, {{kaddr{cd}}} offset:{off}", "lds",
-               reads=(), writes=regs(KF(f % 4)))
+    return Ins(f"ds_read_b128 {KF(f % KSLOTS)}, {{kaddr{cd}}} offset:{off}", "lds",
+               reads=(), writes=regs(KF(f % KSLOTS)))
 
 
 def s_mfmas_and_reads(dt, buf, kstage, skip=0):
     """Matrix instructions of S(buf) = K Q^T for the 64 rows, and the K reads.
 
-    Fragment f = 2*cd + kt goes to ring slot f % 4; it feeds two matrix
+    Fragment f = 2*cd + kt goes to ring slot f % KSLOTS; it feeds two matrix
     instructions (h = 0, 1)."""
     ms = []
     reads = []
@@ -435,20 +442,20 @@ def s_mfmas_and_reads(dt, buf, kstage, skip=0):
             f = 2 * cd + kt
             off = kstage * KSTAGE + kt * (32 * ROWB)
             rd = k_read(f, kstage)
-            # slot f%4 is free once fragment f-4's second matrix instruction has issued
+            # the ring slot is free once fragment f-KSLOTS's second matrix instruction has issued
             if f >= skip:
-                reads.append((2 * f, max(0, 2 * (f - 4) + 2) if f >= 4 else 0, [rd]))
+                reads.append((2 * f, 2 * (f - KSLOTS) + 2 if f >= KSLOTS else 0, [rd]))
             for h in range(2):
                 c = "0" if cd == 0 else S(buf, h, kt)
-                ms.append(mfma(mfma_op(dt), S(buf, h, kt), KF(f % 4), Q(h, cd), c))
+                ms.append(mfma(mfma_op(dt), S(buf, h, kt), KF(f % KSLOTS), Q(h, cd), c))
     return ms, reads
 
 
-def pv_mfmas_and_reads(dt, vstage, base_index):
+def pv_mfmas_and_reads(dt, vstage, base_index, buf):
     """Matrix instructions of O += V^T P^T, then the row sums of P, and the V reads.
 
     Fragment g = 8*kt + 4*cc + db (two ds_read_b64_tr_b16 each) goes to ring
-    slot g % 4 and feeds h = 0, 1."""
+    slot g % VSLOTS and feeds h = 0, 1."""
     ms = []
     reads = []
     first = {}
@@ -458,22 +465,22 @@ def pv_mfmas_and_reads(dt, vstage, base_index):
         for cc in range(2):
             for db in range(4):
                 off = vstage * KSTAGE + (kt * 32 + cc * 16) * ROWB
-                lo = Ins(f"ds_read_b64_tr_b16 {VFlo(g % 4)}, {{vaddr{db}}} offset:{off}", "lds",
-                         writes=regs(VFlo(g % 4)))
-                hi = Ins(f"ds_read_b64_tr_b16 {VFhi(g % 4)}, {{vaddr{db}}} offset:{off + 8 * ROWB}",
-                         "lds", writes=regs(VFhi(g % 4)))
+                lo = Ins(f"ds_read_b64_tr_b16 {VFlo(g % VSLOTS)}, {{vaddr{db}}} offset:{off}", "lds",
+                         writes=regs(VFlo(g % VSLOTS)))
+                hi = Ins(f"ds_read_b64_tr_b16 {VFhi(g % VSLOTS)}, {{vaddr{db}}} offset:{off + 8 * ROWB}",
+                         "lds", writes=regs(VFhi(g % VSLOTS)))
                 first[g] = base_index + len(ms)
                 for h in range(2):
-                    ms.append(mfma(mfma_op(dt), O(h, db), VF(g % 4), P(h, kt, cc), O(h, db)))
+                    ms.append(mfma(mfma_op(dt), O(h, db), VF(g % VSLOTS), P(buf, h, kt, cc), O(h, db)))
                 last[g] = base_index + len(ms)
-                free = last[g - 4] if g >= 4 else 0
+                free = last[g - VSLOTS] if g >= VSLOTS else 0
                 reads.append((first[g], free, [lo, hi]))
                 g += 1
     # the row sums need P only: they run last, under the tile's barrier and transfers
     for kt in range(2):
         for cc in range(2):
             for h in range(2):
-                ms.append(sum_mfma(dt, h, kt, cc))
+                ms.append(sum_mfma(dt, buf, h, kt, cc))
     return ms, reads
 
 
@@ -489,12 +496,12 @@ def exp_stream(dt, buf, hk_order):
                 ins.append(valu(f"v_fma_f32 {b}, {b}, {{sl2}}, -{MRUN[h]}", [b, MRUN[h]], [b]))
                 ins.append(valu(f"v_exp_f32 {a}, {a}", [a], [a], kind="trans", cost=8))
                 ins.append(valu(f"v_exp_f32 {b}, {b}", [b], [b], kind="trans", cost=8))
-                p = p1(h, kt, cc, w)
+                p = p1(buf, h, kt, cc, w)     # in place: the scores it overwrites are consumed
                 ins.append(valu(f"{cvt_op(dt)} {p}, {a}, {b}", [a, b], [p]))
     return ins
 
 
-def sum_mfma(dt, h, kt, cc):
+def sum_mfma(dt, buf, h, kt, cc):
     """Row sums of the rounded P of group (h, kt, cc), added to LACC[h] on the matrix pipe.
 
     v_mfma_f32_16x16x32 reads the P operand with lane 16g + c as column c and
@@ -506,7 +513,7 @@ def sum_mfma(dt, h, kt, cc):
     values makes O a convex combination of V rows with the weights used."""
     op = "v_mfma_f32_16x16x32_bf16" if dt == "bf16" else "v_mfma_f32_16x16x32_f16"
     c = "0" if (kt, cc) == (0, 0) else LACC[h]
-    return mfma(op, LACC[h], SEL, P(h, kt, cc), c, cycles=16)
+    return mfma(op, LACC[h], SEL, P(buf, h, kt, cc), c, cycles=16)
 
 
 def mask_stream(buf, h):
@@ -582,7 +589,7 @@ def rescale_block():
     b = Block()
     b.pad(48)   # the last P*V products have written their AGPRs
     t = RTMP
-    k = 0
+    k = 0   # (RTMP)
     for h in range(2):
         for db in range(4):
             for r in range(16):
@@ -597,8 +604,8 @@ def rescale_block():
 
 
 def prefetch_k(b, kstage):
-    """The first 4 K fragment reads of the next tile's scores (ring slots 0-3)."""
-    for f in range(4):
+    """The first KSLOTS K fragment reads of the next tile's scores."""
+    for f in range(KSLOTS):
         b.put(k_read(f, kstage))
 
 
@@ -630,23 +637,25 @@ def tile_step(dt, j_parity, masked, causal, uid):
     vst = j_parity % 4
     cur, nxt = j_parity % 2, (j_parity + 1) % 2
     b = Block()
-    b.lgkm = [set(regs(KF(f))) for f in range(4)]
-    ms_s, rd_s = s_mfmas_and_reads(dt, nxt, kst, skip=4)
-    ms_pv, rd_pv = pv_mfmas_and_reads(dt, vst, len(ms_s))
+    b.lgkm = [set(regs(KF(f))) for f in range(KSLOTS)]
+    ms_s, rd_s = s_mfmas_and_reads(dt, nxt, kst, skip=KSLOTS)
+    ms_pv, rd_pv = pv_mfmas_and_reads(dt, vst, len(ms_s), cur)
     lds_plan = list(rd_s)
     for (use, free, ins) in rd_pv:
-        lds_plan.append((use, max(free, use - 8), ins))
+        lds_plan.append((use, max(free, use - VLEAD), ins))
     # the sync point: the matrix instruction that first uses the last V fragment
     # (so every V(j) read of this wave has been issued; the wait returns them)
     sync_at = rd_pv[-1][0]
     sync = [Ins("s_waitcnt vmcnt(8) lgkmcnt(0)", "wait"), Ins("s_barrier", "barrier")]
-    nextk = [k_read(f, (j_parity + 2) % 4) for f in range(4)]
+    nextk = [k_read(f, (j_parity + 2) % 4) for f in range(KSLOTS)]
     streams = [
         Stream(nextk, sync_at, "nextk"),
         Stream(dma_issue((j_parity + 3) % 4), 2, "dma"),
         Stream(fold_stream(), 8, "fold"),
-        Stream(exp_stream(dt, cur, [(0, 0), (1, 0), (0, 1), (1, 1)]), 0, "exp"),
     ]
+    exps = Stream(exp_stream(dt, cur, [(0, 0), (1, 0), (0, 1), (1, 1)]), 0, "exp")
+    if not MAX_FIRST:
+        streams.append(exps)
     tail = []
     if masked:
         tail += [raw(f"s_add_u32 {S_KV0}, {S_KV0}, {BC}")]
@@ -656,6 +665,8 @@ def tile_step(dt, j_parity, masked, causal, uid):
     tail.append(valu(f"v_cmp_neq_f32 vcc, 1.0, {ALPHA[0]}", [ALPHA[0]], ["vcc"], kind="cmp"))
     tail.append(valu(f"v_cmp_neq_f32 {S_ANY}, 1.0, {ALPHA[1]}", [ALPHA[1]], [S_ANY], kind="cmp"))
     streams.append(Stream(tail, len(ms_s), "max"))
+    if MAX_FIRST:
+        streams.append(exps)
     schedule(b, ms_s + ms_pv, streams, lds_plan, inserts=[(sync_at, sync)])
     if not masked:
         b.put(raw(f"s_add_u32 {S_KV0}, {S_KV0}, {BC}"))
@@ -736,9 +747,9 @@ def first_tile(dt, masked_first):
 def drain(dt, parity):
     """Last tile T-1 (T-1 % 4 == parity): exp S(T-1), then P V with nothing left to overlap."""
     b = Block()
-    b.lgkm = [set(regs(KF(f))) for f in range(4)]   # the K reads issued for a next tile
+    b.lgkm = [set(regs(KF(f))) for f in range(KSLOTS)]   # the K reads issued for a next tile
     cur = parity % 2
-    ms_pv, rd_pv = pv_mfmas_and_reads(dt, parity % 4, 0)
+    ms_pv, rd_pv = pv_mfmas_and_reads(dt, parity % 4, 0, cur)
     schedule(b, ms_pv, [Stream(fold_stream(), 0, "fold"),
                         Stream(exp_stream(dt, cur, [(0, 0), (1, 0), (0, 1), (1, 1)]), 0, "exp")],
              rd_pv)
