@@ -74,12 +74,11 @@ def measured_traffic(workload_name: str):
     """HBM bytes per launch recorded under profiles/ for this workload, or None.
 
     The profile summary stores the FETCH_SIZE + WRITE_SIZE bytes (scaled by a
-    plain-copy calibration) together with the sha256 of the kernel source it
-    was taken with; a changed kernel makes the figure stale, so it is dropped.
+    plain-copy calibration) together with the sha256 of the kernel sources it
+    was taken with (kernel_source_sha); a changed kernel makes the figure
+    stale, so it is dropped.
     """
-    import hashlib
     path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload_name}.md")
-    src = os.path.join(ROOT, "exact_io_aware_37_amd", "csrc", "fa_fwd.hip")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -89,11 +88,19 @@ def measured_traffic(workload_name: str):
             fields[key.strip()] = val.strip()
     if "traffic_bytes_per_launch" not in fields:
         return None
-    with open(src, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
-    if fields.get("traffic_kernel_source_sha256") != sha:
+    if fields.get("traffic_kernel_source_sha256") != kernel_source_sha():
         return None
     return float(fields["traffic_bytes_per_launch"])
+
+
+def kernel_source_sha() -> str:
+    """sha256 over the kernel sources: fa_fwd.hip and the generator of its 64-row body."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in ("fa_fwd.hip", "gen_fwd_w64.py"):
+        with open(os.path.join(ROOT, "exact_io_aware_37_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def power_context(fa, w, qd, kd, vd, o, lse, scale, stream, dcode, fp8_descales=None):
