@@ -633,11 +633,17 @@ __device__ __forceinline__ u32x4s raw_desc(const void* base, uint32_t bytes) {
   return u32x4s{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
 }
 
+// Launch shape: 4 waves of 64 rows, 64-key tiles, a 4-stage ring of one K
+// and one V tile (16 KiB each) per stage.
+struct CfgW64 {
+  static constexpr int BR = 256, BC = 64, NT = 256, LDS_BYTES = 8 * 16384;
+};
+
 template <typename T, bool CAUSAL>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(CfgW64::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 attn_fwd_w64(Params p) {
   constexpr int D = 128;
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[8 * 16384];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[CfgW64::LDS_BYTES];
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_t*)lds;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -647,7 +653,7 @@ attn_fwd_w64(Params p) {
   int b, hq, qt;
   map_block(p, CAUSAL, b, hq, qt);
   const int hkv = hq / p.group;
-  const int q0 = qt * 256;
+  const int q0 = qt * CfgW64::BR;
   const int q0w = q0 + 64 * wave;
   const size_t qhead = (size_t)(b * p.Hq + hq) * p.Nq;
   const size_t kvhead = (size_t)(b * p.Hkv + hkv) * p.Nkv;
@@ -2267,7 +2273,7 @@ Geometry geometry_for(int d, int dtype) {
     return {CfgF32<128>::BR, CfgF32<128>::BC, CfgF32<128>::NT, CfgF32<128>::LDS_BYTES};
   }
   if (d == 64) return {Cfg16<64>::BR, Cfg16<64>::BC, Cfg16<64>::NT, Cfg16<64>::LDS_BYTES};
-  return {Cfg16<128>::BR, Cfg16<128>::BC, Cfg16<128>::NT, Cfg16<128>::LDS_BYTES};
+  return {CfgW64::BR, CfgW64::BC, CfgW64::NT, CfgW64::LDS_BYTES};
 }
 
 size_t elem_size(int dtype) { return dtype == FA_F32 ? 4 : 2; }
@@ -2336,7 +2342,7 @@ int run32(const Params& p, long long blocks, hipStream_t stream) {
 
 template <typename T, bool CAUSAL>
 int run_w64(const Params& p, long long blocks, hipStream_t stream) {
-  return launch(attn_fwd_w64<T, CAUSAL>, 0, p, blocks, 256, stream);
+  return launch(attn_fwd_w64<T, CAUSAL>, 0, p, blocks, CfgW64::NT, stream);
 }
 
 template <typename T>

@@ -127,7 +127,8 @@ def test_status_strings(lib):
 def test_launch_info(lib):
     st, info = fa.fa_launch_info(2, 32, 32, 8192, 8192, 128, 0, fa.FA_BF16)
     assert st == fa.FA_OK
-    assert info["threads"] % 64 == 0 and info["rows_per_block"] % 32 == 0
+    # d = 128 in 16 bits: four waves of 64 query rows each
+    assert info["threads"] == 256 and info["rows_per_block"] == 256 and info["keys_per_tile"] == 64
     assert info["blocks"] == 2 * 32 * math.ceil(8192 / info["rows_per_block"])
     assert 0 < info["lds_bytes"] <= 160 * 1024
     st, info = fa.fa_launch_info(1, 1, 1, 256, 256, 64, 0, fa.FA_F32)
