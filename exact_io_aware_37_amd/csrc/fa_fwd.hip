@@ -114,6 +114,11 @@ __device__ __forceinline__ int xcd_local(int bid, int nb) {
 
 // ----------------------------------------------- 16-bit (bf16 / f16) path
 //
+// This 32-row-per-wave kernel serves head dimension 64; at 128 the forward
+// runs the 64-row-per-wave kernel further below (attn_fwd_w64).  The split-KV
+// and paged kernels reuse the layouts and helpers of this section at both
+// head dimensions.
+//
 // Workgroup: 8 waves x 32 query rows = 256 rows.  K/V tiles of 64 keys move
 // global -> LDS by buffer DMA (buffer_load ... lds, 16 B per lane, no VGPR
 // staging; rows past N_kv come back as zeros) into a 4-stage ring, issued two

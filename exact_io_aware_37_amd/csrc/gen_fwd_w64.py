@@ -20,7 +20,7 @@ it sits).
 Why assembly.  A wave that owns 64 query rows reads every K and V fragment
 from LDS once for two matrix instructions, half the LDS bytes per FLOP of the
 32-row layout.  Its live state is O (128 registers), Q (64), two score tiles
-(128) and P (32): more than the 256 vector registers of a wave, so O and Q sit
+(128): more than the 256 vector registers of a wave, so O and Q sit
 in accumulation registers (AGPRs), which only the matrix instructions and
 moves touch, while scores and probabilities stay in VGPRs for the vector
 units.  The compiler picks one register form per function for every matrix
@@ -33,10 +33,11 @@ also inserts the wait states gfx950 needs between dependent instructions
 Register map (per wave; one wave per SIMD, 512 registers):
   a[0:127]    O^T accumulators, block (h, db): a[16*(4h+db) : +16]
   a[128:191]  Q^T operand, (h, cd): a[128 + 4*(8h+cd) : +4]
-  v[0:127]    two score buffers; buffer b, block (h, kt): v[64b + 16*(2h+kt) : +16]
-  v[128:159]  P, (h, kt, cc): v[128 + 4*(4h+2kt+cc) : +4]
-  v[160:175]  K fragment ring (4 slots), v[176:191] V fragment ring (4 slots)
-  v[192:229]  row statistics and temporaries
+  v[0:127]    two score buffers; buffer b, block (h, kt): v[64b + 16*(2h+kt) : +16];
+              P of (h, kt, cc) is packed (two 16-bit values per register) in
+              place over the first 4 of the 8 scores it is made from
+  v[128:151]  K fragment ring (6 slots), v[152:175] V fragment ring (6 slots)
+  v[176:229]  row statistics, row-sum selector and accumulators, temporaries
   v230..v255  left to the compiler for the statement's operands
 h: which 32-row half of the wave's rows; kt: which 32 keys of a 64-key tile;
 cd: which 16 head dimensions; db: which 32 output dimensions; cc: which 16
