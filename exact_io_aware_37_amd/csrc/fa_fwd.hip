@@ -1005,9 +1005,7 @@ __device__ __forceinline__ void attn_fwd_e4m3_body(const Params& p) {
         const float e3 = fast_exp2(fmaf(s[kt][4 * w + 3], p.sl2, -mu));
         // The first conversion's upper half is rewritten by the second, so
         // its pass-through operand can be any register: e0's own, which dies
-        // here (no extra move).  It must not be pk's register: writing the
-        // registers that the last P*V product takes its B operand from gave
-        // wrong products.
+        // here (no extra move).
         int d = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, __float_as_int(e0), false);
         d = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, d, true);
         pk[kt * 4 + w] = d;
