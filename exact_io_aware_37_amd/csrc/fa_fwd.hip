@@ -822,9 +822,26 @@ __device__ __forceinline__ int swz8_v(int row) {
   return D == 128 ? ((((row >> 1) & 1) | (((row >> 3) & 1) << 1)) << 1) : (((row >> 3) & 1) << 1);
 }
 
+// The last result registers of the 8-bit 32x32x64 instruction are written 20
+// issue slots after it, one more than the compiler pads before a vector
+// read of them (measured on MI355X; the build's latency check rejects such a
+// read).  A result is therefore handed to the rest of the code through this
+// statement: it reads the result, so the compiler pads before it, and its own
+// s_nop adds 5 slots the compiler counts as one.
+__device__ __forceinline__ void settle(f32x16& x) { asm volatile("s_nop 4" : "+v"(x)); }
+
 __device__ __forceinline__ f32x16 mma_e4m3(i32x8 a, i32x8 b, f32x16 c) {
   // Format fields 0 (E4M3 for both operands), no block scales.
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// The same product with block scales on B: lane c + 32b supplies the E8M0
+// exponent (biased by 127, low byte of sb) of column c's block b of 32 K
+// values, which are bytes 16b .. 16b+15 of both lane c and lane c + 32 (the
+// instruction takes K from a lane pair in chunks of 16: measured on MI355X);
+// A is unscaled (127).
+__device__ __forceinline__ f32x16 mma_e4m3_bscaled(i32x8 a, i32x8 b, f32x16 c, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, sb);
 }
 
 template <int D, bool CAUSAL>
@@ -926,20 +943,29 @@ __device__ __forceinline__ void attn_fwd_e4m3_body(const Params& p) {
   f32x16 acc[D / 32];
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
-  // Row sums of the rounded P come from the matrix cores too, on
-  // v_mfma_f32_16x16x128_f8f6f4 with the P operand unchanged as B: that
-  // instruction reads lane 16g + c as column c, 32-byte group g, so group g
-  // holds half g/2 of query c + 16 (g % 2).  A is 1.0 on the (row, group)
-  // pairs that add up both halves of one query: rows 0 and 8 take groups 0
-  // and 2 (query c), rows 4 and 12 groups 1 and 3 (query c + 16).  Output
-  // register 0 of lane l is row 4 (l / 16), column l % 16: the sum of query
-  // l % 32 over the 64 keys of the tile; the other rows are zero.
-  f32x4 accs = f32x4{};
-  const int rsel = lane & 15, gsel = lane >> 4;
-  const bool on = ((rsel == 0 || rsel == 8) && !(gsel & 1)) || ((rsel == 4 || rsel == 12) && (gsel & 1));
-  const int onev = on ? 0x38383838 : 0;   // E4M3 1.0 in every byte
-  const i32x8 sel = {onev, onev, onev, onev, onev, onev, onev, onev};
-  float m_run = -INFINITY;   // exponent reference (log2 units), same in both half-waves
+  // Row sums of the rounded P come from the matrix cores too: the P operand
+  // (with its block scales) times an all-ones A, on the same instruction as
+  // P*V; every row of the result holds the sum of its column's query, and
+  // register 0 of lane l is the sum of query l % 32.
+  f32x16 accs = f32x16{};
+  i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                0x38383838, 0x38383838, 0x38383838, 0x38383838};   // E4M3 1.0
+  // held in its own 8 registers (as an opaque value, not rebuilt from one
+  // register before every use)
+  asm volatile("" : "+v"(ones));
+  // Exponent references (log2 units).  O and the row sum are kept against
+  // m_run, the same in both half-waves.  The probabilities of each tile are
+  // formed against the tile's own m_tile = m_run - k, with k the integer
+  // floor(m_run - tile maximum), so that the tile's largest probability lies
+  // in (1/2, 1] (exactly 1 when the tile holds the reference's own score)
+  // and the small ones keep E4M3's precision relative to their own tile
+  // instead of falling below its subnormal range against a far larger key
+  // elsewhere in the row.  The tile's factor 2^-k, a power of two, is applied
+  // exactly by the matrix instructions as the E8M0 block scale sbyte of every
+  // block of the P operand.
+  float m_run = -INFINITY;
+  float m_tile = 0.f;
+  int sbyte = 127;
 
   auto compute_s = [&](const lds_t* st, f32x16 (&s)[KT]) {
 #pragma unroll
@@ -956,6 +982,8 @@ __device__ __forceinline__ void attn_fwd_e4m3_body(const Params& p) {
         s[kt] = mma_e4m3(a, qreg[cd], s[kt]);
       }
     }
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) settle(s[kt]);
   };
 
   auto compute_pv = [&](const lds_t* st, const i32x8& pk) {
@@ -967,9 +995,12 @@ __device__ __forceinline__ void attn_fwd_e4m3_body(const Params& p) {
       for (int i = 0; i < 4; ++i)
         r[i] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(a0 + i * 16 * C::ROWB));
       const i32x8 x = {r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
-      acc[db] = mma_e4m3(x, pk, acc[db]);
+      acc[db] = mma_e4m3_bscaled(x, pk, acc[db], sbyte);
     }
-    accs = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, pk, accs, 0, 0, 0, 0, 0, 0);
+    accs = mma_e4m3_bscaled(ones, pk, accs, sbyte);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) settle(acc[db]);
+    settle(accs);
   };
 
   // New exponent reference from a tile of raw scores; O and the sum move to
@@ -985,6 +1016,13 @@ __device__ __forceinline__ void attn_fwd_e4m3_body(const Params& p) {
     const float m_new = (mc > m_run + kLazy) ? mc : m_run;
     const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
     m_run = m_new;
+    // k >= -kLazy; a tile more than 200 below the reference (or with no
+    // allowed key) is formed against m_run - 200 and scaled by byte 0: its
+    // weight, under 2^-127 of the row's, is dropped.  No finite score yet:
+    // P = 0 against reference 0.
+    const float k = fminf(floorf(m_run - mc), 200.f);
+    m_tile = m_run == -INFINITY ? 0.f : m_run - k;
+    sbyte = (int)fmaxf(127.f - k, 0.f);
     accs[0] *= alpha;
     if (wave_any(alpha != 1.f)) {
 #pragma unroll
@@ -992,9 +1030,9 @@ __device__ __forceinline__ void attn_fwd_e4m3_body(const Params& p) {
     }
   };
 
-  // P = exp2(s * sl2 - ref), rounded to E4M3 in the byte order of the P*V operand.
+  // P = exp2(s * sl2 - m_tile), rounded to E4M3 in the byte order of the P*V operand.
   auto exponentiate = [&](const f32x16 (&s)[KT], i32x8& pk) {
-    const float mu = (m_run == -INFINITY) ? 0.f : m_run;
+    const float mu = m_tile;
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll

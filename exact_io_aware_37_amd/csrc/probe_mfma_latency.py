@@ -26,7 +26,11 @@ KINDS = {
     "v_mfma_f32_16x16x32_bf16": (4, 4, 4, "0x3f803f80", 32.0),
     "v_mfma_f32_16x16x32_f16": (4, 4, 4, "0x3c003c00", 32.0),
     "v_mfma_f32_32x32x2_f32": (1, 1, 16, "1.0", 2.0),
+    # block-scaled forms, both scales 1.0 (E8M0 127 in v80 and v81)
+    "v_mfma_scale_f32_32x32x64_f8f6f4": (8, 8, 16, "0x38383838", 64.0),
+    "v_mfma_scale_f32_16x16x128_f8f6f4": (8, 8, 4, "0x38383838", 128.0),
 }
+SCALED_OPERANDS = ", v80, v81 op_sel_hi:[0,0,0]"
 WAITS = range(2, 26)
 A0, B0, D0 = 40, 50, 60
 
@@ -41,10 +45,13 @@ def source():
                 body = [f"v_mov_b32 v{A0 + i}, {one}" for i in range(na)]
                 body += [f"v_mov_b32 v{B0 + i}, {one}" for i in range(nb)]
                 body += [f"v_mov_b32 v{D0 + i}, -1.0" for i in range(nd)]
+                scaled = "_scale_" in mn
+                if scaled:
+                    body += ["v_mov_b32 v80, 127", "v_mov_b32 v81, 127"]
                 body.append("s_nop 7")
                 a = f"v[{A0}:{A0 + na - 1}]" if na > 1 else f"v{A0}"
                 b = f"v[{B0}:{B0 + nb - 1}]" if nb > 1 else f"v{B0}"
-                body.append(f"{mn} v[{D0}:{D0 + nd - 1}], {a}, {b}, 0")
+                body.append(f"{mn} v[{D0}:{D0 + nd - 1}], {a}, {b}, 0" + (SCALED_OPERANDS if scaled else ""))
                 left = n
                 while left > 0:
                     k = min(left, 8)
@@ -53,7 +60,7 @@ def source():
                 body.append(f"v_mov_b32 %[o], v{D0 + r}")
                 body += ["s_nop 7"] * 12
                 clob = ", ".join(f'"v{x}"' for x in list(range(A0, A0 + 8)) + list(range(B0, B0 + 8))
-                                 + list(range(D0, D0 + 16)))
+                                 + list(range(D0, D0 + 16)) + [80, 81])
                 src.append(f"__global__ void __launch_bounds__(64) p{vid}(float* out) {{")
                 src.append("  float o;")
                 text = "\\n".join(body)

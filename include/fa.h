@@ -135,10 +135,20 @@ int fa_launch_info(int B, int Hq, int Hkv, int N_q, int N_kv, int d, int causal,
  * accumulators; the instruction adds its 64 products with somewhat less than
  * fp32 precision); probabilities in fp32, rounded to E4M3 (round to nearest
  * even) for the P V product; the normaliser is the sum of those rounded
- * probabilities, so O is a convex combination of V rows.  The E4M3 rounding
- * of P is the dominant error: relative 2^-4 per probability in the normal
- * range, which also bounds the relative error of the summed probabilities
- * that lse is taken from.
+ * probabilities, so O is a convex combination of V rows.  The probabilities
+ * of each 64-key tile are rounded relative to that tile's own power-of-two
+ * reference (its largest probability lies in (1/2, 1]) and carried to the
+ * row's common reference by an exact power-of-two block scale of the matrix
+ * instruction.  The E4M3 rounding of P is the dominant error: relative 2^-4
+ * per probability in E4M3's normal range, which also bounds the relative
+ * error of the summed probabilities that lse is taken from.  Limits: a
+ * probability below 2^-10 of the largest one of its tile is flushed to zero
+ * (in the subnormal range, above that, the absolute error is at most 2^-10
+ * of the tile's reference), so within one tile keys far below the tile's
+ * strongest key lose their weight, while keys in other tiles keep theirs
+ * however far below the row's maximum they lie; a tile whose weight is below
+ * 2^-127 of the row's reference is dropped.  A long row with one dominant
+ * key therefore keeps the summed mass of all its other tiles.
  *
  * scale: any finite value.  descale_q, descale_k, descale_v: finite and
  * > 0 (FA_ERR_SCALE otherwise).  d: 64 or 128.  Size limits as fa_fwd with

@@ -25,7 +25,11 @@ the GPU path, which rounds the probabilities to E4M3 before the P*V product
 sum of those rounded probabilities (the convention of the 16-bit path, so
 that O is a convex combination of V rows), and forms its sums on a matrix
 instruction that does not add its 64 products in IEEE fp32 (see
-``MFMA8_SUM_REL``).
+``MFMA8_SUM_REL``).  The probabilities of each block of keys are formed
+against a power-of-two reference of that block (at least its largest
+probability, less than twice it) and carried to the row's common reference
+by an exact power-of-two factor; every block lies inside one tile of
+``P_TILE`` consecutive keys (tiles start at key 0).
 """
 
 from __future__ import annotations
@@ -75,6 +79,9 @@ def attention_fp8_fp64(q8, k8, v8, descale_q: float, descale_k: float, descale_v
 #   below 2^-10 that becomes 0 loses at most itself.
 REL_E4M3 = 2.0 ** -4
 ABS_E4M3 = 2.0 ** -10
+# keys per tile: every block of probabilities that shares one reference lies
+# inside one tile
+P_TILE = 64
 
 # The 8-bit matrix instruction (v_mfma_f32_32x32x64_f8f6f4) forms each of
 # its 64 products exactly but adds them with less than fp32 precision.
@@ -88,6 +95,21 @@ ABS_E4M3 = 2.0 ** -10
 MFMA8_SUM_REL = 2.0 ** -10
 
 
+# Fixed bars beside the per-element model: |O_gpu - O| <= 2^-3 max|V| and
+# |lse_gpu - lse| <= 2^-3 for every row.  Where every rounded probability
+# lies in E4M3's normal range relative to its block's reference, each weight
+# carries a relative error of at most 2^-4, so the normalised weights of a
+# row move by at most a factor (1 +- 2^-4) / (1 -+ 2^-4): O moves by at most
+# about 2^-4 max_j |v_j - O| <= 2^-3 max|V|, and the row sum by a factor whose
+# logarithm is below 0.065, leaving more than 0.06 of the lse bar for the
+# scores' accumulation error (2^-10 |scale| sum|q k|, about 0.007 for the
+# unit-variance inputs of the tests) and the subnormal tail.  A path that
+# loses a large part of a row's mass (for example by flushing a long row of
+# small probabilities to zero against one far larger key) fails them.
+FIXED_BAR_O_REL = 2.0 ** -3
+FIXED_BAR_LSE = 2.0 ** -3
+
+
 def _rows(Nq, rows):
     return np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64).reshape(-1)
 
@@ -95,9 +117,10 @@ def _rows(Nq, rows):
 def _rounding_terms(q, k, v, scale, causal, rows, row_chunk=None):
     """Per-row softmax terms of the rounding model (exact fp64 weights w_j).
 
-    eta_j = max(2^-4 w_j, min(w_j, 2^-10 w_max)) bounds the E4M3 rounding
-    error of key j divided by the row sum, for every position of the
-    exponent reference (see ``fp8_p_rounding_bound``).  Returns, per output
+    eta_j = max(2^-4 w_j, min(w_j, 2^-9 t_j)), t_j the largest weight of the
+    tile of key j, bounds the E4M3 rounding error of key j divided by the row
+    sum, for every block of the tile and every position of the block's
+    reference (see ``fp8_p_rounding_bound``).  Returns, per output
     element or row:
       A   = sum_j eta_j |v_j - O|        rho = sum_j eta_j
       Bw  = sum_j w_j |v_j - O|          W   = sum_j w_j |v_j|
@@ -133,7 +156,7 @@ def _rounding_terms(q, k, v, scale, causal, rows, row_chunk=None):
                     sabs = np.where(allowed, sabs, 0.0)
                 e = np.exp(s - s.max(axis=1, keepdims=True))
                 w = e / e.sum(axis=1, keepdims=True)
-                eta = np.maximum(REL_E4M3 * w, np.minimum(w, ABS_E4M3 * w.max(axis=1, keepdims=True)))
+                eta = np.maximum(REL_E4M3 * w, np.minimum(w, 2.0 * ABS_E4M3 * tile_max(w)))
                 o = w @ vb
                 dev = np.abs(vb[None, :, :] - o[:, None, :])          # |v_j - O| per row
                 A[b, h, sl] = np.einsum("rj,rjd->rd", eta, dev)
@@ -145,16 +168,32 @@ def _rounding_terms(q, k, v, scale, causal, rows, row_chunk=None):
     return A, rho, Bw, W, S, O
 
 
+def tile_max(w: np.ndarray) -> np.ndarray:
+    """Per key, the largest value of its tile of P_TILE keys along the last axis (same shape)."""
+    n = w.shape[-1]
+    t = -(-n // P_TILE)
+    pad = np.zeros(w.shape[:-1] + (t * P_TILE,), dtype=w.dtype)
+    pad[..., :n] = w
+    m = pad.reshape(w.shape[:-1] + (t, P_TILE)).max(axis=-1)
+    return np.repeat(m, P_TILE, axis=-1)[..., :n]
+
+
 def fp8_p_rounding_bound(q, k, v, scale: float, causal: bool = False, rows=None) -> np.ndarray:
     """Per-element bound on |O_gpu - O| caused by rounding P to E4M3 alone.
 
-    The GPU forms p_j = 2^(s_j - r) against an exponent reference r that is
-    never above the row maximum of the scores (it moves to a running maximum),
-    rounds every p_j to E4M3 (p~_j) and returns sum_j p~_j v_j / sum_j p~_j.
-    With the exact weights w_j (w_max their maximum), p_j = c * w_j / w_max
-    for some c >= 1, so the rounding error e_j of key j, divided by the exact
-    sum L, is at most eta_j = max(2^-4 w_j, min(w_j, 2^-10 w_max)) for every
-    admissible c.  The rounded weights p~_j / sum p~ then differ from w_j by
+    The GPU forms the probabilities of each block of keys (a subset of one
+    tile of P_TILE keys) as p_j = 2^(s_j - r_b) against a reference r_b of
+    the block whose power of two 2^r_b lies in [m_b, 2 m_b), m_b the block's
+    largest 2^(s_j); it rounds every p_j to E4M3 (p~_j), carries the block to
+    the row's common reference by an exact power of two, and returns
+    sum_j p~_j v_j / sum_j p~_j.  In units of the exact weights w_j (which sum
+    to 1), key j is rounded with a relative error of at most 2^-4 in E4M3's
+    normal range and an absolute one of at most 2^-10 times the block's
+    reference, itself below 2 t_j (t_j the largest weight of the tile), in
+    the subnormal range; a value flushed to zero loses at most itself.  So
+    the rounding error e_j of key j, divided by the exact sum L, is at most
+    eta_j = max(2^-4 w_j, min(w_j, 2^-9 t_j)) for every admissible block and
+    reference.  The rounded weights p~_j / sum p~ then differ from w_j by
     at most (eta_j + w_j rho) / (1 - rho), rho = sum eta, and since both sets
     of weights sum to 1,
         |O_gpu - O| <= (sum_j eta_j |v_j - O| + rho sum_j w_j |v_j - O|) / (1 - rho).

@@ -14,7 +14,10 @@ arithmetic of the path.  Its two sources of error:
     test_score_accumulation_model checks it on single-key rows, where lse is
     the score itself.
 plus the final bf16 rounding of O (2^-8 relative) and the fp32 arithmetic.
-Outputs are poisoned with NaN first, so an unwritten element fails.
+Beside that model every case also meets two fixed bars, |dO| <= 2^-3 max|V|
+and |dlse| <= 2^-3 (oracle.fp8_ref.FIXED_BAR_O_REL / FIXED_BAR_LSE), which a
+path that loses a sizeable part of a row's mass fails whatever the model
+admits.  Outputs are poisoned with NaN first, so an unwritten element fails.
 """
 
 import numpy as np
@@ -24,7 +27,7 @@ import torch
 import exact_io_aware_37_amd as fa
 import workloads
 from oracle import attention_fp8_fp64, dequantize_e4m3, fp8_tolerances
-from oracle.fp8_ref import MFMA8_SUM_REL
+from oracle.fp8_ref import FIXED_BAR_LSE, FIXED_BAR_O_REL, MFMA8_SUM_REL
 
 pytestmark = pytest.mark.gpu
 
@@ -59,8 +62,12 @@ def compare(name, o_gpu, l_gpu, codes, ds, causal, scale, rows=None):
     err_l = np.abs(lg - ref_l)
     say(f"    {name}: max|dO|={err_o.max():.3e} (worst err/tol {np.max(err_o / tol_o):.3f}) "
         f"max|dlse|={err_l.max():.3e} (worst err/tol {np.max(err_l / tol_l):.3f})")
+    bar_o = FIXED_BAR_O_REL * float(np.max(np.abs(deq[2])))
+    say(f"    {name}: fixed bars: max|dO| / (2^-3 max|V|) = {err_o.max() / bar_o:.3f}, "
+        f"max|dlse| / 2^-3 = {err_l.max() / FIXED_BAR_LSE:.3f}")
     assert np.all(err_o <= tol_o), float(np.max(err_o / tol_o))
     assert np.all(err_l <= tol_l), float(np.max(err_l / tol_l))
+    assert err_o.max() <= bar_o and err_l.max() <= FIXED_BAR_LSE
 
 
 def run_case(name, B, Hq, Hkv, Nq, Nkv, D, causal, seed=0, sigma=1.0, scale=None,
@@ -179,10 +186,8 @@ def test_longest_key_sequence_the_host_accepts():
     E4M3 codes of 32 times that row's unit vector, in the last key, at key 2^22 and at the
     start of the ragged last tile: its score (about 30) exceeds the log of the other keys'
     summed weight (about 16.4) by so much that the exact output is that key's V row to ~1e-6,
-    and a wrong offset changes it at order one.  (With a score near 16, where that key holds
-    ~20% of the mass, the other keys' probabilities lie below E4M3's smallest subnormal
-    relative to the reference and round to zero; the output then follows the planted key
-    alone, which the rounding model bounds but which says little about the addressing.)"""
+    and a wrong offset changes it at order one.  (The regime of a dominant key holding only
+    part of a long row's mass is test_long_rows_flat_and_dominant_key.)"""
     n_kv = (1 << 31) // (128 * 2) - 257
     codes, ds = workloads.make_inputs_fp8(1, 1, 1, 300, n_kv, 128, seed=4444)
     q8, k8, v8 = codes
@@ -197,3 +202,36 @@ def test_longest_key_sequence_the_host_accepts():
     o, l = run_gpu((q8, k8, v8), ds, False, scale)
     say(f"    max|O| over the checked rows {float(o[0, 0, rows].float().abs().max()):.3f}")
     compare("longest accepted N_kv (E4M3)", o, l, (q8, k8, v8), ds, False, scale, rows=rows)
+
+
+def test_long_rows_flat_and_dominant_key():
+    """N_kv = 2^20 + 37 keys, d = 128, two query heads on one K/V head, 64 query rows, not
+    causal; 8 rows per head go to the oracle.  Head 0 has flat scores (its Q scaled down by
+    1/16: every key carries a comparable share of the mass).  In head 1 each checked row has
+    one planted key whose score is about 12.5 above the others' typical one (e^-12 < 2^-10):
+    against a single exponent reference for the whole row every other probability would round
+    to zero, although together they hold most of the row's mass.  Against per-block
+    references they keep E4M3's precision; both heads must meet the per-element model and
+    the fixed bars."""
+    n_kv, nq, d = (1 << 20) + 37, 64, 128
+    rows = np.array([0, 5, 17, 31, 32, 50, 62, 63])
+    codes, ds = workloads.make_inputs_fp8(1, 2, 1, nq, n_kv, d, seed=4321)
+    q8, k8, v8 = codes
+    q8[0, 0] = (q8[0, 0].to(torch.float32) / 16.0).to(torch.float8_e4m3fn)
+    rng = np.random.default_rng(5)
+    planted = rng.choice(n_kv - 1000, rows.size, replace=False)
+    scale = workloads.default_scale(d)
+    for i, j in zip(rows, planted):
+        x = q8[0, 1, i].to(torch.float64) * ds[0]
+        y = (12.5 / scale) * x / (x.norm() ** 2) / ds[1]
+        k8[0, 0, j] = y.clamp(-448.0, 448.0).to(torch.float32).to(torch.float8_e4m3fn)
+    kd = k8[0, 0].to(torch.float64) * ds[1]
+    for i, j in zip(rows, planted):
+        sc = scale * (kd @ (q8[0, 1, i].to(torch.float64) * ds[0])).numpy()
+        w = np.exp(sc - sc.max())
+        share = w[j] / w.sum()
+        assert sc.argmax() == j and 0.01 < share < 0.5, (i, share)
+        assert np.median(w) < 2.0 ** -10                # flushed against a row-wide reference
+    say(f"[case] long rows: N_kv={n_kv}")
+    o, l = run_gpu((q8, k8, v8), ds, False, scale)
+    compare("long rows", o, l, (q8, k8, v8), ds, False, scale, rows=rows)

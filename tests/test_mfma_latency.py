@@ -75,6 +75,7 @@ def test_probe_source_has_every_register():
     total = sum(len(probe.WAITS) * nd for (_, _, nd, _, _) in probe.KINDS.values())
     assert src.count("__global__ void") == total
     assert set(probe.KINDS) == set(ml.NEED)
+    assert 'v_mfma_scale_f32_32x32x64_f8f6f4 v[60:75], v[40:47], v[50:57], 0, v80, v81' in src
 
 
 def test_library_device_code_passes(tmp_path):

@@ -5,9 +5,12 @@
 * ``attention_fp8_fp64`` against ``attention_fp64`` on inputs dequantised by
   torch, and against scaling laws of the dequantisation factors.
 * ``fp8_p_rounding_bound`` against a simulation of the GPU's rounding of P
-  (torch's float8_e4m3fn conversion, an independent round-to-nearest-even),
-  for every admissible position of the exponent reference; and shown not to
-  be vacuous: the slip of dividing by the unrounded sum breaks it.
+  (torch's float8_e4m3fn conversion, an independent round-to-nearest-even)
+  with a power-of-two reference per block of keys, for tiles and half-tiles
+  and every admissible reference offset; and shown not to be vacuous: the
+  slip of dividing by the unrounded sum breaks it, and so does a single
+  reference for a whole long row with one dominant key (the flush to zero
+  the per-block references avoid), which also breaks the fixed bars.
 * ``fp8_tolerances`` against a simulation of both error sources of the GPU
   path at once (scores moved by the modelled accumulation error, randomly and
   adversarially, then P rounded), and against its own special case without
@@ -23,6 +26,7 @@ import torch
 import workloads
 from oracle import (attention_fp64, attention_fp8_fp64, dequantize_e4m3, e4m3_decode,
                     fp8_p_rounding_bound, probabilities_fp64)
+from oracle.fp8_ref import FIXED_BAR_LSE, FIXED_BAR_O_REL
 
 
 def torch_decode(codes):
@@ -112,21 +116,60 @@ def test_quantisation_recipe():
 
 # ---- the tolerance model of the GPU path ----
 
-def _simulate(q, k, v, scale, causal, log2_c, fmt=torch.float8_e4m3fn):
-    """O with P formed against a reference log2_c below the row maximum, rounded to
-    ``fmt`` (torch's conversion), divided by the sum of the rounded P."""
-    w = probabilities_fp64(q, k, scale, causal)             # exact softmax rows
+def _round_blocks(w, rng=None, split=False, offsets=None, fmt=torch.float8_e4m3fn):
+    """Rounded weights of the GPU path: each block of keys (a tile of P_TILE keys, or with
+    ``split`` its two halves of keys j with (j // 4) % 2 = 0 / 1) is taken against a
+    power-of-two reference T in [m, 2m), m its largest weight, rounded to ``fmt`` (torch's
+    round-to-nearest-even) and scaled back by T exactly.  The reference offset log2(T/m) is
+    drawn from ``rng`` per block, or taken from ``offsets``."""
+    from oracle.fp8_ref import P_TILE
+    n = w.shape[-1]
+    out = np.zeros_like(w)
+    key = np.arange(n)
+    groups = []
+    for t0 in range(0, n, P_TILE):
+        tile = key[t0:t0 + P_TILE]
+        if split:
+            groups += [tile[(tile // 4) % 2 == 0], tile[(tile // 4) % 2 == 1]]
+        else:
+            groups.append(tile)
+    for gi, g in enumerate(groups):
+        if g.size == 0:
+            continue
+        m = w[..., g].max(axis=-1, keepdims=True)
+        if offsets is not None:
+            f = offsets[gi % len(offsets)]
+        else:
+            f = rng.uniform(0.0, 1.0, size=m.shape)
+        T = np.where(m > 0, m * 2.0 ** f, 1.0)
+        p = w[..., g] / T
+        pr = torch.from_numpy(np.ascontiguousarray(p)).to(fmt).to(torch.float64).numpy()
+        out[..., g] = pr * T
+    return out
+
+
+def _round_rowwide(w, log2_c, fmt=torch.float8_e4m3fn):
+    """Rounded weights with one reference for the whole row, log2_c above its largest weight:
+    the scheme the per-block references replace."""
     wmax = w.max(axis=-1, keepdims=True)
     p = (2.0 ** log2_c) * w / wmax
-    pr = torch.from_numpy(p).to(fmt).to(torch.float64).numpy()
-    B, Hq, Nq, Nkv = w.shape
-    Hkv = k.shape[1]
-    o = np.empty((B, Hq, Nq, v.shape[-1]))
+    return torch.from_numpy(p).to(fmt).to(torch.float64).numpy() * wmax / 2.0 ** log2_c
+
+
+def _output(wr, v, Hkv):
+    B, Hq = wr.shape[:2]
+    o = np.empty(wr.shape[:3] + (v.shape[-1],))
     for b in range(B):
         for h in range(Hq):
             g = h // (Hq // Hkv)
-            o[b, h] = (pr[b, h] @ v[b, g]) / pr[b, h].sum(axis=-1, keepdims=True)
+            o[b, h] = (wr[b, h] @ v[b, g]) / wr[b, h].sum(axis=-1, keepdims=True)
     return o
+
+
+def _simulate(q, k, v, scale, causal, rng=None, split=False, offsets=None):
+    """O of the GPU path's rounding of P alone (exact scores, per-block references)."""
+    w = probabilities_fp64(q, k, scale, causal)
+    return _output(_round_blocks(w, rng, split, offsets), v, k.shape[1])
 
 
 REGIMES = [("diffuse", 0.05), ("typical", 0.125), ("sharp", 0.6), ("very sharp", 2.5)]
@@ -141,9 +184,11 @@ def test_bound_holds_for_every_reference_offset(name, scale, causal):
     v = rng.standard_normal((1, 1, 300, 32))
     o_ref, _ = attention_fp64(q, k, v, scale, causal)
     bound = fp8_p_rounding_bound(q, k, v, scale, causal)
-    for log2_c in (0.0, 0.37, 1.0, 3.5, 7.9, 8.0):          # the reference may trail the max by < 2^8
-        err = np.abs(_simulate(q, k, v, scale, causal, log2_c) - o_ref)
-        assert np.all(err <= bound * (1 + 1e-9) + 1e-15), (name, log2_c, float((err - bound).max()))
+    cases = [dict(offsets=[0.0]), dict(offsets=[0.999]), dict(offsets=[0.37, 0.0, 0.9]),
+             dict(rng=rng), dict(rng=rng, split=True), dict(offsets=[0.5, 0.01], split=True)]
+    for c in cases:
+        err = np.abs(_simulate(q, k, v, scale, causal, **c) - o_ref)
+        assert np.all(err <= bound * (1 + 1e-9) + 1e-15), (name, c.keys(), float((err - bound).max()))
 
 
 def test_bound_is_not_vacuous():
@@ -157,15 +202,60 @@ def test_bound_is_not_vacuous():
     o_ref, _ = attention_fp64(q, k, v, 0.6, False)
     bound = fp8_p_rounding_bound(q, k, v, 0.6, False)
     w = probabilities_fp64(q, k, 0.6, False)
-    p = (2.0 ** 0.37) * w / w.max(axis=-1, keepdims=True)
-    pr = torch.from_numpy(p).to(torch.float8_e4m3fn).to(torch.float64).numpy()
-    o_slip = (pr[0, 0] @ v[0, 0]) / p[0, 0].sum(axis=-1, keepdims=True)
+    wr = _round_blocks(w, offsets=[0.37])
+    o_slip = (wr[0, 0] @ v[0, 0]) / w[0, 0].sum(axis=-1, keepdims=True)
     assert np.any(np.abs(o_slip - o_ref[0, 0]) > bound[0, 0])
     v = rng.standard_normal((1, 1, 64, 32))
     o_ref, _ = attention_fp64(q, k, v, 0.6, False)
     bound = fp8_p_rounding_bound(q, k, v, 0.6, False)
-    err = np.abs(_simulate(q, k, v, 0.6, False, 0.37) - o_ref)
+    err = np.abs(_simulate(q, k, v, 0.6, False, offsets=[0.37]) - o_ref)
     assert err.max() > 0.05 * bound.max()
+
+
+def test_one_reference_per_row_breaks_the_bound_and_the_fixed_bar():
+    """One key far above a long row of keys: with one reference for the whole row every other
+    probability falls below E4M3's subnormal range and is flushed, losing most of the mass;
+    the model (per-block references) and the fixed bar both reject that, and accept the
+    per-block rounding of the same row."""
+    rng = np.random.default_rng(11)
+    n = 1 << 18
+    q = np.zeros((1, 1, 1, 16))
+    q[0, 0, 0, 0] = 1.0
+    k = 0.05 * rng.standard_normal((1, 1, n, 16))
+    k[0, 0, 4321, 0] = 8.0                # e^-8 < 2^-10: the rest flush against its reference
+    v = rng.standard_normal((1, 1, n, 16))
+    o_ref, lse_ref = attention_fp64(q, k, v, 1.0)
+    w = probabilities_fp64(q, k, 1.0)
+    assert w[0, 0, 0, 4321] < 0.02 and w[0, 0, 0, 4321] > 1e-4   # the planted key holds little mass
+    bound = fp8_p_rounding_bound(q, k, v, 1.0)
+    bar_o = FIXED_BAR_O_REL * np.abs(v).max()
+    wr = _round_rowwide(w, 0.0)
+    o_row = _output(wr, v, 1)
+    assert np.any(np.abs(o_row - o_ref) > bound) and np.max(np.abs(o_row - o_ref)) > bar_o
+    lse_row = np.log(wr.sum(axis=-1)) + lse_ref
+    assert np.max(np.abs(lse_row - lse_ref)) > FIXED_BAR_LSE
+    for split in (False, True):
+        wb = _round_blocks(w, rng, split)
+        err = np.abs(_output(wb, v, 1) - o_ref)
+        assert np.all(err <= bound * (1 + 1e-9)) and err.max() <= bar_o
+        assert np.max(np.abs(np.log(wb.sum(axis=-1)))) <= FIXED_BAR_LSE
+
+
+@pytest.mark.parametrize("name,scale", [("diffuse", 0.05), ("typical", 0.125), ("sharp", 0.6)])
+def test_fixed_bar_holds_for_per_block_rounding(name, scale):
+    """The fixed bars (|dO| <= 2^-3 max|V|, |dlse| <= 2^-3) hold for the per-block rounding on
+    random rows, reference offsets drawn at random."""
+    rng = np.random.default_rng(21 + int(100 * scale))
+    q = rng.standard_normal((1, 2, 16, 64))
+    k = rng.standard_normal((1, 1, 2000, 64))
+    v = rng.standard_normal((1, 1, 2000, 64))
+    o_ref, lse_ref = attention_fp64(q, k, v, scale)
+    w = probabilities_fp64(q, k, scale)
+    for split in (False, True):
+        wb = _round_blocks(w, rng, split)
+        err = np.abs(_output(wb, v, 1) - o_ref)
+        assert err.max() <= FIXED_BAR_O_REL * np.abs(v).max()
+        assert np.max(np.abs(np.log(wb.sum(axis=-1)))) <= FIXED_BAR_LSE
 
 
 def test_bound_special_cases():
@@ -194,7 +284,7 @@ def test_bound_special_cases():
 def test_tolerances_cover_perturbed_scores_and_rounded_p(name, scale, causal):
     """Simulate the GPU path's two error sources together: every score moved by up to the
     modelled accumulation error (random, and adversarially signed against V), P formed
-    against a trailing reference, rounded to E4M3, divided by the unrounded sum."""
+    against per-block references, rounded to E4M3, divided by the rounded sum."""
     from oracle import fp8_tolerances
     from oracle.fp8_ref import MFMA8_SUM_REL
     rng = np.random.default_rng(int(scale * 100) + 7 * causal)
@@ -214,10 +304,10 @@ def test_tolerances_cover_perturbed_scores_and_rounded_p(name, scale, causal):
             eps = d * sign
         st = np.where(mask, s + eps, -np.inf)
         mx = st.max(axis=1, keepdims=True)
-        p = np.exp(st - mx) * 2.0 ** 3.3         # reference 3.3 (log2) below the maximum
-        pr = torch.from_numpy(p).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+        p = np.exp(st - mx)                       # unnormalised, largest 1
+        pr = _round_blocks(p, rng, split=trial % 2 == 1)
         o = (pr @ v[0, 0]) / pr.sum(axis=1, keepdims=True)
-        lse = mx[:, 0] - 3.3 * np.log(2.0) + np.log(pr.sum(axis=1))
+        lse = mx[:, 0] + np.log(pr.sum(axis=1))
         assert np.all(np.abs(o - o_ref[0, 0]) <= tol_o[0, 0]), (name, trial)
         assert np.all(np.abs(lse - l_ref[0, 0]) <= tol_l[0, 0]), (name, trial)
 
@@ -235,5 +325,5 @@ def test_tolerances_reduce_to_the_rounding_bound_without_score_error():
     rho = 2.0 ** -4                                    # uniform weights, all in the normal range
     pv = 2.0 ** -10 * w_abs * (1 + 2.0 ** -4) / (1 - rho)
     assert np.allclose(t0, (e + pv) * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(o) + 1e-4 * np.abs(v).max(),
-                       rtol=1e-12, atol=0)
-    assert np.allclose(l0, -np.log1p(-rho) + 2.0 ** -10 + 1e-5 * (1 + np.abs(lse)), rtol=1e-12, atol=0)
+                       rtol=1e-14, atol=0)
+    assert np.allclose(l0, -np.log1p(-rho) + 2.0 ** -10 + 1e-5 * (1 + np.abs(lse)), rtol=1e-14, atol=0)
