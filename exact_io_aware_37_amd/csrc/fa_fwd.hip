@@ -644,19 +644,20 @@ struct CfgW64 {
   static constexpr int BR = 256, BC = 64, NT = 256, LDS_BYTES = 8 * 16384;
 };
 
+// One work item (batch b, query head hq, 256-row query tile qt): operands of
+// the generated body, then the body itself.
 template <typename T, bool CAUSAL>
-__global__ void __launch_bounds__(CfgW64::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
-attn_fwd_w64(Params p) {
+__device__ __forceinline__ void w64_item(const Params& p, uint32_t lds0, int b, int hq, int qt) {
   constexpr int D = 128;
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[CfgW64::LDS_BYTES];
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_t*)lds;
-  const int tid = threadIdx.x;
+  // The lane index through an opaque copy: the per-lane operands below are
+  // then computed afresh for each item instead of being hoisted out of the
+  // persistent loop, where they could only survive the body (which uses
+  // nearly every vector register) in scratch memory.
+  int tid;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, half = lane >> 5;
-
-  int b, hq, qt;
-  map_block(p, CAUSAL, b, hq, qt);
   const int hkv = hq / p.group;
   const int q0 = qt * CfgW64::BR;
   const int q0w = q0 + 64 * wave;
@@ -744,6 +745,41 @@ attn_fwd_w64(Params p) {
     else asm volatile(FA_W64_F16_FULL : : FA_W64_OPERANDS : FA_W64_CLOBBERS);
   }
 #undef FA_W64_OPERANDS
+}
+
+// Non-causal grids: one work item per workgroup (map_block).  Causal grids
+// are persistent: min(items, CUs) workgroups, all resident from the start,
+// each taking the items of ranks bid, 2G - 1 - bid, 2G + bid, 4G - 1 - bid,
+// ... (G workgroups; ranks in map_block's causal order, longest tiles
+// first).  The zig-zag pairs long items with short ones, and no workgroup
+// waits for the hardware to dispatch it: with one workgroup per CU the
+// dispatcher hands new workgroups to the shader engines of an XCD in strict
+// rotation and holds them while the next engine in turn has no free CU,
+// which left CUs idle between short causal items.
+template <typename T, bool CAUSAL>
+__global__ void __launch_bounds__(CfgW64::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+attn_fwd_w64(Params p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[CfgW64::LDS_BYTES];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_t*)lds;
+  if constexpr (!CAUSAL) {
+    int b, hq, qt;
+    map_block(p, false, b, hq, qt);
+    w64_item<T, false>(p, lds0, b, hq, qt);
+  } else {
+    const int G = (int)gridDim.x, bid = (int)blockIdx.x;
+    const int n = p.n_heads * p.n_qtiles;
+    for (int j = 0;; ++j) {
+      const int r = (j & 1) ? (j + 1) * G - 1 - bid : j * G + bid;
+      if (r >= n) break;   // every later rank of this workgroup is larger
+      const int rr = r / p.n_heads;
+      const int hl = r - rr * p.n_heads;
+      const int b = hl / p.Hq;
+      // the previous item's epilogue staged O in the LDS this item's
+      // transfers overwrite
+      if (j) __syncthreads();
+      w64_item<T, true>(p, lds0, b, hl - b * p.Hq, p.n_qtiles - 1 - rr);
+    }
+  }
 }
 
 // ----------------------------------------------------- FP8 (e4m3) path
@@ -2381,8 +2417,34 @@ int run32(const Params& p, long long blocks, hipStream_t stream) {
   return launch(attn_fwd_mfma_f32<D, CAUSAL>, C::LDS_BYTES, p, blocks, C::NT, stream);
 }
 
+// Compute units of the device `stream` runs on (cached per device).
+int cu_count(hipStream_t stream, int* out) {
+  static std::mutex mu;
+  static int cached[64] = {0};
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e == hipSuccess && (dev < 0 || dev >= 64)) e = hipErrorInvalidDevice;
+  if (e == hipSuccess) {
+    std::lock_guard<std::mutex> lock(mu);
+    if (!cached[dev]) e = hipDeviceGetAttribute(&cached[dev], hipDeviceAttributeMultiprocessorCount, dev);
+    *out = cached[dev];
+  }
+  if (e != hipSuccess || *out < 1) {
+    snprintf(g_hip_error, sizeof g_hip_error, "HIP error: %s (%s)", hipGetErrorName(e),
+             hipGetErrorString(e));
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
 template <typename T, bool CAUSAL>
 int run_w64(const Params& p, long long blocks, hipStream_t stream) {
+  if constexpr (CAUSAL) {   // persistent grid: one workgroup per CU at most
+    int cus = 0;
+    const int st = cu_count(stream, &cus);
+    if (st != FA_OK) return st;
+    blocks = blocks < cus ? blocks : cus;
+  }
   return launch(attn_fwd_w64<T, CAUSAL>, 0, p, blocks, CfgW64::NT, stream);
 }
 
