@@ -211,6 +211,59 @@ def test_library_allocates_no_device_memory():
     assert free1 == free0
 
 
+def _peak_bytes(fn):
+    """Device memory that torch's allocator holds at the peak of fn(), above what
+    was allocated before it (every result of fn is released afterwards)."""
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    out = fn()
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated() - base
+    del out
+    return peak
+
+
+def test_peak_memory_naive_grows_quadratically_fused_linearly():
+    """The memory comparison of the causal lab in "FlashAttention: IO-aware
+    attention kernel" (section 5): B=1, 28 query heads over 4 KV heads, d=128,
+    causal, S in {1024, 2048, 4096}.  A path that materialises the S x S score and
+    probability matrices (plain torch, fp32) needs about 4 times the memory per
+    doubling of S; the fused forward needs exactly its outputs, O and lse, which
+    double with S, and nothing else (the library allocates no device memory).
+    Each naive measurement follows one untimed run of the same shape, so that
+    the workspace the matrix library allocates on first use is not counted."""
+    scale = 1.0 / math.sqrt(128)
+    naive, fused = [], []
+    for S in (1024, 2048, 4096):
+        q, k, v = case_inputs(1, 28, 4, S, S, 128, "bf16", seed=S)
+        qd, kd, vd = (x.to(DEV) for x in (q, k, v))
+        q32 = qd.float()
+        k32t = kd.float().repeat_interleave(7, dim=1).transpose(-1, -2).contiguous()
+        v32 = vd.float().repeat_interleave(7, dim=1)
+        above = torch.ones(S, S, dtype=torch.bool, device=DEV).triu(1)
+
+        def materialised():
+            s = torch.matmul(q32, k32t) * scale
+            s.masked_fill_(above, float("-inf"))
+            p = torch.softmax(s, dim=-1)
+            return torch.matmul(p, v32)
+
+        say(f"[case] peak memory S={S}")
+        materialised()   # the matrix library's workspace for this shape, kept by torch afterwards
+        naive.append(_peak_bytes(materialised))
+        fused.append(_peak_bytes(lambda: fa.fwd(qd, kd, vd, causal=True, scale=scale)))
+        outputs = 28 * S * 128 * 2 + 28 * S * 4
+        say(f"    naive {naive[-1] / 2**20:.1f} MiB, fused {fused[-1] / 2**20:.2f} MiB "
+            f"(O + lse = {outputs / 2**20:.2f} MiB)")
+        assert fused[-1] == outputs
+        del q32, k32t, v32, above, qd, kd, vd
+    for a, b in zip(naive, naive[1:]):
+        assert 3.5 <= b / a <= 4.05, naive
+    for a, b in zip(fused, fused[1:]):
+        assert b == 2 * a, fused
+
+
 def test_invalid_call_on_gpu_returns_status():
     q = torch.zeros(1, 1, 8, 96, dtype=torch.bfloat16, device=DEV)
     with pytest.raises(fa.FAError) as e:
