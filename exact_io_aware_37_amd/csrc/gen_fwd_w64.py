@@ -28,7 +28,11 @@ instruction and cannot express that split; here every register is assigned
 by hand, and the matrix instructions, LDS reads, DMA transfers and vector
 instructions of a tile are interleaved by the list scheduler below, which
 also inserts the wait states gfx950 needs between dependent instructions
-(the hardware does not check them for matrix results).
+(the hardware does not check them for matrix results).  With one wave per
+SIMD the wave's in-order issue is the bottleneck besides the matrix pipe:
+the scheduler fills each matrix instruction's shadow by measured issue
+costs and puts waits and LDS reads where they issue cheapest, right after
+a matrix instruction.
 
 Register map (per wave; one wave per SIMD, 512 registers):
   a[0:127]    O^T accumulators, block (h, db): a[16*(4h+db) : +16]
@@ -59,7 +63,6 @@ KSTAGE = BC * ROWB          # bytes of one K (or V) tile in LDS
 VRING = 4 * KSTAGE          # the V ring starts after the 4-stage K ring
 NSTAGE = 4
 MFMA_CYCLES = 32            # v_mfma_f32_32x32x16: 8 passes of 4 cycles
-SLOT_BUDGET = 28            # issue cycles for other instructions per matrix instruction
 
 # ----------------------------------------------------------------- registers
 
@@ -95,7 +98,6 @@ def p1(buf, h, kt, cc, w):
 
 KSLOTS = 6    # K fragment ring depth
 VLEAD = 12    # V reads may start this many matrix instructions before their use
-MAX_FIRST = False  # True: the row-maximum work of S(j+1) outranks the remaining exponentials of S(j)
 VSLOTS = 6    # V fragment ring depth
 
 
@@ -221,11 +223,16 @@ WS_WAR = 8
 
 
 class Stream:
-    def __init__(self, ins, start=0, name=""):
+    def __init__(self, ins, start=0, name="", deadline=None):
         self.ins = list(ins)
         self.pos = 0
         self.start = start      # earliest matrix-instruction index after which it may run
         self.name = name
+        self.deadline = deadline   # matrix-instruction index before which all of it has issued
+        self.pace = 0              # > 0: instruction i not before matrix index start + pace * (i // 2)
+
+    def ready_at(self, m):
+        return self.start + self.pace * (self.pos // 2) <= m if self.pace else self.start <= m
 
     def done(self):
         return self.pos >= len(self.ins)
@@ -341,29 +348,60 @@ class Block:
         return "\n".join(i.text for i in self.out)
 
 
-def schedule(block, mfmas, streams, lds_plan, budget=SLOT_BUDGET, inserts=()):
+# Issue costs of one wave's instruction stream (one wave per SIMD), measured on MI355X with
+# register-only loops of v_mfma_f32_32x32x16_bf16 followed by the instructions in question:
+# the wave issues in order, so the matrix pipe idles whenever the instructions between two
+# matrix instructions take longer to issue than the first one takes to run.
+ISSUE_MFMA = 8       # a matrix instruction; one scalar instruction right after it is free
+COST_VALU = 4
+COST_TRANS = 8       # v_exp_f32 and the other transcendentals
+COST_SALU = 4        # s_waitcnt, s_add, s_nop 0 anywhere but right after a matrix instruction
+COST_MEM = 7         # an LDS read or buffer load right after a matrix, scalar or memory instruction
+COST_MEM_LATE = 16   # ... right after a vector instruction
+DMA_PACE = 5         # the K/V transfers of a step: one piece per 5 matrix instructions at most
+VECTOR_KINDS = ("valu", "trans", "cmp", "perm", "accr", "accw")
+
+
+def issue_cost(ins, prev_kind, free_slot):
+    k = ins.kind
+    if k in ("salu", "wait"):
+        return 0 if free_slot else COST_SALU
+    if k in ("lds", "lds_dma", "vmem", "lds_w"):
+        return COST_MEM_LATE if prev_kind in VECTOR_KINDS else COST_MEM
+    if k == "trans":
+        return COST_TRANS
+    return COST_VALU
+
+
+def schedule(block, mfmas, streams, lds_plan, inserts=()):
     """Interleave `mfmas` (in order) with vector streams and LDS reads.
 
     lds_plan: list of (first consuming matrix index, matrix index from which
-    the ring slot is free, [Ins ...]), issued before the first matrix
-    instruction at or after the free index; `inserts`: (matrix index, [Ins])
-    emitted right before that matrix instruction.  After each matrix
-    instruction, ready stream instructions (streams in priority order, each
-    in program order) fill its shadow: the remaining stream work spread evenly
-    over the remaining matrix time, at most `budget` cycles per 32-cycle
-    instruction.  A matrix instruction whose operands a stream still has to
-    produce first pulls those producers in."""
+    the ring slot is free, [Ins ...]); `inserts`: (matrix index, [Ins])
+    emitted right before that matrix instruction.  Right after each matrix
+    instruction come, in this order: the s_waitcnt for the next matrix
+    instruction's LDS operands (in the scalar slot that costs nothing there),
+    the LDS reads that become due, and then ready stream instructions
+    (streams in priority order, each in program order) until the issue
+    cycles spent reach the matrix instruction's run time minus its own issue
+    cycles.  A matrix instruction whose operands a stream still has to
+    produce first pulls those producers in; a stream with a deadline is
+    flushed before the matrix instruction of that index."""
     li = 0
     plan = sorted(lds_plan, key=lambda x: (x[1], x[0]))
     at = {}
     for idx, ins in inserts:
         at.setdefault(idx, []).extend(ins)
-    mtime = [mi.cost for mi in mfmas]
     for m, mi in enumerate(mfmas):
         while li < len(plan) and plan[li][1] <= m:
             for ins in plan[li][2]:
                 block.put(ins)
             li += 1
+        for st in streams:
+            if st.deadline is not None and m >= st.deadline:
+                while not st.done():
+                    block.put(st.peek())
+                    st.pos += 1
         for ins in at.get(m, []):
             block.put(ins)
         need = set(mi.reads)
@@ -378,25 +416,37 @@ def schedule(block, mfmas, streams, lds_plan, budget=SLOT_BUDGET, inserts=()):
                 block.put(st.peek())
                 st.pos += 1
         block.put(mi)
-        # even spread: work still queued in streams that may run from here on,
-        # over the matrix time left (this instruction's included)
-        left = sum(ins.cost for st in streams if st.start <= m for ins in st.ins[st.pos:])
-        time_left = sum(mtime[m:])
-        room = min(budget * mi.cost / MFMA_CYCLES,
-                   max(8.0, left * mi.cost / max(time_left, 1)) + 4)
+        window = mi.cost - ISSUE_MFMA
         spent = 0
+        prev_kind, free_slot = "mfma", True
+        nxt = mfmas[m + 1] if m + 1 < len(mfmas) else None
+        if nxt is not None and (m + 1) not in at and block.lds_pending(nxt):
+            n0 = len(block.out)
+            block.waitcnt_for(nxt)
+            if len(block.out) > n0:
+                prev_kind, free_slot = "wait", False
+        while li < len(plan) and plan[li][1] <= m + 1 and (m + 1) not in at:
+            for ins in plan[li][2]:
+                spent += issue_cost(ins, prev_kind, free_slot)
+                block.put(ins)
+                prev_kind, free_slot = ins.kind, False
+            li += 1
         progress = True
-        while spent < room and progress:
+        while spent < window and progress:
             progress = False
             for st in streams:
-                if st.done() or st.start > m:
+                if st.done() or not st.ready_at(m):
                     continue
                 ins = st.peek()
                 if block.lds_pending(ins) or block.need(ins) > 0:
                     continue
+                c = issue_cost(ins, prev_kind, free_slot)
+                if spent + c > window and spent > 0:
+                    continue
                 block.put(ins)
                 st.pos += 1
-                spent += ins.cost
+                spent += c
+                prev_kind, free_slot = ins.kind, False
                 progress = True
                 break
     while li < len(plan):
@@ -456,27 +506,26 @@ def pv_mfmas_and_reads(dt, vstage, base_index, buf):
     """Matrix instructions of O += V^T P^T, then the row sums of P, and the V reads.
 
     Fragment g = 8*kt + 4*cc + db (two ds_read_b64_tr_b16 each) goes to ring
-    slot g % VSLOTS and feeds h = 0, 1."""
+    slot g % VSLOTS and feeds h = 0, 1, one after the other."""
     ms = []
-    reads = []
-    first = {}
-    last = {}
-    g = 0
+    uses = {}
     for kt in range(2):
         for cc in range(2):
-            for db in range(4):
-                off = vstage * KSTAGE + (kt * 32 + cc * 16) * ROWB
-                lo = Ins(f"ds_read_b64_tr_b16 {VFlo(g % VSLOTS)}, {{vaddr{db}}} offset:{off}", "lds",
-                         writes=regs(VFlo(g % VSLOTS)))
-                hi = Ins(f"ds_read_b64_tr_b16 {VFhi(g % VSLOTS)}, {{vaddr{db}}} offset:{off + 8 * ROWB}",
-                         "lds", writes=regs(VFhi(g % VSLOTS)))
-                first[g] = base_index + len(ms)
-                for h in range(2):
-                    ms.append(mfma(mfma_op(dt), O(h, db), VF(g % VSLOTS), P(buf, h, kt, cc), O(h, db)))
-                last[g] = base_index + len(ms)
-                free = last[g - VSLOTS] if g >= VSLOTS else 0
-                reads.append((first[g], free, [lo, hi]))
-                g += 1
+            for (h, db) in [(h, db) for db in range(4) for h in range(2)]:
+                g = 8 * kt + 4 * cc + db
+                uses.setdefault(g, []).append(base_index + len(ms))
+                ms.append(mfma(mfma_op(dt), O(h, db), VF(g % VSLOTS), P(buf, h, kt, cc), O(h, db)))
+    reads = []
+    for g in range(16):
+        kt, cc, db = g // 8, (g // 4) % 2, g % 4
+        off = vstage * KSTAGE + (kt * 32 + cc * 16) * ROWB
+        lo = Ins(f"ds_read_b64_tr_b16 {VFlo(g % VSLOTS)}, {{vaddr{db}}} offset:{off}", "lds",
+                 writes=regs(VFlo(g % VSLOTS)))
+        hi = Ins(f"ds_read_b64_tr_b16 {VFhi(g % VSLOTS)}, {{vaddr{db}}} offset:{off + 8 * ROWB}",
+                 "lds", writes=regs(VFhi(g % VSLOTS)))
+        free = max(uses[g - VSLOTS]) + 1 if g >= VSLOTS else 0
+        reads.append((min(uses[g]), free, [lo, hi]))
+    reads.sort(key=lambda r: r[0])
     # the row sums need P only: they run last, under the tile's barrier and transfers
     for kt in range(2):
         for cc in range(2):
@@ -485,21 +534,31 @@ def pv_mfmas_and_reads(dt, vstage, base_index, buf):
     return ms, reads
 
 
-def exp_stream(dt, buf, hk_order):
-    """P(buf) = exp2(s * sl2 - m), rounded to the input type and packed as the P*V operand."""
-    ins = []
-    for (h, kt) in hk_order:
+def exp_stream(dt, buf):
+    """P(buf) = exp2(s * sl2 - m), rounded to the input type and packed as the P*V operand.
+
+    Groups (h, kt, cc) in the order the P*V instructions consume them; within the
+    stream the conversion of a pair of scores comes after the FMAs of the next
+    pair, so that no instruction waits on the one issued right before it (a
+    conversion reads two exponentials)."""
+    units = []
+    for kt in range(2):
         for cc in range(2):
-            for w in range(4):
-                r0, r1 = cc * 8 + 2 * w, cc * 8 + 2 * w + 1
-                a, b = s1(buf, h, kt, r0), s1(buf, h, kt, r1)
-                ins.append(valu(f"v_fma_f32 {a}, {a}, {{sl2}}, -{MRUN[h]}", [a, MRUN[h]], [a]))
-                ins.append(valu(f"v_fma_f32 {b}, {b}, {{sl2}}, -{MRUN[h]}", [b, MRUN[h]], [b]))
-                ins.append(valu(f"v_exp_f32 {a}, {a}", [a], [a], kind="trans", cost=8))
-                ins.append(valu(f"v_exp_f32 {b}, {b}", [b], [b], kind="trans", cost=8))
-                p = p1(buf, h, kt, cc, w)     # in place: the scores it overwrites are consumed
-                ins.append(valu(f"{cvt_op(dt)} {p}, {a}, {b}", [a, b], [p]))
-    return ins
+            for h in range(2):
+                for w in range(4):
+                    a, b = s1(buf, h, kt, cc * 8 + 2 * w), s1(buf, h, kt, cc * 8 + 2 * w + 1)
+                    f = [valu(f"v_fma_f32 {a}, {a}, {{sl2}}, -{MRUN[h]}", [a, MRUN[h]], [a]),
+                         valu(f"v_fma_f32 {b}, {b}, {{sl2}}, -{MRUN[h]}", [b, MRUN[h]], [b])]
+                    e = [valu(f"v_exp_f32 {a}, {a}", [a], [a], kind="trans", cost=8),
+                         valu(f"v_exp_f32 {b}, {b}", [b], [b], kind="trans", cost=8)]
+                    # packed in place over scores of the same group that earlier
+                    # conversions (or this one) have consumed
+                    p = p1(buf, h, kt, cc, w)
+                    units.append((f, e, [valu(f"{cvt_op(dt)} {p}, {a}, {b}", [a, b], [p])]))
+    ins = units[0][0] + units[0][1]
+    for k in range(1, len(units)):
+        ins += units[k][0] + units[k - 1][2] + units[k][1]
+    return ins + units[-1][2]
 
 
 def sum_mfma(dt, buf, h, kt, cc):
@@ -649,14 +708,16 @@ def tile_step(dt, j_parity, masked, causal, uid):
     sync_at = rd_pv[-1][0]
     sync = [Ins("s_waitcnt vmcnt(8) lgkmcnt(0)", "wait"), Ins("s_barrier", "barrier")]
     nextk = [k_read(f, (j_parity + 2) % 4) for f in range(KSLOTS)]
+    # priority order: the next tile's first K reads, the K/V transfers (paced, all issued
+    # before the sync), the exponentials, the running sum, the row maximum of S(j+1)
+    dma = Stream(dma_issue((j_parity + 3) % 4), 2, "dma", deadline=sync_at)
+    dma.pace = DMA_PACE
     streams = [
         Stream(nextk, sync_at, "nextk"),
-        Stream(dma_issue((j_parity + 3) % 4), 2, "dma"),
+        dma,
+        Stream(exp_stream(dt, cur), 0, "exp"),
         Stream(fold_stream(), 8, "fold"),
     ]
-    exps = Stream(exp_stream(dt, cur, [(0, 0), (1, 0), (0, 1), (1, 1)]), 0, "exp")
-    if not MAX_FIRST:
-        streams.append(exps)
     tail = []
     if masked:
         tail += [raw(f"s_add_u32 {S_KV0}, {S_KV0}, {BC}")]
@@ -666,8 +727,6 @@ def tile_step(dt, j_parity, masked, causal, uid):
     tail.append(valu(f"v_cmp_neq_f32 vcc, 1.0, {ALPHA[0]}", [ALPHA[0]], ["vcc"], kind="cmp"))
     tail.append(valu(f"v_cmp_neq_f32 {S_ANY}, 1.0, {ALPHA[1]}", [ALPHA[1]], [S_ANY], kind="cmp"))
     streams.append(Stream(tail, len(ms_s), "max"))
-    if MAX_FIRST:
-        streams.append(exps)
     schedule(b, ms_s + ms_pv, streams, lds_plan, inserts=[(sync_at, sync)])
     if not masked:
         b.put(raw(f"s_add_u32 {S_KV0}, {S_KV0}, {BC}"))
@@ -752,7 +811,7 @@ def drain(dt, parity):
     cur = parity % 2
     ms_pv, rd_pv = pv_mfmas_and_reads(dt, parity % 4, 0, cur)
     schedule(b, ms_pv, [Stream(fold_stream(), 0, "fold"),
-                        Stream(exp_stream(dt, cur, [(0, 0), (1, 0), (0, 1), (1, 1)]), 0, "exp")],
+                        Stream(exp_stream(dt, cur), 0, "exp")],
              rd_pv)
     b.put(Ins("s_branch .Lepi", "branch"))
     return b
