@@ -147,9 +147,9 @@ S_TMP = "s76"
 S_M0 = "s77"         # saved M0
 S_H8K = "s78"        # 8192 (row offset of the second query half)
 S_T2 = "s79"         # tile index mod 4
-MASKS = ["s[80:81]", "s[82:83]", "s[84:85]"]
-S_ANY = "s[86:87]"
-SGPR_CLOBBERS = [f"s{i}" for i in range(72, 88)]
+MASKS = ["s[80:81]", "s[82:83]", "s[84:85]", "s[86:87]", "s[88:89]"]
+S_ANY = "s[90:91]"
+SGPR_CLOBBERS = [f"s{i}" for i in range(72, 92)]
 
 # ---------------------------------------------------------------- instructions
 
@@ -576,18 +576,29 @@ def sum_mfma(dt, buf, h, kt, cc):
     return mfma(op, LACC[h], SEL, P(buf, h, kt, cc), c, cycles=16)
 
 
-def mask_stream(buf, h):
-    """Scores of keys past the row's limit (tail, causal) -> -inf, for half h."""
-    ins = [valu(f"v_sub_u32_e64 {LIMR[h]}, {LIMH[h]}, {S_KV0}", [LIMH[h]], [LIMR[h]])]
-    k = 0
-    for kt in range(2):
-        for r in range(16):
-            off = kt * 32 + (r >> 2) * 8 + (r & 3)
-            m = MASKS[k % 3]
-            ins.append(valu(f"v_cmp_gt_i32 {m}, {off}, {LIMR[h]}", [LIMR[h]], [m], kind="cmp"))
-            a = s1(buf, h, kt, r)
-            ins.append(valu(f"v_cndmask_b32 {a}, {a}, {NEGINF}, {m}", [a, NEGINF, m], [a]))
-            k += 1
+def mask_stream(buf):
+    """Scores of keys past the row's limit (tail, causal) -> -inf, both halves.
+
+    One compare into a mask pair and one select per score; the compares run
+    len(MASKS) - 1 ahead of their selects (rotating over the mask pairs), so
+    that no select waits for the mask its compare wrote."""
+    ins = [valu(f"v_sub_u32_e64 {LIMR[h]}, {LIMH[h]}, {S_KV0}", [LIMH[h]], [LIMR[h]]) for h in range(2)]
+    pairs = []
+    for h in range(2):
+        for kt in range(2):
+            for r in range(16):
+                k = len(pairs)
+                off = kt * 32 + (r >> 2) * 8 + (r & 3)
+                m = MASKS[k % len(MASKS)]
+                a = s1(buf, h, kt, r)
+                pairs.append((valu(f"v_cmp_gt_i32 {m}, {off}, {LIMR[h]}", [LIMR[h]], [m], kind="cmp"),
+                              valu(f"v_cndmask_b32 {a}, {a}, {NEGINF}, {m}", [a, NEGINF, m], [a])))
+    lead = len(MASKS)
+    for k in range(len(pairs) + lead):
+        if k >= lead:
+            ins.append(pairs[k - lead][1])
+        if k < len(pairs):
+            ins.append(pairs[k][0])
     return ins
 
 
@@ -721,7 +732,7 @@ def tile_step(dt, j_parity, masked, causal, uid):
     tail = []
     if masked:
         tail += [raw(f"s_add_u32 {S_KV0}, {S_KV0}, {BC}")]
-        tail += mask_stream(nxt, 0) + mask_stream(nxt, 1)
+        tail += mask_stream(nxt)
     tail += max_stream(nxt, 0) + max_stream(nxt, 1)
     # does any lane's reference move (O must then be rescaled before the next P*V)?
     tail.append(valu(f"v_cmp_neq_f32 vcc, 1.0, {ALPHA[0]}", [ALPHA[0]], ["vcc"], kind="cmp"))
@@ -793,7 +804,7 @@ def first_tile(dt, masked_first):
     ms, rd = s_mfmas_and_reads(dt, 0, 0)
     tail = []
     if masked_first:
-        tail += mask_stream(0, 0) + mask_stream(0, 1)
+        tail += mask_stream(0)
     tail += max_stream(0, 0, first=True) + max_stream(0, 1, first=True)
     schedule(b, ms, [Stream(tail, len(ms), "max")], rd)
     # tile 1 visible to every wave, then the first K reads of S(1)
