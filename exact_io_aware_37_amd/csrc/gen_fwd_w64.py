@@ -373,6 +373,33 @@ def issue_cost(ins, prev_kind, free_slot):
     return COST_VALU
 
 
+def issue_time(instructions):
+    """Modelled cycles of a straight-line instruction list under the issue costs above:
+    in-order issue, one matrix instruction at a time in the matrix pipe (its `cost`
+    cycles); waits on memory and barriers are not modelled.  Returns (cycles, busy)."""
+    t = mfree = busy = 0.0
+    prev_kind, free_slot = "mfma", False
+    for ins in instructions:
+        k = ins.kind
+        if k == "mfma":
+            start = max(t, mfree)
+            mfree = start + ins.cost
+            busy += ins.cost
+            t = start + ISSUE_MFMA
+            prev_kind, free_slot = k, True
+            continue
+        if k == "nop":
+            t += COST_SALU * (int(ins.text.split()[1]) + 1) - (COST_SALU if free_slot else 0)
+        elif k in ("barrier", "label"):
+            continue
+        elif k == "branch":
+            t += 0 if free_slot else COST_SALU
+        else:
+            t += issue_cost(ins, prev_kind, free_slot)
+        prev_kind, free_slot = k, False
+    return max(t, mfree), busy
+
+
 def schedule(block, mfmas, streams, lds_plan, inserts=()):
     """Interleave `mfmas` (in order) with vector streams and LDS reads.
 
