@@ -152,6 +152,31 @@ def test_odd_shapes(shape):
     compare("odd", q, k, v, causal, workloads.default_scale(D), dtype)
 
 
+def _random_shapes(n, seed):
+    """Seeded shapes for the 16-bit paths: 1-2 batches, GQA groups of 1-7 heads,
+    query and key lengths drawn across 1-1200 (ragged tiles, N_q != N_kv, fewer
+    rows than a wave or than a workgroup), d in {64, 128}, causal or not."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        hkv = int(rng.integers(1, 3))
+        group = int(rng.choice([1, 2, 4, 7]))
+        nq = int(rng.integers(1, 1200))
+        nkv = int(rng.integers(1, 1200))
+        out.append((int(rng.integers(1, 3)), hkv * group, hkv, nq, nkv, int(rng.choice([64, 128])),
+                    str(rng.choice(["bf16", "f16"])), bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("shape", _random_shapes(24, 2026), ids=lambda s: "x".join(map(str, s)))
+def test_random_shapes(shape):
+    """Every element against the oracle for seeded random shapes (the seeded draw is the
+    shape list itself, fixed by the seed)."""
+    B, Hq, Hkv, Nq, Nkv, D, dtype, causal = shape
+    q, k, v = case_inputs(B, Hq, Hkv, Nq, Nkv, D, dtype, seed=Nq * 7 + Nkv)
+    compare("random", q, k, v, causal, workloads.default_scale(D), dtype)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("scale", [0.0, -0.09, 0.5])
 def test_scale_values(dtype, scale):

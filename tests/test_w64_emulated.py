@@ -166,6 +166,8 @@ CASES = [
     ("bf16", True, 256, 256, 0),       # causal first tile: masked prologue
     ("f16", False, 256, 330, 0),
     ("f16", True, 300, 300, 256),
+    ("bf16", True, 512, 700, 256),     # causal, more keys than query rows
+    ("f16", False, 40, 1000, 0),       # 16 tiles, rows only in part of one wave
 ]
 
 
