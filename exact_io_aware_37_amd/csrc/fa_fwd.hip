@@ -114,25 +114,15 @@ __device__ __forceinline__ int xcd_local(int bid, int nb) {
 
 // ----------------------------------------------- 16-bit (bf16 / f16) path
 //
-// This 32-row-per-wave kernel serves head dimension 64; at 128 the forward
-// runs the 64-row-per-wave kernel further below (attn_fwd_w64).  The split-KV
-// and paged kernels reuse the layouts and helpers of this section at both
-// head dimensions.
-//
-// Workgroup: 8 waves x 32 query rows = 256 rows.  K/V tiles of 64 keys move
-// global -> LDS by buffer DMA (buffer_load ... lds, 16 B per lane, no VGPR
-// staging; rows past N_kv come back as zeros) into a 4-stage ring, issued two
-// tiles ahead.  K is stored row-major with an XOR swizzle of its 16-byte
-// chunks (conflict-free 16-byte operand reads); V is stored row-major too,
-// with its own swizzle, and read transposed by ds_read_b64_tr_b16, which
-// hands each lane four keys of one head-dimension column: the V^T operand of
-// the P*V product without any transpose pass.
-//
-// Main loop (tiles that need no mask), software-pipelined per wave:
-//   phase A: MFMA S(j+1) = K(j+1) Q^T   ||  VALU exp(S(j)) -> P(j), row sums
-//   phase B: MFMA O += V(j) P(j)        ||  VALU row max of S(j+1), new reference
-// Diagonal (causal) and ragged-tail tiles run afterwards through a plain,
-// masked, non-pipelined step.
+// Helpers and layouts shared by the 16-bit kernels: the forward (attn_fwd_w64,
+// 64 query rows per wave, at d = 64 and 128), split-KV, paged and backward.
+// K/V tiles move global -> LDS by buffer DMA (buffer_load ... lds, 16 B per
+// lane, no VGPR staging; rows past N_kv come back as zeros).  K is stored
+// row-major with an XOR swizzle of its 16-byte chunks (conflict-free 16-byte
+// operand reads); V is stored row-major too, with its own swizzle, and read
+// transposed by ds_read_b64_tr_b16, which hands each lane four keys of one
+// head-dimension column: the V^T operand of the P*V product without any
+// transpose pass.
 //
 // The exponent reference is lazy: it moves to the new running max only when
 // that max exceeds it by more than 2^8 (then O and the sum are rescaled by
@@ -220,27 +210,6 @@ struct Mma16<_Float16> {
   }
 };
 
-template <int D>
-struct Cfg16 {
-  static constexpr int QH = 1;                  // 32-row query halves per wave
-  static constexpr int NW = 8;                  // waves per workgroup
-  static constexpr int NT = 64 * NW;            // threads per workgroup
-  static constexpr int BR = 32 * QH * NW;       // query rows per workgroup
-  static constexpr int BC = 64;                 // keys per K/V tile
-  static constexpr int KT = BC / 32;            // 32-key blocks per tile
-  static constexpr int WAVES_PER_EU = QH == 1 ? 2 : 1;
-  static constexpr int STAGES = 4;              // LDS ring depth (tiles)
-  static constexpr int ROWB = D * 2;            // bytes per K/V row
-  static constexpr int NCH = D / 8;             // 16-byte chunks per row
-  static constexpr int TILEB = BC * ROWB;       // bytes of one K (or V) tile
-  static constexpr int STAGEB = 2 * TILEB;      // K tile then V tile
-  static constexpr int LDS_BYTES = STAGES * STAGEB;
-  static constexpr int CHUNKS = STAGEB / 1024;  // 1 KiB DMA instructions per tile
-  static constexpr int DPW = CHUNKS / NW;       // ... per wave
-  static_assert(DPW * NW == CHUNKS && DPW >= 1, "DMA split");
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-};
-
 // XOR swizzles of the 16-byte chunk index within a row (period 16 rows).
 // K: 16 consecutive rows read the same logical chunk -> 16 distinct chunks.
 // V: a transposed read touches 4 consecutive rows x 4 chunks -> 16 distinct.
@@ -251,372 +220,11 @@ __device__ __forceinline__ int swz_v(int row) {
   return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
 }
 
-// Body of the 16-bit kernel.  It lives in a device function because the
-// host compilation pass does not emit launch stubs for kernel templates whose
-// own body holds template lambdas.
-template <typename T, int D, bool CAUSAL>
-__device__ __forceinline__ void attn_fwd_mfma16_body(const Params& p) {
-  using C = Cfg16<D>;
-  constexpr int KT = C::KT;
-  constexpr int QH = C::QH;
-  using M = Mma16<T>;
-  // One LDS object per ring stage and operand: with compile-time stage
-  // indices the compiler can tell a read of one stage from a DMA into another
-  // and does not stall the read on the unrelated transfer; the K ring fills
-  // the first 64 KiB so every K stage offset fits a ds_read immediate.
-  __shared__ __attribute__((aligned(1024))) unsigned char k0[C::TILEB];
-  __shared__ __attribute__((aligned(1024))) unsigned char k1[C::TILEB];
-  __shared__ __attribute__((aligned(1024))) unsigned char k2[C::TILEB];
-  __shared__ __attribute__((aligned(1024))) unsigned char k3[C::TILEB];
-  __shared__ __attribute__((aligned(1024))) unsigned char v0[C::TILEB];
-  __shared__ __attribute__((aligned(1024))) unsigned char v1[C::TILEB];
-  __shared__ __attribute__((aligned(1024))) unsigned char v2[C::TILEB];
-  __shared__ __attribute__((aligned(1024))) unsigned char v3[C::TILEB];
-  auto kst = [&]<int S>() -> lds_t* {
-    if constexpr ((S & 3) == 0) return (lds_t*)k0;
-    else if constexpr ((S & 3) == 1) return (lds_t*)k1;
-    else if constexpr ((S & 3) == 2) return (lds_t*)k2;
-    else return (lds_t*)k3;
-  };
-  auto vst = [&]<int S>() -> lds_t* {
-    if constexpr ((S & 3) == 0) return (lds_t*)v0;
-    else if constexpr ((S & 3) == 1) return (lds_t*)v1;
-    else if constexpr ((S & 3) == 2) return (lds_t*)v2;
-    else return (lds_t*)v3;
-  };
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
-  const int half = lane >> 5;
-  const int l32 = lane & 31;
-
-  int b, hq, qt;
-  map_block(p, CAUSAL, b, hq, qt);
-  const int hkv = hq / p.group;
-  const int q0 = qt * C::BR;
-  const int qw0 = q0 + wave * 32 * QH;   // first query row of this wave
-  // Query half h of the wave holds rows qw0 + 32h .. +31; lane l32 of it
-  // holds row qw0 + 32h + l32 (its O column and its row statistics).
-
-  const size_t qhead = (size_t)(b * p.Hq + hq) * p.Nq;
-  const size_t kvhead = (size_t)(b * p.Hkv + hkv) * p.Nkv;
-  const rsrc_t rq = make_rsrc(static_cast<const uint16_t*>(p.q) + qhead * D, (uint32_t)p.Nq * C::ROWB);
-  const rsrc_t rk = make_rsrc(static_cast<const uint16_t*>(p.k) + kvhead * D, (uint32_t)p.Nkv * C::ROWB);
-  const rsrc_t rv = make_rsrc(static_cast<const uint16_t*>(p.v) + kvhead * D, (uint32_t)p.Nkv * C::ROWB);
-
-  const int kv_end = CAUSAL ? min(p.Nkv, q0 + C::BR) : p.Nkv;
-  const int n_tiles = (kv_end + C::BC - 1) / C::BC;
-  // Tiles whose every key is allowed for every row of the workgroup.
-  const int n_main = CAUSAL ? min((q0 + 1) / C::BC, p.Nkv / C::BC) : p.Nkv / C::BC;
-
-  // DMA of tile t into ring stage S (= t mod 4).
-  auto issue = [&]<int S>(int t) {
-    const int kv0 = t * C::BC;
-#pragma unroll
-    for (int u = 0; u < C::DPW; ++u) {
-      const int i = wave * C::DPW + u;            // 1 KiB chunk of the stage (wave-uniform)
-      const bool isv = i >= C::CHUNKS / 2;
-      const int ci = isv ? i - C::CHUNKS / 2 : i;
-      const int slot = ci * 64 + lane;            // 16-byte slot within the tile
-      const int row = slot / C::NCH;
-      const int c = (slot % C::NCH) ^ (isv ? swz_v<D>(row) : swz_k<D>(row));
-      lds_t* dst = (isv ? vst.template operator()<S>() : kst.template operator()<S>()) + ci * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? rv : rk, (lds_t*)dst, 16,
-                                               (kv0 + row) * C::ROWB + c * 16, 0, 0, 0);
-    }
-  };
-
-  // Tile t has landed in LDS for every wave; tile t+2 (ring stage S) is issued.
-  auto advance = [&]<int S>(int t) {
-    if (t + 1 < n_tiles) wait_vm_lgkm<C::DPW>();
-    else wait_vm_lgkm<0>();
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (t + 2 < n_tiles) issue.template operator()<S>(t + 2);
-  };
-
-  issue.template operator()<0>(0);
-  if (n_tiles > 1) issue.template operator()<1>(1);
-
-  // Q^T operand, held for the whole loop: lane (l32, half) has row myq, dims
-  // cd*16 + half*8 .. +7.  Rows past N_q read as zeros.  qmode 1 flips both
-  // halves' sign bits (exact negation), qmode 2 zeroes Q.
-  const uint32_t qxor = p.qmode == 1 ? 0x80008000u : 0u;
-  const uint32_t qand = p.qmode == 2 ? 0u : 0xffffffffu;
-  u32x4 qreg[QH][D / 16];
-#pragma unroll
-  for (int h = 0; h < QH; ++h) {
-#pragma unroll
-    for (int cd = 0; cd < D / 16; ++cd) {
-      const int row = qw0 + 32 * h + l32;
-      const u32x4 x = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, (row * D + cd * 16 + half * 8) * 2, 0, 0));
-      qreg[h][cd] = (x ^ qxor) & qand;
-    }
-  }
-
-  // Per-lane LDS byte offsets of the operand reads.  The swizzles have a
-  // period of 16 rows and act on chunk-index bits that a loop index only
-  // XORs, so one base per operand suffices:
-  //   K, dims cd*16.. of row l32 (+32 kt):   kbase ^ (cd * 32)   (+ kt * 32 rows)
-  //   V^T, columns db*32.., keys as above:   vbase ^ (db * 64)   (+ row offsets)
-  const int kbase = l32 * C::ROWB + ((half ^ (swz_k<D>(l32) & 1)) * 16) + ((swz_k<D>(l32) >> 1) * 32);
-  const int g16 = lane >> 4, s16 = lane & 15;
-  const int vrow = (g16 >> 1) * 4 + (s16 >> 2);
-  const int vbase = vrow * C::ROWB + (swz_v<D>(vrow) >> 2) * 64 + (g16 & 1) * 32 +
-                    ((s16 & 3) >> 1) * 16 + (s16 & 1) * 8;
-
-  f32x16 acc[QH][D / 32];
-#pragma unroll
-  for (int h = 0; h < QH; ++h)
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) acc[h][i] = f32x16{};
-  float m_run[QH];   // exponent reference (log2 units), shared by both half-waves
-  float l_run[QH];   // this lane's part of the row sum, against m_run
-#pragma unroll
-  for (int h = 0; h < QH; ++h) {
-    m_run[h] = -INFINITY;
-    l_run[h] = 0.f;
-  }
-
-  // The lane bases pass through an empty asm in every call so that the
-  // compiler recomputes the few XORs per tile instead of hoisting one address
-  // register per (stage, chunk) pair out of the loop.
-  auto compute_s = [&](const lds_t* st, f32x16 (&s)[QH][KT]) {
-    int kb = kbase;
-    asm volatile("" : "+v"(kb));
-#pragma unroll
-    for (int h = 0; h < QH; ++h)
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) s[h][kt] = f32x16{};
-#pragma unroll
-    for (int cd = 0; cd < D / 16; ++cd) {
-      const lds_t* a = st + (kb ^ (cd * 32));
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        const u32x4 x = *(const u32x4 __attribute__((address_space(3)))*)(a + kt * 32 * C::ROWB);
-#pragma unroll
-        for (int h = 0; h < QH; ++h) s[h][kt] = M::mma(x, qreg[h][cd], s[h][kt]);
-      }
-    }
-  };
-
-  auto compute_pv = [&](const lds_t* st, const u32x4 (&pk)[QH][KT][2]) {
-    int vb = vbase;
-    asm volatile("" : "+v"(vb));
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const lds_t* a0 = st + (vb ^ (db * 64)) + (kt * 32 + cc * 16) * C::ROWB;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)a0);
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(a0 + 8 * C::ROWB));
-          const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-          const u32x4 x = {l2[0], l2[1], h2[0], h2[1]};
-#pragma unroll
-          for (int h = 0; h < QH; ++h) acc[h][db] = M::mma(x, pk[h][kt][cc], acc[h][db]);
-        }
-      }
-    }
-  };
-
-  // New exponent reference of query half h from a tile of raw scores;
-  // returns the factor that moves earlier sums to it (1 when the reference
-  // stays, 0 the first time).
-  auto new_reference = [&](const f32x16 (&s)[KT], int h) -> float {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-    mx = pair_max(mx);
-    const float mc = mx * p.sl2;
-    const float m_new = (mc > m_run[h] + kLazy) ? mc : m_run[h];
-    const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run[h] - m_new);
-    m_run[h] = m_new;
-    return alpha;
-  };
-
-  auto rescale = [&](const float (&alpha)[QH]) {
-    bool any = false;
-#pragma unroll
-    for (int h = 0; h < QH; ++h) {
-      l_run[h] *= alpha[h];
-      any = any || (alpha[h] != 1.f);
-    }
-    if (wave_any(any)) {
-#pragma unroll
-      for (int h = 0; h < QH; ++h)
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i) acc[h][i] *= alpha[h];
-    }
-  };
-
-  // P = exp2(s * sl2 - ref), rounded to T and packed as the B operand of P*V;
-  // the row sum accumulates the rounded values in fp32.
-  auto exponentiate = [&](const f32x16 (&s)[KT], u32x4 (&pk)[KT][2], int h) {
-    const float mu = (m_run[h] == -INFINITY) ? 0.f : m_run[h];
-    float ls0 = 0.f, ls1 = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float e0 = fast_exp2(fmaf(s[kt][cc * 8 + 2 * w], p.sl2, -mu));
-          const float e1 = fast_exp2(fmaf(s[kt][cc * 8 + 2 * w + 1], p.sl2, -mu));
-          const uint32_t pr = M::pack(e0, e1);
-          pk[kt][cc][w] = pr;
-          if (w & 1) ls1 = M::sum2(pr, ls1);
-          else ls0 = M::sum2(pr, ls0);
-        }
-      }
-    }
-    l_run[h] += ls0 + ls1;
-  };
-
-  f32x16 s_cur[QH][KT];
-  u32x4 pk[QH][KT][2];
-
-  // Steady iteration j (j % 4 == R): tile j+1 is unmasked too.
-  auto steady = [&]<int R>(int j) {
-    advance.template operator()<(R + 3) & 3>(j + 1);
-    f32x16 s_next[QH][KT];
-#pragma unroll
-    for (int h = 0; h < QH; ++h) exponentiate(s_cur[h], pk[h], h);   // VALU on S(j) ...
-    compute_s(kst.template operator()<(R + 1) & 3>(), s_next);       // ... under MFMA S(j+1)
-    compute_pv(vst.template operator()<R>(), pk);                    // MFMA O += V(j) P(j) ...
-    float alpha[QH];
-#pragma unroll
-    for (int h = 0; h < QH; ++h) alpha[h] = new_reference(s_next[h], h);   // ... under the scan of S(j+1)
-    rescale(alpha);
-#pragma unroll
-    for (int h = 0; h < QH; ++h)
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) s_cur[h][kt] = s_next[h][kt];
-  };
-  // Last unmasked iteration j = n_main - 1 (j % 4 == R).
-  auto last_main = [&]<int R>(int j) {
-    if (j + 1 < n_tiles) advance.template operator()<(R + 3) & 3>(j + 1);
-#pragma unroll
-    for (int h = 0; h < QH; ++h) exponentiate(s_cur[h], pk[h], h);
-    compute_pv(vst.template operator()<R>(), pk);
-  };
-  // A tile that needs a mask (ragged tail; causal diagonal), t % 4 == R.
-  // Rows with no allowed key in it get p = 0 exactly.
-  auto masked = [&]<int R>(int t) {
-    if (t > n_main || n_main == 0) advance.template operator()<(R + 2) & 3>(t);
-    const int kv0 = t * C::BC;
-    const bool active = (qw0 < p.Nq) && (!CAUSAL || kv0 <= qw0 + 32 * QH - 1);
-    if (active) {
-      f32x16 s[QH][KT];
-      compute_s(kst.template operator()<R>(), s);
-      float alpha[QH];
-#pragma unroll
-      for (int h = 0; h < QH; ++h) {
-        const int myq = qw0 + 32 * h + l32;
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + kt * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-            if ((key >= p.Nkv) || (CAUSAL && key > myq)) s[h][kt][r] = -INFINITY;
-          }
-        }
-        alpha[h] = new_reference(s[h], h);
-      }
-      rescale(alpha);
-#pragma unroll
-      for (int h = 0; h < QH; ++h) exponentiate(s[h], pk[h], h);
-      compute_pv(vst.template operator()<R>(), pk);
-    }
-  };
-
-  if (n_main > 0) {
-    advance.template operator()<2>(0);
-    compute_s(kst.template operator()<0>(), s_cur);
-    float alpha[QH];
-#pragma unroll
-    for (int h = 0; h < QH; ++h) alpha[h] = new_reference(s_cur[h], h);
-    rescale(alpha);
-    int j = 0;
-    for (; j + 4 < n_main; j += 4) {
-      steady.template operator()<0>(j);
-      steady.template operator()<1>(j + 1);
-      steady.template operator()<2>(j + 2);
-      steady.template operator()<3>(j + 3);
-    }
-    for (; j + 1 < n_main; ++j) {
-      switch (j & 3) {
-        case 0: steady.template operator()<0>(j); break;
-        case 1: steady.template operator()<1>(j); break;
-        case 2: steady.template operator()<2>(j); break;
-        default: steady.template operator()<3>(j); break;
-      }
-    }
-    switch (j & 3) {
-      case 0: last_main.template operator()<0>(j); break;
-      case 1: last_main.template operator()<1>(j); break;
-      case 2: last_main.template operator()<2>(j); break;
-      default: last_main.template operator()<3>(j); break;
-    }
-  }
-  for (int t = n_main; t < n_tiles; ++t) {
-    switch (t & 3) {
-      case 0: masked.template operator()<0>(t); break;
-      case 1: masked.template operator()<1>(t); break;
-      case 2: masked.template operator()<2>(t); break;
-      default: masked.template operator()<3>(t); break;
-    }
-  }
-
-  // Epilogue: combine the half-waves' sums, divide once, write O and lse.
-  // Rows past N_q fall outside the buffer ranges and are dropped.
-  const rsrc_t ro = make_rsrc(static_cast<uint16_t*>(p.o) + qhead * D, (uint32_t)p.Nq * C::ROWB);
-  const rsrc_t rl = make_rsrc(p.lse + qhead, (uint32_t)p.Nq * 4u);
-#pragma unroll
-  for (int h = 0; h < QH; ++h) {
-    const int myq = qw0 + 32 * h + l32;
-    const float l_tot = pair_sum(l_run[h]);
-    const float inv = 1.f / l_tot;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 w;
-        w[0] = M::pack(acc[h][db][4 * g] * inv, acc[h][db][4 * g + 1] * inv);
-        w[1] = M::pack(acc[h][db][4 * g + 2] * inv, acc[h][db][4 * g + 3] * inv);
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, w), ro,
-                                              (myq * D + db * 32 + g * 8 + half * 4) * 2, 0, 0);
-      }
-    }
-    if (half == 0)
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((m_run[h] + fast_log2(l_tot)) * kLn2), rl,
-                                            myq * 4, 0, 0);
-  }
-}
-
-template <int D>
-constexpr int kNT16 = Cfg16<D>::NT;
-template <int D>
-constexpr int kWavesPerEU16 = Cfg16<D>::WAVES_PER_EU;
-
-template <typename T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(kNT16<D>)
-    __attribute__((amdgpu_waves_per_eu(kWavesPerEU16<D>, kWavesPerEU16<D>)))
-attn_fwd_mfma16(Params p) {
-  attn_fwd_mfma16_body<T, D, CAUSAL>(p);
-}
-
-// ------------------------------------ 64 rows per wave (bf16 / f16, d = 128)
+// ------------------------------- 64 rows per wave (bf16 / f16, d = 64 and 128)
 //
-// The same computation as attn_fwd_mfma16 with each wave owning 64 query
-// rows instead of 32, one wave per SIMD (4 waves, 256 rows per workgroup):
-// every K and V fragment read from LDS feeds two matrix instructions, half
-// the LDS traffic per FLOP.  O and Q live in accumulation registers, scores
+// The forward of the 16-bit inputs: each wave owns 64 query rows, one wave
+// per SIMD (4 waves, 256 rows per workgroup), and every K and V fragment read
+// from LDS feeds two matrix instructions (one per 32-row half).  O and Q live in accumulation registers, scores
 // and probabilities in vector registers; that split, the register
 // assignment and the instruction schedule are written out by
 // gen_fwd_w64.py, whose header describes them, into fa_fwd_w64.inc, and the
@@ -639,16 +247,24 @@ __device__ __forceinline__ u32x4s raw_desc(const void* base, uint32_t bytes) {
 }
 
 // Launch shape: 4 waves of 64 rows, 64-key tiles, a 4-stage ring of one K
-// and one V tile (16 KiB each) per stage.
+// and one V tile (64 * 2d bytes each) per stage.
+template <int D>
 struct CfgW64 {
-  static constexpr int BR = 256, BC = 64, NT = 256, LDS_BYTES = 8 * 16384;
+  static constexpr int BR = 256, BC = 64, NT = 256;
+  static constexpr int ROWB = 2 * D;                // bytes per Q, K, V or O row
+  static constexpr int KSTAGE = BC * ROWB;          // one K (or V) tile
+  static constexpr int VRING = 4 * KSTAGE;          // the V ring follows the 4 K stages
+  static constexpr int LDS_BYTES = 8 * KSTAGE;
+  static constexpr int NPIECE = KSTAGE / 2048;      // 1 KiB DMA pieces per wave and stage
+  static constexpr int NCH = ROWB / 16;             // 16-byte chunks per row
 };
+
 
 // One work item (batch b, query head hq, 256-row query tile qt): operands of
 // the generated body, then the body itself.
-template <typename T, bool CAUSAL>
+template <typename T, bool CAUSAL, int D>
 __device__ __forceinline__ void w64_item(const Params& p, uint32_t lds0, int b, int hq, int qt) {
-  constexpr int D = 128;
+  using C = CfgW64<D>;
   // The lane index through an opaque copy: the per-lane operands below are
   // then computed afresh for each item instead of being hoisted out of the
   // persistent loop, where they could only survive the body (which uses
@@ -659,61 +275,62 @@ __device__ __forceinline__ void w64_item(const Params& p, uint32_t lds0, int b, 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, half = lane >> 5;
   const int hkv = hq / p.group;
-  const int q0 = qt * CfgW64::BR;
+  const int q0 = qt * C::BR;
   const int q0w = q0 + 64 * wave;
   const size_t qhead = (size_t)(b * p.Hq + hq) * p.Nq;
   const size_t kvhead = (size_t)(b * p.Hkv + hkv) * p.Nkv;
-  const u32x4s rq = raw_desc(static_cast<const uint16_t*>(p.q) + qhead * D, (uint32_t)p.Nq * 256u);
-  const u32x4s rk = raw_desc(static_cast<const uint16_t*>(p.k) + kvhead * D, (uint32_t)p.Nkv * 256u);
-  const u32x4s rv = raw_desc(static_cast<const uint16_t*>(p.v) + kvhead * D, (uint32_t)p.Nkv * 256u);
-  const u32x4s ro = raw_desc(static_cast<uint16_t*>(p.o) + qhead * D, (uint32_t)p.Nq * 256u);
+  const u32x4s rq = raw_desc(static_cast<const uint16_t*>(p.q) + qhead * D, (uint32_t)p.Nq * C::ROWB);
+  const u32x4s rk = raw_desc(static_cast<const uint16_t*>(p.k) + kvhead * D, (uint32_t)p.Nkv * C::ROWB);
+  const u32x4s rv = raw_desc(static_cast<const uint16_t*>(p.v) + kvhead * D, (uint32_t)p.Nkv * C::ROWB);
+  const u32x4s ro = raw_desc(static_cast<uint16_t*>(p.o) + qhead * D, (uint32_t)p.Nq * C::ROWB);
   const u32x4s rl = raw_desc(p.lse + qhead, (uint32_t)p.Nq * 4u);
 
-  // DMA share: wave w moves 1 KiB chunks 8w .. 8w+7 of each 32 KiB stage
-  // (K tile = chunks 0-15, V tile = 16-31); chunk c, lane l writes 16 bytes
-  // of row 4c + l/16 at logical 16-byte column l % 16, stored at column
-  // (l % 16) ^ swizzle(row): K rows swizzle by row % 16 (the 16 lanes that
-  // read one logical column of 16 rows hit 16 distinct bank groups), V rows by
-  // 4 * (row % 4) (a transposed read touches 4 rows x 4 columns).
+  // DMA share: waves 0-1 move the K tile, waves 2-3 the V tile, NPIECE 1 KiB
+  // pieces each (pieces ci0 .. ci0 + NPIECE-1 of the tile); piece c, lane l
+  // writes 16 bytes of row c * (1024 / ROWB) + l / NCH at logical 16-byte
+  // column l % NCH, stored at column (l % NCH) ^ swizzle(row).
   const bool isv = wave >= 2;
   const u32x4s rdma = isv ? rv : rk;
-  const int ci0 = (8 * wave) & 15;
-  const uint32_t dmabase = lds0 + (isv ? 65536u : 0u) + (uint32_t)ci0 * 1024u;
+  const int ci0 = (C::NPIECE * wave) & (2 * C::NPIECE - 1);
+  const uint32_t dmabase = lds0 + (isv ? (uint32_t)C::VRING : 0u) + (uint32_t)ci0 * 1024u;
   uint32_t dmaoff[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const int row = (ci0 + u) * 4 + (lane >> 4);
-    const int sw = isv ? ((row & 3) << 2) : (row & 15);
-    dmaoff[u] = (uint32_t)(row * 256 + (((lane & 15) ^ sw) * 16));
+    const int row = (ci0 + u) * (1024 / C::ROWB) + lane / C::NCH;
+    const int sw = isv ? swz_v<D>(row) : swz_k<D>(row);
+    dmaoff[u] = (uint32_t)(row * C::ROWB + (((lane % C::NCH) ^ sw) * 16));
   }
   // K fragment (A operand of S^T = K Q^T): key row l32 of a 32-key block,
-  // logical column 2cd + half, physical column ^ (row % 16).
-  const int swz = l32 & 15;
-  const uint32_t kbase = (uint32_t)(l32 * 256 + ((half ^ (swz & 1)) * 16) + ((swz >> 1) * 32));
+  // logical column 2cd + half, physical column ^ swizzle(row).
+  const int swz = swz_k<D>(l32);
+  const uint32_t kbase = (uint32_t)(l32 * C::ROWB + ((half ^ (swz & 1)) * 16) + ((swz >> 1) * 32));
   // V^T fragment (A operand of O^T += V^T P^T) by ds_read_b64_tr_b16: lane
   // (g, s) of its 16-lane group addresses key row 4*(g/2) + s/4 and 4
   // dimensions at 16*(g%2) + 4*(s%4); the read hands lane r of the group the
   // 4 keys of dimension 16*(g%2) + r.
   const int g16 = lane >> 4, s16 = lane & 15;
   const int vrow = (g16 >> 1) * 4 + (s16 >> 2);
-  const uint32_t vbase = (uint32_t)(vrow * 256 + (vrow & 3) * 64 + (g16 & 1) * 32 +
+  const uint32_t vbase = (uint32_t)(vrow * C::ROWB + swz_v<D>(vrow) * 16 + (g16 & 1) * 32 +
                                     ((s16 & 3) >> 1) * 16 + (s16 & 1) * 8);
+  // (at d = 64 only kaddr0-3 and vaddr0-1 are operands of the body)
   const uint32_t kaddr0 = lds0 + (kbase ^ 0u), kaddr1 = lds0 + (kbase ^ 32u),
                  kaddr2 = lds0 + (kbase ^ 64u), kaddr3 = lds0 + (kbase ^ 96u),
                  kaddr4 = lds0 + (kbase ^ 128u), kaddr5 = lds0 + (kbase ^ 160u),
                  kaddr6 = lds0 + (kbase ^ 192u), kaddr7 = lds0 + (kbase ^ 224u);
-  const uint32_t vaddr0 = lds0 + 65536u + (vbase ^ 0u), vaddr1 = lds0 + 65536u + (vbase ^ 64u),
-                 vaddr2 = lds0 + 65536u + (vbase ^ 128u), vaddr3 = lds0 + 65536u + (vbase ^ 192u);
-  // Q rows q0w + 32h + l32, dimensions 16cd + 8*half (+ 8192 bytes for h = 1)
-  const uint32_t qoff = (uint32_t)((q0w + l32) * 256 + half * 16);
+  const uint32_t vr = lds0 + (uint32_t)C::VRING;
+  const uint32_t vaddr0 = vr + (vbase ^ 0u), vaddr1 = vr + (vbase ^ 64u),
+                 vaddr2 = vr + (vbase ^ 128u), vaddr3 = vr + (vbase ^ 192u);
+  // Q rows q0w + 32h + l32, dimensions 16cd + 8*half (+ 32 rows for h = 1)
+  const uint32_t qoff = (uint32_t)((q0w + l32) * C::ROWB + half * 16);
   // Mask limit: key j of row i is kept iff j <= min(N_kv - 1, causal ? i : inf)
   const int big = 0x3fffffff;
   const int lim0 = min(p.Nkv - 1, CAUSAL ? q0w + l32 : big);
   const int lim1 = min(p.Nkv - 1, CAUSAL ? q0w + 32 + l32 : big);
-  // Epilogue: row q0w + 4i + lane/16, 16-byte column lane % 16; lse of row q0w + 32h + l32
-  const uint32_t ooff = (uint32_t)((q0w + (lane >> 4)) * 256 + (lane & 15) * 16);
+  // Epilogue: row q0w + (64 / NCH) i + lane / NCH, 16-byte column lane % NCH;
+  // lse of row q0w + 32h + l32
+  const uint32_t ooff = (uint32_t)((q0w + lane / C::NCH) * C::ROWB + (lane % C::NCH) * 16);
   const uint32_t lseoff = (uint32_t)((q0w + l32) * 4);
-  const uint32_t obase = lds0 + (uint32_t)wave * 16384u;
+  const uint32_t obase = lds0 + (uint32_t)wave * (64u * C::ROWB);
   // Selector of the row-sum instruction (v_mfma_f32_16x16x32 reading P as B):
   // lane 16g + c holds A row c, columns 8g .. 8g+7; 1.0 in rows 0 and 8 for
   // g = 0, 2 and rows 4 and 12 for g = 1, 3, i.e. where lane % 8 == 4 * (g % 2).
@@ -727,24 +344,36 @@ __device__ __forceinline__ void w64_item(const Params& p, uint32_t lds0, int b, 
   const uint32_t qxor = p.qmode == 1 ? 0x80008000u : 0u;
   const uint32_t qand = p.qmode == 2 ? 0u : 0xffffffffu;
 
-#define FA_W64_OPERANDS                                                                     \
+#define FA_W64_COMMON                                                                       \
   [rq] "s"(rq), [rdma] "s"(rdma), [ro] "s"(ro), [rl] "s"(rl), [dmabase] "s"(dmabase),       \
       [sl2] "s"(sl2), [qxor] "s"(qxor), [qand] "s"(qand), [ntiles] "s"(ntiles),             \
       [nmain] "s"(nmain), [obase] "s"(obase), [kaddr0] "v"(kaddr0), [kaddr1] "v"(kaddr1),  \
-      [kaddr2] "v"(kaddr2), [kaddr3] "v"(kaddr3), [kaddr4] "v"(kaddr4), [kaddr5] "v"(kaddr5), \
-      [kaddr6] "v"(kaddr6), [kaddr7] "v"(kaddr7), [vaddr0] "v"(vaddr0), [vaddr1] "v"(vaddr1), \
-      [vaddr2] "v"(vaddr2), [vaddr3] "v"(vaddr3), [dmaoff0] "v"(dmaoff[0]),                 \
-      [dmaoff1] "v"(dmaoff[1]), [dmaoff2] "v"(dmaoff[2]), [dmaoff3] "v"(dmaoff[3]),         \
-      [qoff] "v"(qoff), [lim0] "v"(lim0), [lim1] "v"(lim1), [ooff] "v"(ooff),              \
-      [lseoff] "v"(lseoff), [selv] "v"(selv)
-  if constexpr (sizeof(T) == 2 && __is_same(T, __bf16)) {
-    if constexpr (CAUSAL) asm volatile(FA_W64_BF16_CAUSAL : : FA_W64_OPERANDS : FA_W64_CLOBBERS);
-    else asm volatile(FA_W64_BF16_FULL : : FA_W64_OPERANDS : FA_W64_CLOBBERS);
+      [kaddr2] "v"(kaddr2), [kaddr3] "v"(kaddr3), [vaddr0] "v"(vaddr0), [vaddr1] "v"(vaddr1), \
+      [dmaoff0] "v"(dmaoff[0]), [dmaoff1] "v"(dmaoff[1]), [dmaoff2] "v"(dmaoff[2]),         \
+      [dmaoff3] "v"(dmaoff[3]), [qoff] "v"(qoff), [lim0] "v"(lim0), [lim1] "v"(lim1),       \
+      [ooff] "v"(ooff), [lseoff] "v"(lseoff), [selv] "v"(selv)
+#define FA_W64_OPERANDS                                                                     \
+  FA_W64_COMMON, [kaddr4] "v"(kaddr4), [kaddr5] "v"(kaddr5), [kaddr6] "v"(kaddr6),          \
+      [kaddr7] "v"(kaddr7), [vaddr2] "v"(vaddr2), [vaddr3] "v"(vaddr3)
+  if constexpr (D == 128) {
+    if constexpr (sizeof(T) == 2 && __is_same(T, __bf16)) {
+      if constexpr (CAUSAL) asm volatile(FA_W64_BF16_CAUSAL : : FA_W64_OPERANDS : FA_W64_CLOBBERS);
+      else asm volatile(FA_W64_BF16_FULL : : FA_W64_OPERANDS : FA_W64_CLOBBERS);
+    } else {
+      if constexpr (CAUSAL) asm volatile(FA_W64_F16_CAUSAL : : FA_W64_OPERANDS : FA_W64_CLOBBERS);
+      else asm volatile(FA_W64_F16_FULL : : FA_W64_OPERANDS : FA_W64_CLOBBERS);
+    }
   } else {
-    if constexpr (CAUSAL) asm volatile(FA_W64_F16_CAUSAL : : FA_W64_OPERANDS : FA_W64_CLOBBERS);
-    else asm volatile(FA_W64_F16_FULL : : FA_W64_OPERANDS : FA_W64_CLOBBERS);
+    if constexpr (sizeof(T) == 2 && __is_same(T, __bf16)) {
+      if constexpr (CAUSAL) asm volatile(FA_W64D64_BF16_CAUSAL : : FA_W64_COMMON : FA_W64_CLOBBERS);
+      else asm volatile(FA_W64D64_BF16_FULL : : FA_W64_COMMON : FA_W64_CLOBBERS);
+    } else {
+      if constexpr (CAUSAL) asm volatile(FA_W64D64_F16_CAUSAL : : FA_W64_COMMON : FA_W64_CLOBBERS);
+      else asm volatile(FA_W64D64_F16_FULL : : FA_W64_COMMON : FA_W64_CLOBBERS);
+    }
   }
 #undef FA_W64_OPERANDS
+#undef FA_W64_COMMON
 }
 
 // Non-causal grids: one work item per workgroup (map_block).  Causal grids
@@ -756,15 +385,15 @@ __device__ __forceinline__ void w64_item(const Params& p, uint32_t lds0, int b, 
 // dispatcher hands new workgroups to the shader engines of an XCD in strict
 // rotation and holds them while the next engine in turn has no free CU,
 // which left CUs idle between short causal items.
-template <typename T, bool CAUSAL>
-__global__ void __launch_bounds__(CfgW64::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <typename T, bool CAUSAL, int D>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 attn_fwd_w64(Params p) {
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[CfgW64::LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[CfgW64<D>::LDS_BYTES];
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_t*)lds;
   if constexpr (!CAUSAL) {
     int b, hq, qt;
     map_block(p, false, b, hq, qt);
-    w64_item<T, false>(p, lds0, b, hq, qt);
+    w64_item<T, false, D>(p, lds0, b, hq, qt);
   } else {
     const int G = (int)gridDim.x, bid = (int)blockIdx.x;
     const int n = p.n_heads * p.n_qtiles;
@@ -777,7 +406,7 @@ attn_fwd_w64(Params p) {
       // the previous item's epilogue staged O in the LDS this item's
       // transfers overwrite
       if (j) __syncthreads();
-      w64_item<T, true>(p, lds0, b, hl - b * p.Hq, p.n_qtiles - 1 - rr);
+      w64_item<T, true, D>(p, lds0, b, hl - b * p.Hq, p.n_qtiles - 1 - rr);
     }
   }
 }
@@ -2349,8 +1978,8 @@ Geometry geometry_for(int d, int dtype) {
     if (d == 64) return {CfgF32<64>::BR, CfgF32<64>::BC, CfgF32<64>::NT, CfgF32<64>::LDS_BYTES};
     return {CfgF32<128>::BR, CfgF32<128>::BC, CfgF32<128>::NT, CfgF32<128>::LDS_BYTES};
   }
-  if (d == 64) return {Cfg16<64>::BR, Cfg16<64>::BC, Cfg16<64>::NT, Cfg16<64>::LDS_BYTES};
-  return {CfgW64::BR, CfgW64::BC, CfgW64::NT, CfgW64::LDS_BYTES};
+  if (d == 64) return {CfgW64<64>::BR, CfgW64<64>::BC, CfgW64<64>::NT, CfgW64<64>::LDS_BYTES};
+  return {CfgW64<128>::BR, CfgW64<128>::BC, CfgW64<128>::NT, CfgW64<128>::LDS_BYTES};
 }
 
 size_t elem_size(int dtype) { return dtype == FA_F32 ? 4 : 2; }
@@ -2403,12 +2032,6 @@ int set_lds_limit(Kernel kern, int lds_bytes) {
   return FA_OK;
 }
 
-template <typename T, int D, bool CAUSAL>
-int run16(const Params& p, long long blocks, hipStream_t stream) {
-  // All LDS of this kernel is static (one object per ring stage).
-  return launch(attn_fwd_mfma16<T, D, CAUSAL>, 0, p, blocks, Cfg16<D>::NT, stream);
-}
-
 template <int D, bool CAUSAL>
 int run32(const Params& p, long long blocks, hipStream_t stream) {
   using C = CfgF32<D>;
@@ -2437,7 +2060,7 @@ int cu_count(hipStream_t stream, int* out) {
   return FA_OK;
 }
 
-template <typename T, bool CAUSAL>
+template <typename T, bool CAUSAL, int D>
 int run_w64(const Params& p, long long blocks, hipStream_t stream) {
   if constexpr (CAUSAL) {   // persistent grid: one workgroup per CU at most
     int cus = 0;
@@ -2445,13 +2068,13 @@ int run_w64(const Params& p, long long blocks, hipStream_t stream) {
     if (st != FA_OK) return st;
     blocks = blocks < cus ? blocks : cus;
   }
-  return launch(attn_fwd_w64<T, CAUSAL>, 0, p, blocks, CfgW64::NT, stream);
+  return launch(attn_fwd_w64<T, CAUSAL, D>, 0, p, blocks, CfgW64<D>::NT, stream);
 }
 
 template <typename T>
 int dispatch16(const Params& p, int d, bool causal, long long blocks, hipStream_t s) {
-  if (d == 64) return causal ? run16<T, 64, true>(p, blocks, s) : run16<T, 64, false>(p, blocks, s);
-  return causal ? run_w64<T, true>(p, blocks, s) : run_w64<T, false>(p, blocks, s);
+  if (d == 64) return causal ? run_w64<T, true, 64>(p, blocks, s) : run_w64<T, false, 64>(p, blocks, s);
+  return causal ? run_w64<T, true, 128>(p, blocks, s) : run_w64<T, false, 128>(p, blocks, s);
 }
 
 template <int D, bool CAUSAL>

@@ -56,24 +56,36 @@ import os
 import re
 import sys
 
-D = 128
 BC = 64
-ROWB = 2 * D
-KSTAGE = BC * ROWB          # bytes of one K (or V) tile in LDS
-VRING = 4 * KSTAGE          # the V ring starts after the 4-stage K ring
 NSTAGE = 4
 MFMA_CYCLES = 32            # v_mfma_f32_32x32x16: 8 passes of 4 cycles
+
+
+def configure(d):
+    """Head dimension d (128 or 64) and what follows from it; body() sets it."""
+    global D, ROWB, KSTAGE, VRING, NCD, NDB, NPIECE
+    assert d in (64, 128)
+    D = d
+    ROWB = 2 * D            # bytes of one K, V, Q or O row
+    KSTAGE = BC * ROWB      # bytes of one K (or V) tile in LDS
+    VRING = 4 * KSTAGE      # the V ring starts after the 4-stage K ring
+    NCD = D // 16           # 16-dimension blocks of Q and K (the score contraction)
+    NDB = D // 32           # 32-dimension blocks of O per 32-row half
+    NPIECE = KSTAGE // 2048  # 1 KiB DMA pieces per wave and stage (two waves per tile)
+
+
+configure(128)
 
 # ----------------------------------------------------------------- registers
 
 
 def O(h, db):
-    b = 16 * (4 * h + db)
+    b = 16 * (NDB * h + db)
     return f"a[{b}:{b + 15}]"
 
 
 def Q(h, cd):
-    b = 128 + 4 * (8 * h + cd)
+    b = 128 + 4 * (NCD * h + cd)
     return f"a[{b}:{b + 3}]"
 
 
@@ -515,7 +527,7 @@ def s_mfmas_and_reads(dt, buf, kstage, skip=0):
     instructions (h = 0, 1)."""
     ms = []
     reads = []
-    for cd in range(8):
+    for cd in range(NCD):
         for kt in range(2):
             f = 2 * cd + kt
             off = kstage * KSTAGE + kt * (32 * ROWB)
@@ -532,19 +544,19 @@ def s_mfmas_and_reads(dt, buf, kstage, skip=0):
 def pv_mfmas_and_reads(dt, vstage, base_index, buf):
     """Matrix instructions of O += V^T P^T, then the row sums of P, and the V reads.
 
-    Fragment g = 8*kt + 4*cc + db (two ds_read_b64_tr_b16 each) goes to ring
+    Fragment g = NDB*(2*kt + cc) + db (two ds_read_b64_tr_b16 each) goes to ring
     slot g % VSLOTS and feeds h = 0, 1, one after the other."""
     ms = []
     uses = {}
     for kt in range(2):
         for cc in range(2):
-            for (h, db) in [(h, db) for db in range(4) for h in range(2)]:
-                g = 8 * kt + 4 * cc + db
+            for (h, db) in [(h, db) for db in range(NDB) for h in range(2)]:
+                g = NDB * (2 * kt + cc) + db
                 uses.setdefault(g, []).append(base_index + len(ms))
                 ms.append(mfma(mfma_op(dt), O(h, db), VF(g % VSLOTS), P(buf, h, kt, cc), O(h, db)))
     reads = []
-    for g in range(16):
-        kt, cc, db = g // 8, (g // 4) % 2, g % 4
+    for g in range(4 * NDB):
+        kt, cc, db = g // (2 * NDB), (g // NDB) % 2, g % NDB
         off = vstage * KSTAGE + (kt * 32 + cc * 16) * ROWB
         lo = Ins(f"ds_read_b64_tr_b16 {VFlo(g % VSLOTS)}, {{vaddr{db}}} offset:{off}", "lds",
                  writes=regs(VFlo(g % VSLOTS)))
@@ -663,12 +675,13 @@ def max_stream(buf, h, first=False):
 
 
 def dma_issue(stage):
-    """The wave's 8 KiB share of a K/V tile into ring stage `stage`: 8 x 1 KiB LDS DMA.
+    """The wave's share of a K/V tile (half of it) into ring stage `stage`: NPIECE x 1 KiB
+    LDS DMA (8 at d = 128, 4 at d = 64).
 
     The tile's byte offset is S_TOFF (S_TOFF2 = S_TOFF + 4 KiB for the second
     four pieces); both advance by one tile after the issue."""
     ins = []
-    for u in range(8):
+    for u in range(NPIECE):
         m0 = stage * KSTAGE + u * 1024
         ins.append(raw(f"s_add_u32 m0, {{dmabase}}, {m0}", "salu", writes=["m0"]))
         soff = S_TOFF if u < 4 else S_TOFF2
@@ -689,9 +702,9 @@ def rescale_block():
     t = RTMP
     k = 0   # (RTMP)
     for h in range(2):
-        for db in range(4):
+        for db in range(NDB):
             for r in range(16):
-                a = 16 * (4 * h + db) + r
+                a = 16 * (NDB * h + db) + r
                 x = t[k % 16]
                 b.out.append(Ins(f"v_accvgpr_read_b32 {x}, a{a}", "accr"))
                 b.out.append(Ins(f"v_mul_f32 {x}, {x}, {ALPHA[h]}", "valu"))
@@ -744,7 +757,7 @@ def tile_step(dt, j_parity, masked, causal, uid):
     # the sync point: the matrix instruction that first uses the last V fragment
     # (so every V(j) read of this wave has been issued; the wait returns them)
     sync_at = rd_pv[-1][0]
-    sync = [Ins("s_waitcnt vmcnt(8) lgkmcnt(0)", "wait"), Ins("s_barrier", "barrier")]
+    sync = [Ins(f"s_waitcnt vmcnt({NPIECE}) lgkmcnt(0)", "wait"), Ins("s_barrier", "barrier")]
     nextk = [k_read(f, (j_parity + 2) % 4) for f in range(KSLOTS)]
     # priority order: the next tile's first K reads, the K/V transfers (paced, all issued
     # before the sync), the exponentials, the running sum, the row maximum of S(j+1)
@@ -790,14 +803,14 @@ def first_tile(dt, masked_first):
     """Prologue: Q to AGPRs, zero O, DMA tiles 0-2, S(0) and its reference."""
     b = Block()
     b.put(raw(f"s_mov_b32 {S_M0}, m0"))
-    b.put(raw(f"s_movk_i32 {S_H8K}, 0x2000"))
+    b.put(raw(f"s_movk_i32 {S_H8K}, {hex(32 * ROWB)}"))
     b.put(raw(f"s_mov_b32 {S_TOFF}, 0"))
     b.put(raw(f"s_movk_i32 {S_TOFF2}, 0x1000"))
     b.put(raw(f"s_mov_b32 {S_KV0}, 0"))
-    # Q rows: 16 loads of 16 bytes per lane into v[0:63], then to AGPRs
+    # Q rows: 2*NCD loads of 16 bytes per lane into v[0:8*NCD-1], then to AGPRs
     for h in range(2):
-        for cd in range(8):
-            dst = f"v[{4 * (8 * h + cd)}:{4 * (8 * h + cd) + 3}]"
+        for cd in range(NCD):
+            dst = f"v[{4 * (NCD * h + cd)}:{4 * (NCD * h + cd) + 3}]"
             soff = "0" if h == 0 else S_H8K
             b.put(Ins(f"buffer_load_dwordx4 {dst}, {{qoff}}, {{rq}}, {soff} offen offset:{cd * 32}",
                       "vmem", writes=regs(dst)))
@@ -805,7 +818,7 @@ def first_tile(dt, masked_first):
         for ins in dma_issue(stage):
             b.put(ins)
     # O = 0 while the loads are in flight
-    for i in range(128):
+    for i in range(32 * NDB):
         b.put(Ins(f"v_accvgpr_write_b32 a{i}, 0", "accw"))
     b.put(valu(f"v_mov_b32 {NEGINF}, 0xff800000", [], [NEGINF]))
     for r in regs(SEL):
@@ -819,14 +832,14 @@ def first_tile(dt, masked_first):
         for r in regs(LACC[h]) + [LRUN[h]]:
             b.put(valu(f"v_mov_b32 {r}, 0", [], [r]))
         b.put(valu(f"v_mov_b32 {ALPHA[h]}, 1.0", [], [ALPHA[h]]))
-    b.put(Ins("s_waitcnt vmcnt(24)", "wait"))
-    for i in range(64):
+    b.put(Ins(f"s_waitcnt vmcnt({3 * NPIECE})", "wait"))   # Q, then tiles 0-2
+    for i in range(8 * NCD):
         b.put(valu(f"v_xor_b32 v{i}, {{qxor}}, v{i}", [f"v{i}"], [f"v{i}"]))
         b.put(valu(f"v_and_b32 v{i}, {{qand}}, v{i}", [f"v{i}"], [f"v{i}"]))
-    for i in range(64):
+    for i in range(8 * NCD):
         b.put(Ins(f"v_accvgpr_write_b32 a{128 + i}, v{i}", "accw", reads=[f"v{i}"]))
     b.pad(4)
-    b.put(Ins("s_waitcnt vmcnt(16)", "wait"))
+    b.put(Ins(f"s_waitcnt vmcnt({2 * NPIECE})", "wait"))   # tile 0
     b.put(Ins("s_barrier", "barrier"))
     ms, rd = s_mfmas_and_reads(dt, 0, 0)
     tail = []
@@ -835,7 +848,7 @@ def first_tile(dt, masked_first):
     tail += max_stream(0, 0, first=True) + max_stream(0, 1, first=True)
     schedule(b, ms, [Stream(tail, len(ms), "max")], rd)
     # tile 1 visible to every wave, then the first K reads of S(1)
-    b.put(Ins("s_waitcnt vmcnt(8) lgkmcnt(0)", "wait"))
+    b.put(Ins(f"s_waitcnt vmcnt({NPIECE}) lgkmcnt(0)", "wait"))
     b.put(Ins("s_barrier", "barrier"))
     b.lgkm = []
     prefetch_k(b, 1)
@@ -873,25 +886,35 @@ def epilogue(dt):
         b.put(valu(f"v_mul_f32 {TMP[h]}, 0x3f317218, {TMP[h]}", [TMP[h]], [TMP[h]]))
         b.put(Ins(f"buffer_store_dword {TMP[h]}, {{lseoff}}, {{rl}}, 0 offen offset:{h * 128}",
                   "vmem", reads=[TMP[h]]))
-    # the wave's O tile (64 rows x 256 bytes) into its own 16 KiB of LDS, row-swizzled
+    # the wave's O tile (64 rows x ROWB bytes) into its own 64*ROWB bytes of LDS, row-swizzled
     # lane (l32, half) of block (h, db) holds row 32h + l32, columns db*32 + 8g + 4*half + (0..3)
-    # byte address: row*256 + ((chunk ^ (row & 15)) * 16) + half*8, chunk = 4*db + g
+    # byte address: row*ROWB + ((chunk ^ sw(row)) * 16) + half*8, chunk = 4*db + g, where
+    # sw(row) = row & 15 with 16 chunks per row (d = 128), (row >> 1) & 7 with 8 (d = 64)
+    lg_rowb = ROWB.bit_length() - 1
+    nch = ROWB // 16
+
+    def swizzle(dst, row):
+        if nch == 16:
+            b.put(valu(f"v_and_b32 {dst}, 15, {row}", [row], [dst]))
+        else:
+            b.put(valu(f"v_lshrrev_b32 {dst}, 1, {row}", [row], [dst]))
+            b.put(valu(f"v_and_b32 {dst}, 7, {dst}", [dst], [dst]))
     b.put(valu(f"v_mbcnt_lo_u32_b32 {t[16]}, -1, 0", [], [t[16]]))
     b.put(valu(f"v_mbcnt_hi_u32_b32 {t[16]}, -1, {t[16]}", [t[16]], [t[16]]))
     b.put(valu(f"v_and_b32 {t[17]}, 31, {t[16]}", [t[16]], [t[17]]))           # l32
     b.pad(18)
     for h in range(2):
-        # row = 32h + l32 -> (row & 15) = l32 & 15; base = lds + row*256 + half*8
-        b.put(valu(f"v_lshlrev_b32 {t[14]}, 8, {t[17]}", [t[17]], [t[14]]))     # l32*256
+        # row = 32h + l32 -> sw(row) = sw(l32); base = lds + row*ROWB + half*8
+        b.put(valu(f"v_lshlrev_b32 {t[14]}, {lg_rowb}, {t[17]}", [t[17]], [t[14]]))  # l32*ROWB
         b.put(valu(f"v_add_u32 {t[14]}, {{obase}}, {t[14]}", [t[14]], [t[14]]))
-        b.put(valu(f"v_add_u32 {t[14]}, {h * 32 * 256}, {t[14]}", [t[14]], [t[14]]))
+        b.put(valu(f"v_add_u32 {t[14]}, {h * 32 * ROWB}, {t[14]}", [t[14]], [t[14]]))
         b.put(valu(f"v_lshrrev_b32 {t[15]}, 2, {HALF4}", [HALF4], [t[15]]))      # half
         b.put(valu(f"v_lshlrev_b32 {t[15]}, 3, {t[15]}", [t[15]], [t[15]]))      # half*8
         b.put(valu(f"v_add_u32 {t[14]}, {t[14]}, {t[15]}", [t[14], t[15]], [t[14]]))
-        b.put(valu(f"v_and_b32 {t[13]}, 15, {t[17]}", [t[17]], [t[13]]))         # row & 15
-        for db in range(4):
+        swizzle(t[13], t[17])
+        for db in range(NDB):
             for g in range(4):
-                base = 16 * (4 * h + db) + 4 * g
+                base = 16 * (NDB * h + db) + 4 * g
                 x = [t[(4 * (db * 4 + g) + i) % 12] for i in range(4)]
                 for i in range(4):
                     b.put(Ins(f"v_accvgpr_read_b32 {x[i]}, a{base + i}", "accr", writes=[x[i]]))
@@ -899,23 +922,24 @@ def epilogue(dt):
                     b.put(valu(f"v_mul_f32 {x[i]}, {x[i]}, {ALPHA[h]}", [x[i], ALPHA[h]], [x[i]]))
                 b.put(valu(f"{cvt_op(dt)} {x[0]}, {x[0]}, {x[1]}", [x[0], x[1]], [x[0]]))
                 b.put(valu(f"{cvt_op(dt)} {x[1]}, {x[2]}, {x[3]}", [x[2], x[3]], [x[1]]))
-                # address: base + ((4db+g) ^ (row&15)) * 16
+                # address: base + ((4db+g) ^ sw(row)) * 16
                 b.put(valu(f"v_xor_b32 {t[12]}, {4 * db + g}, {t[13]}", [t[13]], [t[12]]))
                 b.put(valu(f"v_lshl_add_u32 {t[12]}, {t[12]}, 4, {t[14]}", [t[12], t[14]], [t[12]]))
                 b.put(Ins(f"ds_write_b64 {t[12]}, v[{x[0][1:]}:{int(x[0][1:]) + 1}]", "lds_w",
                           reads=[t[12], x[0], x[1]]))
     b.put(Ins("s_waitcnt lgkmcnt(0)", "wait"))
-    # read back whole rows: read i covers rows 4i .. 4i+3, lane -> row 4i + (lane >> 4),
-    # logical chunk lane & 15 at physical chunk (lane & 15) ^ (row & 15)
-    b.put(valu(f"v_lshrrev_b32 {t[15]}, 4, {t[16]}", [t[16]], [t[15]]))         # lane >> 4
-    b.put(valu(f"v_and_b32 {t[13]}, 15, {t[16]}", [t[16]], [t[13]]))            # lane & 15
-    for i in range(16):
-        row_lo = (4 * i) & 15
+    # read back whole rows: read i covers rows rpr*i .. rpr*i + rpr-1, lane -> row
+    # rpr*i + lane / nch, logical chunk lane % nch at physical chunk (lane % nch) ^ sw(row)
+    rpr = 64 // nch
+    b.put(valu(f"v_lshrrev_b32 {t[15]}, {nch.bit_length() - 1}, {t[16]}", [t[16]], [t[15]]))
+    b.put(valu(f"v_and_b32 {t[13]}, {nch - 1}, {t[16]}", [t[16]], [t[13]]))
+    nread = 64 // rpr
+    for i in range(nread):
         y = f"v[{int(t[0][1:]) + 4 * (i % 3)}:{int(t[0][1:]) + 4 * (i % 3) + 3}]"
-        b.put(valu(f"v_add_u32 {t[12]}, {4 * i}, {t[15]}", [t[15]], [t[12]]))    # row
-        b.put(valu(f"v_and_b32 {t[14]}, 15, {t[12]}", [t[12]], [t[14]]))
+        b.put(valu(f"v_add_u32 {t[12]}, {rpr * i}, {t[15]}", [t[15]], [t[12]]))    # row
+        swizzle(t[14], t[12])
         b.put(valu(f"v_xor_b32 {t[14]}, {t[14]}, {t[13]}", [t[14], t[13]], [t[14]]))
-        b.put(valu(f"v_lshlrev_b32 {t[12]}, 8, {t[12]}", [t[12]], [t[12]]))
+        b.put(valu(f"v_lshlrev_b32 {t[12]}, {lg_rowb}, {t[12]}", [t[12]], [t[12]]))
         b.put(valu(f"v_lshl_add_u32 {t[12]}, {t[14]}, 4, {t[12]}", [t[12], t[14]], [t[12]]))
         b.put(valu(f"v_add_u32 {t[12]}, {{obase}}, {t[12]}", [t[12]], [t[12]]))
         b.put(Ins(f"ds_read_b128 {y}, {t[12]}", "lds", writes=regs(y)))
@@ -924,19 +948,20 @@ def epilogue(dt):
         b.put(Ins(f"buffer_store_dwordx4 {y}, {{ooff}}, {{ro}}, 0 offen offset:{0}" if i == 0 else
                   f"buffer_store_dwordx4 {y}, {{ooff}}, {{ro}}, {S_TMP} offen", "vmem",
                   reads=regs(y)))
-        if i < 15:
-            b.put(raw(f"s_mov_b32 {S_TMP}, {(4 * (i + 1)) * 256}"))
+        if i < nread - 1:
+            b.put(raw(f"s_mov_b32 {S_TMP}, {(rpr * (i + 1)) * ROWB}"))
     b.put(raw(f"s_mov_b32 m0, {S_M0}"))
     return b
 
 
-def body(dt, causal):
-    """The whole per-workgroup asm body as text with {operand} placeholders.
+def body(dt, causal, d=128):
+    """The whole per-workgroup asm body (head dimension d) as text with {operand} placeholders.
 
     Control flow: prologue (tile 0), then one block per tile j chosen by the
     dispatcher from j % 4 (ring stages, score buffer) and from whether tile
     j + 1 needs a mask or does not exist (then the drain of tile j), then the
     epilogue."""
+    configure(d)
     # s_nop: wait states for any vector write of an operand (SGPR or VGPR) made
     # by the compiled code just before the statement
     parts = ["s_nop 7"]
@@ -966,6 +991,7 @@ def body(dt, causal):
         parts += [f".Lm_{p}:", tile_step(dt, p, True, causal, f"m_{p}").text()]
         parts += [f".Ld_{p}:", drain(dt, p).text()]
     parts += [".Lepi:", epilogue(dt).text()]
+    configure(128)
     return "\n".join(parts) + "\n"
 
 
@@ -982,9 +1008,9 @@ OPERANDS = {
 }
 
 
-def asm_text(dt, causal):
+def asm_text(dt, causal, d=128):
     """Body with placeholders turned into named inline-asm operands, labels made unique."""
-    t = body(dt, causal)
+    t = body(dt, causal, d)
     t = re.sub(r"\{(\w+)\}", lambda m: "%[" + m.group(1) + "]", t)
     t = t.replace(".L", ".Lfw%=_")
     return t
@@ -1006,10 +1032,11 @@ def write_inc(path=None):
     """Write the asm bodies as string-literal macros (inline asm needs a literal)."""
     path = path or os.path.join(os.path.dirname(os.path.abspath(__file__)), "fa_fwd_w64.inc")
     out = ["// Generated by gen_fwd_w64.py (run by the library build): do not edit.", ""]
-    for dt in ("bf16", "f16"):
-        for causal in (False, True):
-            name = f"FA_W64_{dt.upper()}_{'CAUSAL' if causal else 'FULL'}"
-            out.append(c_macro(name, asm_text(dt, causal)))
+    for d in (128, 64):
+        for dt in ("bf16", "f16"):
+            for causal in (False, True):
+                name = f"FA_W64{'' if d == 128 else 'D64'}_{dt.upper()}_{'CAUSAL' if causal else 'FULL'}"
+                out.append(c_macro(name, asm_text(dt, causal, d)))
     out.append("#define FA_W64_CLOBBERS " + ", ".join(f'"{c}"' for c in clobbers()))
     out.append("")
     text = "\n".join(out)

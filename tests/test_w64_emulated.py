@@ -29,25 +29,36 @@ TOL = 2e-2
 KBUF, VBUF, QBUF, OBUF, LBUF = 1, 2, 3, 4, 5
 
 
-def operands(wave, q0, Nq, Nkv, causal, scale, dt="bf16", qhead_bytes=0, kvhead_bytes=0):
+def operands(wave, q0, Nq, Nkv, causal, scale, dt="bf16", qhead_bytes=0, kvhead_bytes=0, d=128):
     """Inline-asm operands of one wave: register name -> value (per lane or scalar)."""
     lane = np.arange(64)
     l32, half = lane & 31, lane >> 5
     lds = 0
-    # K fragment addresses: row l32, logical chunk 2cd + half, physical chunk ^ (row & 15)
-    swz = l32 & 15
-    kbase = l32 * 256 + ((half ^ (swz & 1)) * 16) + ((swz >> 1) * 32)
+    rowb = 2 * d
+    vring = 4 * 64 * rowb
+    nch = rowb // 16           # 16-byte chunks per row
+    rpp = 1024 // rowb         # rows per 1 KiB DMA piece
+
+    def sw_k(row):             # K rows: 16-byte chunk index XOR
+        return row & 15 if d == 128 else (row >> 1) & 7
+
+    def sw_v(row):             # V rows
+        return (row & 3) << 2 if d == 128 else ((row >> 1) & 1) << 2
+    # K fragment addresses: row l32, logical chunk 2cd + half, physical chunk ^ sw_k(row)
+    swz = sw_k(l32)
+    kbase = l32 * rowb + ((half ^ (swz & 1)) * 16) + ((swz >> 1) * 32)
     # V^T fragment addresses (ds_read_b64_tr_b16)
     g16, s16 = lane >> 4, lane & 15
     vrow = (g16 >> 1) * 4 + (s16 >> 2)
-    vbase = vrow * 256 + (vrow & 3) * 64 + (g16 & 1) * 32 + ((s16 & 3) >> 1) * 16 + (s16 & 1) * 8
+    vbase = vrow * rowb + sw_v(vrow) * 16 + (g16 & 1) * 32 + ((s16 & 3) >> 1) * 16 + (s16 & 1) * 8
     isv = wave >= 2
-    ci0 = (8 * wave) & 15
+    npiece = 64 * rowb // 2048
+    ci0 = (npiece * wave) & (2 * npiece - 1)
     dmaoff = []
     for u in range(4):
-        row = (ci0 + u) * 4 + (lane >> 4)
-        sw = ((row & 3) << 2) if isv else (row & 15)
-        dmaoff.append(row * 256 + ((lane & 15) ^ sw) * 16)
+        row = (ci0 + u) * rpp + lane // nch
+        sw = sw_v(row) if isv else sw_k(row)
+        dmaoff.append(row * rowb + ((lane % nch) ^ sw) * 16)
     q0w = q0 + 64 * wave
     big = 0x3FFFFFFF
     lim = [np.minimum(Nkv - 1, (q0w + 32 * h + l32) if causal else big) for h in range(2)]
@@ -61,21 +72,21 @@ def operands(wave, q0, Nq, Nkv, causal, scale, dt="bf16", qhead_bytes=0, kvhead_
     else:
         sl2, qxor, qand = 1.0, 0, 0
     sv = {
-        "rq": [QBUF, qhead_bytes, Nq * 256, 0],
-        "rdma": [VBUF if isv else KBUF, kvhead_bytes, Nkv * 256, 0],
-        "ro": [OBUF, qhead_bytes, Nq * 256, 0],
-        "rl": [LBUF, qhead_bytes // 64, Nq * 4, 0],
-        "dmabase": lds + (65536 if isv else 0) + ci0 * 1024,
+        "rq": [QBUF, qhead_bytes, Nq * rowb, 0],
+        "rdma": [VBUF if isv else KBUF, kvhead_bytes, Nkv * rowb, 0],
+        "ro": [OBUF, qhead_bytes, Nq * rowb, 0],
+        "rl": [LBUF, qhead_bytes // (rowb // 4), Nq * 4, 0],
+        "dmabase": lds + (vring if isv else 0) + ci0 * 1024,
         "sl2": int(np.float32(sl2).view(np.uint32)),
         "qxor": qxor, "qand": qand, "ntiles": ntiles, "nmain": nmain,
-        "obase": lds + wave * 16384,
+        "obase": lds + wave * 64 * rowb,
     }
-    vv = {f"kaddr{cd}": lds + (kbase ^ (cd * 32)) for cd in range(8)}
-    vv.update({f"vaddr{db}": lds + 65536 + (vbase ^ (db * 64)) for db in range(4)})
+    vv = {f"kaddr{cd}": lds + (kbase ^ (cd * 32)) for cd in range(d // 16)}
+    vv.update({f"vaddr{db}": lds + vring + (vbase ^ (db * 64)) for db in range(d // 32)})
     vv.update({f"dmaoff{u}": dmaoff[u] for u in range(4)})
-    vv["qoff"] = (q0w + l32) * 256 + half * 16
+    vv["qoff"] = (q0w + l32) * rowb + half * 16
     vv["lim0"], vv["lim1"] = lim
-    vv["ooff"] = (q0w + (lane >> 4)) * 256 + (lane & 15) * 16
+    vv["ooff"] = (q0w + lane // nch) * rowb + (lane % nch) * 16
     vv["lseoff"] = (q0w + l32) * 4
     one = 0x3F803F80 if dt == "bf16" else 0x3C003C00
     vv["selv"] = np.where((lane & 7) == ((lane >> 2) & 4), one, 0)
@@ -100,6 +111,7 @@ def assign_registers(text):
 
 def run_workgroup(text, q, k, v, q0, causal, scale, dt, order):
     B, H, Nq, D = q.shape
+    rowb = 2 * D
     Nkv = k.shape[2]
     sreg, vreg = assign_registers(text)
     body = text
@@ -108,10 +120,10 @@ def run_workgroup(text, q, k, v, q0, causal, scale, dt, order):
     bits = (lambda t: t.view(torch.int16).numpy().view(np.uint8).copy())
     bufs = {QBUF: bits(q.contiguous()).reshape(-1), KBUF: bits(k.contiguous()).reshape(-1),
             VBUF: bits(v.contiguous()).reshape(-1),
-            OBUF: np.full(Nq * 256, 0xFF, np.uint8), LBUF: np.full(Nq * 4, 0xFF, np.uint8)}
+            OBUF: np.full(Nq * rowb, 0xFF, np.uint8), LBUF: np.full(Nq * 4, 0xFF, np.uint8)}
     emu = Emu(body, bufs, order=order)
     for w in range(4):
-        sv, vv = operands(w, q0, Nq, Nkv, causal, scale, dt)
+        sv, vv = operands(w, q0, Nq, Nkv, causal, scale, dt, d=D)
         wave = emu.waves[w]
         for n, val in sv.items():
             r = gen.regs(sreg[n])
@@ -124,22 +136,22 @@ def run_workgroup(text, q, k, v, q0, causal, scale, dt, order):
     return bufs[OBUF], bufs[LBUF]
 
 
-def check(dt, causal, Nq, Nkv, q0, scale=None, sigma=1.0, seed=0, outliers=0.0):
+def check(dt, causal, Nq, Nkv, q0, scale=None, sigma=1.0, seed=0, outliers=0.0, d=128):
     torch_dt = workloads.DTYPES[dt]
-    q, k, v = workloads.make_inputs(1, 1, 1, Nq, Nkv, 128, dt, seed, sigma)
+    q, k, v = workloads.make_inputs(1, 1, 1, Nq, Nkv, d, dt, seed, sigma)
     if outliers:
         rng = np.random.default_rng(seed + 99)
         idx = rng.choice(Nkv, max(1, int(outliers * Nkv)), replace=False)
         k[0, 0, idx] = (k[0, 0, idx].float() * 8).to(torch_dt)
-    scale = workloads.default_scale(128) if scale is None else scale
-    text = gen.body(dt, causal)
+    scale = workloads.default_scale(d) if scale is None else scale
+    text = gen.body(dt, causal, d)
     outs = []
     for order in ([0, 1, 2, 3], [3, 2, 1, 0]):
         outs.append(run_workgroup(text, q, k, v, q0, causal, scale, dt, order))
     assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
     o_bytes, l_bytes = outs[0]
     rows = np.arange(q0, min(q0 + 256, Nq))
-    o = torch.from_numpy(o_bytes.view(np.int16).copy()).view(torch_dt).reshape(Nq, 128)[rows]
+    o = torch.from_numpy(o_bytes.view(np.int16).copy()).view(torch_dt).reshape(Nq, d)[rows]
     lse = l_bytes.view(np.float32).reshape(Nq)[rows]
     ref_o, ref_l = attention_fp64(workloads.to_f64(q), workloads.to_f64(k), workloads.to_f64(v),
                                   scale, causal, rows=rows)
@@ -177,9 +189,27 @@ def test_generated_body_matches_oracle(case):
     check(dt, causal, Nq, Nkv, q0, seed=Nq + Nkv + q0)
 
 
-def test_reference_moves_and_rescales():
+CASES_D64 = [
+    ("bf16", False, 256, 256, 0),      # every parity once
+    ("bf16", False, 256, 650, 0),      # parities twice, ragged tail
+    ("bf16", True, 512, 512, 256),     # causal second query tile
+    ("bf16", True, 256, 256, 0),       # causal first tile: masked prologue
+    ("f16", False, 100, 64, 0),        # one tile, ragged rows
+    ("f16", True, 300, 700, 256),
+]
+
+
+@pytest.mark.parametrize("case", CASES_D64, ids=lambda c: "-".join(map(str, c)))
+def test_generated_body_d64_matches_oracle(case):
+    """The same body generated for head dimension 64."""
+    dt, causal, Nq, Nkv, q0 = case
+    check(dt, causal, Nq, Nkv, q0, seed=Nq + Nkv + q0 + 64, d=64)
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_reference_moves_and_rescales(d):
     """Scores spread over tens of units: the lazy reference moves and O is rescaled."""
-    check("bf16", False, 256, 512, 0, scale=1.0, sigma=2.0, seed=5, outliers=0.02)
+    check("bf16", False, 256, 512, 0, scale=1.0, sigma=2.0, seed=5, outliers=0.02, d=d)
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.09])
