@@ -149,6 +149,7 @@ LACC = ["v[200:203]", "v[204:207]"]   # a tile's row sums per half (register 0; 
 LACC0 = ["v200", "v204"]
 RTMP = [f"v{208 + i}" for i in range(16)]   # rescale temporaries
 ETMP = [f"v{i}" for i in range(64)]    # epilogue temporaries: score buffer 0, dead by then
+EPI_DEPTH = 12               # epilogue: LDS reads of O rows in flight ahead of their stores
 
 # SGPR temporaries (clobbered by the statement)
 S_TOFF = "s72"       # byte offset of the tile being transferred (tile index * 16 KiB)
@@ -928,28 +929,42 @@ def epilogue(dt):
                 b.put(Ins(f"ds_write_b64 {t[12]}, v[{x[0][1:]}:{int(x[0][1:]) + 1}]", "lds_w",
                           reads=[t[12], x[0], x[1]]))
     b.put(Ins("s_waitcnt lgkmcnt(0)", "wait"))
+    b.lgkm = []
     # read back whole rows: read i covers rows rpr*i .. rpr*i + rpr-1, lane -> row
-    # rpr*i + lane / nch, logical chunk lane % nch at physical chunk (lane % nch) ^ sw(row)
+    # rpr*i + lane / nch, logical chunk lane % nch at physical chunk (lane % nch) ^ sw(row).
+    # sw(row) repeats every 16 rows, i.e. every `per` reads, so `per` base addresses serve
+    # all reads (the rest is the instruction's offset).  The reads go to score buffer 1
+    # (dead here), one register quad each, EPI_DEPTH in flight ahead of the stores.
     rpr = 64 // nch
+    per = 16 // rpr
+    nread = 64 // rpr
     b.put(valu(f"v_lshrrev_b32 {t[15]}, {nch.bit_length() - 1}, {t[16]}", [t[16]], [t[15]]))
     b.put(valu(f"v_and_b32 {t[13]}, {nch - 1}, {t[16]}", [t[16]], [t[13]]))
-    nread = 64 // rpr
-    for i in range(nread):
-        y = f"v[{int(t[0][1:]) + 4 * (i % 3)}:{int(t[0][1:]) + 4 * (i % 3) + 3}]"
-        b.put(valu(f"v_add_u32 {t[12]}, {rpr * i}, {t[15]}", [t[15]], [t[12]]))    # row
+    bases = [t[18 + k] for k in range(per)]
+    for k in range(per):
+        b.put(valu(f"v_add_u32 {t[12]}, {rpr * k}, {t[15]}", [t[15]], [t[12]]))    # row
         swizzle(t[14], t[12])
         b.put(valu(f"v_xor_b32 {t[14]}, {t[14]}, {t[13]}", [t[14], t[13]], [t[14]]))
         b.put(valu(f"v_lshlrev_b32 {t[12]}, {lg_rowb}, {t[12]}", [t[12]], [t[12]]))
         b.put(valu(f"v_lshl_add_u32 {t[12]}, {t[14]}, 4, {t[12]}", [t[12], t[14]], [t[12]]))
-        b.put(valu(f"v_add_u32 {t[12]}, {{obase}}, {t[12]}", [t[12]], [t[12]]))
-        b.put(Ins(f"ds_read_b128 {y}, {t[12]}", "lds", writes=regs(y)))
-        b.put(Ins("s_waitcnt lgkmcnt(0)", "wait"))
-        b.lgkm = []
-        b.put(Ins(f"buffer_store_dwordx4 {y}, {{ooff}}, {{ro}}, 0 offen offset:{0}" if i == 0 else
-                  f"buffer_store_dwordx4 {y}, {{ooff}}, {{ro}}, {S_TMP} offen", "vmem",
-                  reads=regs(y)))
-        if i < nread - 1:
-            b.put(raw(f"s_mov_b32 {S_TMP}, {(rpr * (i + 1)) * ROWB}"))
+        b.put(valu(f"v_add_u32 {bases[k]}, {{obase}}, {t[12]}", [t[12]], [bases[k]]))
+
+    def y(i):
+        return f"v[{64 + 4 * i}:{64 + 4 * i + 3}]"
+
+    def store(i):
+        if i > 0:
+            b.put(raw(f"s_mov_b32 {S_TMP}, {(rpr * i) * ROWB}"))
+        b.put(Ins(f"buffer_store_dwordx4 {y(i)}, {{ooff}}, {{ro}}, 0 offen offset:0" if i == 0 else
+                  f"buffer_store_dwordx4 {y(i)}, {{ooff}}, {{ro}}, {S_TMP} offen", "vmem",
+                  reads=regs(y(i))))
+    for i in range(nread):
+        b.put(Ins(f"ds_read_b128 {y(i)}, {bases[i % per]} offset:{(i // per) * 16 * ROWB}", "lds",
+                  reads=[bases[i % per]], writes=regs(y(i))))
+        if i >= EPI_DEPTH - 1:
+            store(i - EPI_DEPTH + 1)
+    for i in range(max(0, nread - EPI_DEPTH + 1), nread):
+        store(i)
     b.put(raw(f"s_mov_b32 m0, {S_M0}"))
     return b
 
