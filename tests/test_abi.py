@@ -130,7 +130,12 @@ def test_launch_info(lib):
     # d = 128 in 16 bits: four waves of 64 query rows each
     assert info["threads"] == 256 and info["rows_per_block"] == 256 and info["keys_per_tile"] == 64
     assert info["blocks"] == 2 * 32 * math.ceil(8192 / info["rows_per_block"])
-    assert 0 < info["lds_bytes"] <= 160 * 1024
+    assert info["lds_bytes"] == 4 * 2 * 64 * 128 * 2   # 4 stages of a K and a V tile
+    # d = 64 in 16 bits: the same kernel and shape, half the LDS
+    st, info = fa.fa_launch_info(4, 16, 16, 1024, 1024, 64, 0, fa.FA_BF16)
+    assert st == fa.FA_OK
+    assert info["threads"] == 256 and info["rows_per_block"] == 256 and info["keys_per_tile"] == 64
+    assert info["blocks"] == 4 * 16 * 4 and info["lds_bytes"] == 4 * 2 * 64 * 64 * 2
     st, info = fa.fa_launch_info(1, 1, 1, 256, 256, 64, 0, fa.FA_F32)
     assert st == fa.FA_OK and info["blocks"] == math.ceil(256 / info["rows_per_block"])
     assert fa.fa_launch_info(1, 1, 1, 0, 1, 64, 0, fa.FA_F32)[0] == fa.FA_ERR_BAD_DIM
