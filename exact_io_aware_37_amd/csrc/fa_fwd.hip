@@ -129,7 +129,9 @@ __device__ __forceinline__ int xcd_local(int bid, int nb) {
 // exp2(m_old - m_new)).  Otherwise probabilities are taken against the older,
 // smaller reference and stay below 2^8.  O / l and lse = ref + log2(l) are
 // the same whatever reference is used, so the result stays exact; only the
-// rescale work is skipped.
+// rescale work is skipped.  The kernels of this file use 2^8 (kLazy; the FP8
+// path needs it: E4M3's largest value is 448); the generated 64-row forward
+// body uses 2^15, as much as f16 probabilities allow (largest value 65504).
 
 typedef __attribute__((address_space(3))) unsigned char lds_t;
 typedef short s16x4 __attribute__((ext_vector_type(4)));

@@ -14,7 +14,7 @@ and accumulator by exp(m_old - m_new), add the tile's exponentials; divide by
 the sum once at the end) inside the query-tile-outer, key-tile-inner loop of
 its sections 2 and 3.3, for the 64 query rows of one wave, with the lazy
 exponent reference of the 16-bit kernel (the reference moves only when the
-row maximum passes it by more than 2^8; O / l and lse do not depend on where
+row maximum passes it by more than 2^15; O / l and lse do not depend on where
 it sits).
 
 Why assembly.  A wave that owns 64 query rows reads every K and V fragment
@@ -58,6 +58,12 @@ import sys
 
 BC = 64
 NSTAGE = 4
+# The exponent reference of a row moves only when the row maximum passes it by more than
+# 2^LAZY (log2 units), so probabilities stay <= 2^15: finite in f16 (largest 65504) and
+# far from fp32 range in O and l.  Every move costs a pass over O (the rescale block);
+# the larger headroom leaves it to rows whose maximum really jumps.
+LAZY = 15
+LAZY_HEX = "0x41700000"     # 15.0f
 MFMA_CYCLES = 32            # v_mfma_f32_32x32x16: 8 passes of 4 cycles
 
 
@@ -665,7 +671,7 @@ def max_stream(buf, h, first=False):
         # first tile: the reference is the tile maximum itself; nothing to rescale
         ins.append(valu(f"v_mov_b32 {MRUN[h]}, {MX[h]}", [MX[h]], [MRUN[h]]))
         return ins
-    ins.append(valu(f"v_add_f32 {TMP[h]}, 0x41000000, {MRUN[h]}", [MRUN[h]], [TMP[h]]))
+    ins.append(valu(f"v_add_f32 {TMP[h]}, {LAZY_HEX}, {MRUN[h]}", [MRUN[h]], [TMP[h]]))
     m = MASKS[h]
     ins.append(valu(f"v_cmp_gt_f32 {m}, {MX[h]}, {TMP[h]}", [MX[h], TMP[h]], [m], kind="cmp"))
     ins.append(valu(f"v_cndmask_b32 {MNEW[h]}, {MRUN[h]}, {MX[h]}, {m}", [MRUN[h], MX[h], m],

@@ -90,6 +90,7 @@ class Emu:
     def __init__(self, text, buffers, lds_bytes=160 * 1024, order=None):
         self.lines = []
         self.labels = {}
+        self.executed = {}     # line index -> times executed (all waves)
         for raw in text.split("\n"):
             line = raw.split(";")[0].strip()
             if not line:
@@ -232,6 +233,7 @@ class Emu:
                 seg[seg == w.wid] = -1
 
     def step(self, w, line):
+        self.executed[w.pc] = self.executed.get(w.pc, 0) + 1
         op, _, rest = line.partition(" ")
         args = [a.strip() for a in rest.split(",")] if rest else []
         pc_next = w.pc + 1

@@ -10,6 +10,7 @@ waves in two orders between barriers, which must give identical bytes.  The
 generator's own checks (wait states between dependent instructions) run as it
 emits the code."""
 
+import math
 import os
 import sys
 
@@ -133,10 +134,12 @@ def run_workgroup(text, q, k, v, q0, causal, scale, dt, order):
         for n, val in vv.items():
             wave.v[int(vreg[n][1:])] = np.asarray(val, np.int64).astype(np.uint32)
     emu.run()
+    run_workgroup.rescales = emu.executed.get(emu.labels[".Lrescale"], 0)
     return bufs[OBUF], bufs[LBUF]
 
 
-def check(dt, causal, Nq, Nkv, q0, scale=None, sigma=1.0, seed=0, outliers=0.0, d=128):
+def check(dt, causal, Nq, Nkv, q0, scale=None, sigma=1.0, seed=0, outliers=0.0, d=128,
+          rescales=None):
     torch_dt = workloads.DTYPES[dt]
     q, k, v = workloads.make_inputs(1, 1, 1, Nq, Nkv, d, dt, seed, sigma)
     if outliers:
@@ -148,6 +151,9 @@ def check(dt, causal, Nq, Nkv, q0, scale=None, sigma=1.0, seed=0, outliers=0.0, 
     outs = []
     for order in ([0, 1, 2, 3], [3, 2, 1, 0]):
         outs.append(run_workgroup(text, q, k, v, q0, causal, scale, dt, order))
+    if rescales is not None:
+        # executions of the rescale block, summed over the 4 waves
+        assert rescales(run_workgroup.rescales), run_workgroup.rescales
     assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
     o_bytes, l_bytes = outs[0]
     rows = np.arange(q0, min(q0 + 256, Nq))
@@ -209,7 +215,36 @@ def test_generated_body_d64_matches_oracle(case):
 @pytest.mark.parametrize("d", [128, 64])
 def test_reference_moves_and_rescales(d):
     """Scores spread over tens of units: the lazy reference moves and O is rescaled."""
-    check("bf16", False, 256, 512, 0, scale=1.0, sigma=2.0, seed=5, outliers=0.02, d=d)
+    check("bf16", False, 256, 512, 0, scale=1.0, sigma=2.0, seed=5, outliers=0.02, d=d,
+          rescales=lambda n: n > 0)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_reference_moves_only_past_its_threshold(dt):
+    """Keys in three blocks whose scores sit 14, then 16, log2 units above the first
+    block's: the first step stays on the old reference (probabilities up to 2^14,
+    finite in f16 too), the second moves it, once per wave."""
+    d, nkv = 128, 192
+    q, k, v = workloads.make_inputs(1, 1, 1, 256, nkv, d, dt, 11, 1.0)
+    torch_dt = workloads.DTYPES[dt]
+    qq = torch.zeros(1, 1, 256, d)
+    qq[..., 0] = 1.0
+    kk = torch.zeros(1, 1, nkv, d)
+    kk[0, 0, 64:128, 0] = 14.0
+    kk[0, 0, 128:, 0] = 30.0
+    scale = math.log(2)            # score * scale * log2(e) = key[0] in log2 units
+    got = []
+    for order in ([0, 1, 2, 3], [3, 2, 1, 0]):
+        o, lse = run_workgroup(gen.body(dt, False, d), qq.to(torch_dt), kk.to(torch_dt), v,
+                               0, False, scale, dt, order)
+        got.append(run_workgroup.rescales)
+    assert got == [4, 4], got
+    o = torch.from_numpy(o.view(np.int16).copy()).view(torch_dt).reshape(256, d)
+    lse = lse.view(np.float32)
+    ref_o, ref_l = attention_fp64(workloads.to_f64(qq.to(torch_dt)), workloads.to_f64(kk.to(torch_dt)),
+                                  workloads.to_f64(v), scale, False)
+    assert float(np.max(np.abs(o.double().numpy() - ref_o[0, 0]))) <= TOL
+    assert float(np.max(np.abs(lse.astype(np.float64) - ref_l[0, 0]))) <= TOL
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.09])
