@@ -221,6 +221,17 @@ template <int D>
 __device__ __forceinline__ int swz_v(int row) {
   return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
 }
+// Tiles read both ways (row reads for one product, ds_read_b64_tr_b16 for the
+// other: Q, dO and K in the backward): the chunk index XOR
+// 4 * (row % 4) + (row / 4) % 4 at d = 128, 4 * ((row / 2) % 2) + (row / 4) % 4
+// at d = 64.  16 consecutive rows still see 16 distinct chunks (8 per row
+// parity at d = 64), and the 4 rows of a transposed read see 4 distinct
+// groups of 4 chunks, so neither read has a bank conflict (64 banks of 4 bytes).
+template <int D>
+__device__ __forceinline__ int swz_kt(int row) {
+  return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3))
+                  : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+}
 
 // ------------------------------- 64 rows per wave (bf16 / f16, d = 64 and 128)
 //
@@ -1266,19 +1277,19 @@ __global__ void __launch_bounds__(256) attn_splitkv_combine(const float* __restr
 // for dQ.  Every output element is written once by one wave (no atomics), so
 // the result is deterministic.
 //
-// Tiles live in LDS with the K swizzle (16-byte chunk index XOR a row
-// function); the same layout serves both operand reads, the 16-byte row
-// reads and the transposed ds_read_b64_tr_b16 reads.
+// Tiles live in LDS with the two-way swizzle swz_kt (16-byte chunk index XOR a
+// row function); the same layout serves both operand reads, the 16-byte row
+// reads and the transposed ds_read_b64_tr_b16 reads, without bank conflicts.
 
 // Transposed-read lane base for rows vrow and vrow + 8 of a 16-row group
-// stored with swz_k; the head-dimension block db is applied as "^ (db * 64)".
+// stored with swz_kt; the head-dimension block db is applied as "^ (db * 64)".
 template <int D>
-__device__ __forceinline__ int tr_base_k(int lane, int hi) {
+__device__ __forceinline__ int tr_base_bwd(int lane, int hi) {
   constexpr int ROWB = D * 2;
   const int g16 = lane >> 4, s16 = lane & 15;
   const int row = (g16 >> 1) * 4 + (s16 >> 2) + 8 * hi;
   const int c = (g16 & 1) * 2 + ((s16 & 3) >> 1);
-  return row * ROWB + ((c ^ swz_k<D>(row)) * 16) + (s16 & 1) * 8;
+  return row * ROWB + ((c ^ swz_kt<D>(row)) * 16) + (s16 & 1) * 8;
 }
 
 struct BwdParams {
@@ -1385,7 +1396,7 @@ __device__ __forceinline__ void attn_bwd_dkdv_body(const BwdParams& p) {
     const int ci = wave * (C::VCH / C::NW) + u;
     const int slot = ci * 64 + lane;
     const int row = slot / C::NCH;
-    const int c = (slot % C::NCH) ^ swz_k<D>(row);
+    const int c = (slot % C::NCH) ^ swz_kt<D>(row);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_t*)vall + ci * 1024, 16,
                                              (k0 + row) * C::ROWB + c * 16, 0, 0, 0);
   }
@@ -1419,7 +1430,7 @@ __device__ __forceinline__ void attn_bwd_dkdv_body(const BwdParams& p) {
       const int ci = isd ? i - C::CH : i;
       const int slot = ci * 64 + lane;
       const int row = slot / C::NCH;
-      const int c = (slot % C::NCH) ^ swz_k<D>(row);
+      const int c = (slot % C::NCH) ^ swz_kt<D>(row);
       lds_t* dst = (isd ? ost.template operator()<S>() : qst.template operator()<S>()) + ci * 1024;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(isd ? ro : rq, dst, 16, (q0 + row) * C::ROWB + c * 16,
                                                0, 0, 0);
@@ -1442,8 +1453,8 @@ __device__ __forceinline__ void attn_bwd_dkdv_body(const BwdParams& p) {
   wait_vm_lgkm<0>();   // V, K registers (and step 0) complete for this wave
   __builtin_amdgcn_s_barrier();
 
-  const int kbase = l32 * C::ROWB + ((half ^ (swz_k<D>(l32) & 1)) * 16) + ((swz_k<D>(l32) >> 1) * 32);
-  const int tb0 = tr_base_k<D>(lane, 0), tb1 = tr_base_k<D>(lane, 1);
+  const int kbase = l32 * C::ROWB + ((half ^ (swz_kt<D>(l32) & 1)) * 16) + ((swz_kt<D>(l32) >> 1) * 32);
+  const int tb0 = tr_base_bwd<D>(lane, 0), tb1 = tr_base_bwd<D>(lane, 1);
 
   f32x16 adv[D / 32], adk[D / 32];
 #pragma unroll
@@ -1663,7 +1674,7 @@ __device__ __forceinline__ void attn_bwd_dq_body(const BwdParams& p) {
       const int ci = isv ? i - C::CH : i;
       const int slot = ci * 64 + lane;
       const int row = slot / C::NCH;
-      const int c = (slot % C::NCH) ^ swz_k<D>(row);
+      const int c = (slot % C::NCH) ^ swz_kt<D>(row);
       lds_t* dst = (isv ? vst.template operator()<S>() : kst.template operator()<S>()) + ci * 1024;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? rv : rk, dst, 16, (kv0 + row) * C::ROWB + c * 16,
                                                0, 0, 0);
@@ -1695,8 +1706,8 @@ __device__ __forceinline__ void attn_bwd_dq_body(const BwdParams& p) {
   const float2 st = myq < p.Nq ? p.stats[qhead + myq] : make_float2(0.f, 0.f);
   const float l2v = st.x, dvv = st.y;
 
-  const int kbase = l32 * C::ROWB + ((half ^ (swz_k<D>(l32) & 1)) * 16) + ((swz_k<D>(l32) >> 1) * 32);
-  const int tb0 = tr_base_k<D>(lane, 0), tb1 = tr_base_k<D>(lane, 1);
+  const int kbase = l32 * C::ROWB + ((half ^ (swz_kt<D>(l32) & 1)) * 16) + ((swz_kt<D>(l32) >> 1) * 32);
+  const int tb0 = tr_base_bwd<D>(lane, 0), tb1 = tr_base_bwd<D>(lane, 1);
 
   f32x16 acc[D / 32];
 #pragma unroll
