@@ -983,6 +983,13 @@ def body(dt, causal, d=128):
     j + 1 needs a mask or does not exist (then the drain of tile j), then the
     epilogue."""
     configure(d)
+    try:
+        return _body(dt, causal)
+    finally:
+        configure(128)
+
+
+def _body(dt, causal):
     # s_nop: wait states for any vector write of an operand (SGPR or VGPR) made
     # by the compiled code just before the statement
     parts = ["s_nop 7"]
@@ -1012,7 +1019,6 @@ def body(dt, causal, d=128):
         parts += [f".Lm_{p}:", tile_step(dt, p, True, causal, f"m_{p}").text()]
         parts += [f".Ld_{p}:", drain(dt, p).text()]
     parts += [".Lepi:", epilogue(dt).text()]
-    configure(128)
     return "\n".join(parts) + "\n"
 
 
