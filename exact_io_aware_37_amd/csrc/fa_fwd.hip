@@ -237,8 +237,9 @@ __device__ __forceinline__ int swz_kt(int row) {
 //
 // The forward of the 16-bit inputs: each wave owns 64 query rows, one wave
 // per SIMD (4 waves, 256 rows per workgroup), and every K and V fragment read
-// from LDS feeds two matrix instructions (one per 32-row half).  O and Q live in accumulation registers, scores
-// and probabilities in vector registers; that split, the register
+// from LDS feeds two matrix instructions (one per 32-row half).  O and Q
+// live in accumulation registers, scores and probabilities in vector
+// registers; that split, the register
 // assignment and the instruction schedule are written out by
 // gen_fwd_w64.py, whose header describes them, into fa_fwd_w64.inc, and the
 // whole per-workgroup computation (Q load, the K/V DMA ring of 4 stages
