@@ -96,10 +96,10 @@ def measured_traffic(workload_name: str):
 
 
 def kernel_source_sha() -> str:
-    """sha256 over the kernel sources: fa_fwd.hip and the generator of its 64-row body."""
+    """sha256 over the kernel sources: fa_fwd.hip and the generators of its 64-row bodies."""
     import hashlib
     h = hashlib.sha256()
-    for name in ("fa_fwd.hip", "gen_fwd_w64.py"):
+    for name in ("fa_fwd.hip", "gen_fwd_w64.py", "gen_fwd_w64_fp8.py"):
         with open(os.path.join(ROOT, "exact_io_aware_37_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -400,8 +400,11 @@ def main():
                   "rows_per_wave": 32, "waves_per_block": 8,
                   "note": "two launches per step: chunk kernel, then combine"}
     elif path == "fp8":
+        # d = 128: the 64-row E4M3 body, 4 waves of 64 rows; d = 64: 8 waves of 32 rows
         launch = {"entry": "fa_fwd_fp8", "rows_per_block": 256, "keys_per_tile": 64,
-                  "threads_per_block": 512, "blocks": w.B * w.Hq * ((w.Nq + 255) // 256),
+                  "threads_per_block": 256 if w.D == 128 else 512,
+                  "lds_bytes": 65536 if w.D == 128 else 131072 * w.D // 128,
+                  "blocks": w.B * w.Hq * ((w.Nq + 255) // 256),
                   "descales": list(descales)}
     else:
         launch = fa.fa_launch_info(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, w.causal, dcode)[1]

@@ -437,16 +437,18 @@ attn_fwd_w64(Params p) {
 // O^T += V^T P^T contracts the 64 keys of a whole tile in one instruction
 // per 32 output dimensions, with P rounded to E4M3 (round to nearest even)
 // on the way.  The row sums of that rounded P come from the matrix cores
-// too (a v_mfma_f32_16x16x128_f8f6f4 per tile), so O is a convex
+// too (one more scaled 32x32x64 instruction per tile, with an all-ones
+// operand), so O is a convex
 // combination of V rows with the rounded weights, and the vector units do
 // no additions for them.  Q's and K's factors fold into the exponent scale,
 // V's into the final 1/l; O is written in bf16, lse in fp32.
 //
-// Workgroup, ring, DMA and lazy reference are those of the 16-bit path
-// (256 rows, 64-key tiles, 4-stage ring).  The lazy reference bounds every
-// probability by 2^8, inside E4M3's range (largest finite 448).  The
-// unmasked tiles run as a ping-pong between the two halves of the
-// workgroup (described at the loop).
+// This compiled kernel (8 waves of 32 rows) serves head dimension 64; at 128
+// the generated 64-row body above (attn_fwd_w64_e4m3) computes the same
+// thing with the same layouts.  Workgroup, ring, DMA and lazy reference are
+// those of the 16-bit path (256 rows, 64-key tiles, 4-stage ring).  The
+// lazy reference moves past 2^8.  The unmasked tiles run as a ping-pong
+// between the two halves of the workgroup (described at the loop).
 //
 // Operand layouts.  The 8-bit instruction pairs byte j of lane-half h of A
 // with byte j of lane-half h of B, so both operands only need the same
@@ -521,6 +523,126 @@ __device__ __forceinline__ f32x16 mma_e4m3(i32x8 a, i32x8 b, f32x16 c) {
 // A is unscaled (127).
 __device__ __forceinline__ f32x16 mma_e4m3_bscaled(i32x8 a, i32x8 b, f32x16 c, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, sb);
+}
+
+// -------------------------- 64 rows per wave, E4M3 inputs (head dimension 128)
+//
+// The FP8 forward on the generated 64-row body (gen_fwd_w64_fp8.py): the same
+// computation as attn_fwd_e4m3 below (scores on the 8-bit instruction, each
+// 64-key tile's probabilities rounded to E4M3 against a power-of-two reference
+// of their own, carried by the P operand's block scales, row sums on the
+// matrix instruction, O * V's factor / l in bf16), with each wave owning 64
+// rows, one wave per SIMD, so that every K and V fragment read from LDS feeds
+// two matrix instructions, and the instruction order set by the generator's
+// issue-cost schedule.  Operand layouts are those of attn_fwd_e4m3 (same
+// swizzles and byte orders); O leaves through LDS in whole bf16 rows.
+struct CfgW64E {
+  static constexpr int BR = 256, BC = 64, NT = 256;
+  static constexpr int ROWB = 128;                  // bytes per E4M3 K or V row
+  static constexpr int KSTAGE = BC * ROWB;
+  static constexpr int VRING = 4 * KSTAGE;
+  static constexpr int LDS_BYTES = 8 * KSTAGE;      // also holds the 4 waves' bf16 O tiles
+  static constexpr int NPIECE = KSTAGE / 2048;
+  static_assert(LDS_BYTES >= 4 * 64 * 256, "O staging");
+};
+
+template <bool CAUSAL>
+__device__ __forceinline__ void w64_item_e4m3(const Params& p, uint32_t lds0, int b, int hq, int qt) {
+  using C = CfgW64E;
+  int tid;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, half = lane >> 5;
+  const int hkv = hq / p.group;
+  const int q0 = qt * C::BR;
+  const int q0w = q0 + 64 * wave;
+  const size_t qhead = (size_t)(b * p.Hq + hq) * p.Nq;
+  const size_t kvhead = (size_t)(b * p.Hkv + hkv) * p.Nkv;
+  const u32x4s rq = raw_desc(static_cast<const uint8_t*>(p.q) + qhead * 128, (uint32_t)p.Nq * 128u);
+  const u32x4s rk = raw_desc(static_cast<const uint8_t*>(p.k) + kvhead * 128, (uint32_t)p.Nkv * 128u);
+  const u32x4s rv = raw_desc(static_cast<const uint8_t*>(p.v) + kvhead * 128, (uint32_t)p.Nkv * 128u);
+  const u32x4s ro = raw_desc(static_cast<uint16_t*>(p.o) + qhead * 128, (uint32_t)p.Nq * 256u);
+  const u32x4s rl = raw_desc(p.lse + qhead, (uint32_t)p.Nq * 4u);
+
+  // DMA share: waves 0-1 the K tile, waves 2-3 the V tile, 4 KiB each; piece
+  // c, lane l: 16 bytes of row 8c + l/8, logical chunk l%8 at chunk ^ swizzle.
+  const bool isv = wave >= 2;
+  const u32x4s rdma = isv ? rv : rk;
+  const int ci0 = (C::NPIECE * wave) & (2 * C::NPIECE - 1);
+  const uint32_t dmabase = lds0 + (isv ? (uint32_t)C::VRING : 0u) + (uint32_t)ci0 * 1024u;
+  uint32_t dmaoff[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int row = (ci0 + u) * 8 + lane / 8;
+    const int sw = isv ? swz8_v<128>(row) : swz8_k<128>(row);
+    dmaoff[u] = (uint32_t)(row * C::ROWB + (((lane % 8) ^ sw) * 16));
+  }
+  // K fragment: key row l32, head-dimension bytes 64cd + 32*half as two chunks.
+  const uint32_t kbase = (uint32_t)(l32 * C::ROWB + (((half * 2) ^ swz8_k<128>(l32)) * 16));
+  const uint32_t kaddr0 = lds0 + (kbase ^ 0u), kaddr1 = lds0 + ((kbase ^ 0u) ^ 16u),
+                 kaddr2 = lds0 + (kbase ^ 64u), kaddr3 = lds0 + ((kbase ^ 64u) ^ 16u);
+  // V^T fragment by ds_read_b64_tr_b8 (the lane pattern of attn_fwd_e4m3).
+  const int g16 = lane >> 4, s16 = lane & 15, t8 = s16 >> 1;
+  const int vrow = (t8 >> 2) * 8 + (g16 >> 1) * 4 + (t8 & 3);
+  const uint32_t vbase = (uint32_t)(vrow * C::ROWB + swz8_v<128>(vrow) * 16 + (g16 & 1) * 16 + (s16 & 1) * 8);
+  const uint32_t vr = lds0 + (uint32_t)C::VRING;
+  const uint32_t vaddr0 = vr + (vbase ^ 0u), vaddr1 = vr + (vbase ^ 32u),
+                 vaddr2 = vr + (vbase ^ 64u), vaddr3 = vr + (vbase ^ 96u);
+  // Q rows q0w + 32h + l32, bytes 64cd + 32*half (+ 32 rows for h = 1)
+  const uint32_t qoff = (uint32_t)((q0w + l32) * C::ROWB + half * 32);
+  const int big = 0x3fffffff;
+  const int lim0 = min(p.Nkv - 1, CAUSAL ? q0w + l32 : big);
+  const int lim1 = min(p.Nkv - 1, CAUSAL ? q0w + 32 + l32 : big);
+  // bf16 O rows of 256 bytes: row q0w + 4i + lane/16, 16-byte column lane%16
+  const uint32_t ooff = (uint32_t)((q0w + lane / 16) * 256 + (lane % 16) * 16);
+  const uint32_t lseoff = (uint32_t)((q0w + l32) * 4);
+  const uint32_t obase = lds0 + (uint32_t)wave * (64u * 256u);
+  const int kv_end = CAUSAL ? min(p.Nkv, q0 + 256) : p.Nkv;
+  const uint32_t ntiles = (uint32_t)((kv_end + 63) / 64);
+  const uint32_t nmain = (uint32_t)(CAUSAL ? min((q0 + 1) / 64, p.Nkv / 64) : p.Nkv / 64);
+  const uint32_t sl2 = __float_as_uint(p.sl2);
+  const uint32_t qxor = p.qmode == 1 ? 0x80808080u : 0u;
+  const uint32_t qand = p.qmode == 2 ? 0u : 0xffffffffu;
+  const uint32_t oscale = __float_as_uint(p.oscale);
+
+#define FA_W64_E4M3_OPERANDS                                                                \
+  [rq] "s"(rq), [rdma] "s"(rdma), [ro] "s"(ro), [rl] "s"(rl), [dmabase] "s"(dmabase),       \
+      [sl2] "s"(sl2), [qxor] "s"(qxor), [qand] "s"(qand), [ntiles] "s"(ntiles),             \
+      [nmain] "s"(nmain), [obase] "s"(obase), [oscale] "s"(oscale), [kaddr0] "v"(kaddr0),   \
+      [kaddr1] "v"(kaddr1), [kaddr2] "v"(kaddr2), [kaddr3] "v"(kaddr3), [vaddr0] "v"(vaddr0), \
+      [vaddr1] "v"(vaddr1), [vaddr2] "v"(vaddr2), [vaddr3] "v"(vaddr3),                     \
+      [dmaoff0] "v"(dmaoff[0]), [dmaoff1] "v"(dmaoff[1]), [dmaoff2] "v"(dmaoff[2]),         \
+      [dmaoff3] "v"(dmaoff[3]), [qoff] "v"(qoff), [lim0] "v"(lim0), [lim1] "v"(lim1),       \
+      [ooff] "v"(ooff), [lseoff] "v"(lseoff)
+  if constexpr (CAUSAL) asm volatile(FA_W64_E4M3_CAUSAL : : FA_W64_E4M3_OPERANDS : FA_W64_CLOBBERS);
+  else asm volatile(FA_W64_E4M3_FULL : : FA_W64_E4M3_OPERANDS : FA_W64_CLOBBERS);
+#undef FA_W64_E4M3_OPERANDS
+}
+
+template <bool CAUSAL>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+attn_fwd_w64_e4m3(Params p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[CfgW64E::LDS_BYTES];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_t*)lds;
+  if constexpr (!CAUSAL) {
+    int b, hq, qt;
+    map_block(p, false, b, hq, qt);
+    w64_item_e4m3<false>(p, lds0, b, hq, qt);
+  } else {
+    // persistent zig-zag grid, as attn_fwd_w64
+    const int G = (int)gridDim.x, bid = (int)blockIdx.x;
+    const int n = p.n_heads * p.n_qtiles;
+    for (int j = 0;; ++j) {
+      const int r = (j & 1) ? (j + 1) * G - 1 - bid : j * G + bid;
+      if (r >= n) break;
+      const int rr = r / p.n_heads;
+      const int hl = r - rr * p.n_heads;
+      const int b = hl / p.Hq;
+      if (j) __syncthreads();
+      w64_item_e4m3<true>(p, lds0, b, hl - b * p.Hq, p.n_qtiles - 1 - rr);
+    }
+  }
 }
 
 template <int D, bool CAUSAL>
@@ -2093,6 +2215,15 @@ int dispatch16(const Params& p, int d, bool causal, long long blocks, hipStream_
 
 template <int D, bool CAUSAL>
 int run8(const Params& p, long long blocks, hipStream_t stream) {
+  if constexpr (D == 128) {   // the 64-row body; causal grids persistent as in run_w64
+    if constexpr (CAUSAL) {
+      int cus = 0;
+      const int st = cu_count(stream, &cus);
+      if (st != FA_OK) return st;
+      blocks = blocks < cus ? blocks : cus;
+    }
+    return launch(attn_fwd_w64_e4m3<CAUSAL>, 0, p, blocks, CfgW64E::NT, stream);
+  }
   return launch(attn_fwd_e4m3<D, CAUSAL>, 0, p, blocks, Cfg8<D>::NT, stream);
 }
 

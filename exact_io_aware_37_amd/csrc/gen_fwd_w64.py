@@ -3,7 +3,8 @@
     python -m exact_io_aware_37_amd.csrc.gen_fwd_w64      (run by the build)
 
 writes ``fa_fwd_w64.inc`` beside this file: one string constant per kernel
-variant (bf16 / f16 inputs, causal or not, head dimension 128) holding the
+variant (bf16 / f16 inputs, causal or not, head dimension 64 or 128; and the
+E4M3 variants of gen_fwd_w64_fp8.py) holding the
 whole per-workgroup computation as gfx950 assembly, which the kernel in
 ``fa_fwd.hip`` runs in one inline-asm statement after computing addresses and
 buffer descriptors in C++.
@@ -234,11 +235,13 @@ def raw(text, kind="salu", cost=4, reads=(), writes=()):
 # A matrix instruction's A/B operands are not rewritten within 8 slots of it.
 
 WS_MFMA_VALU = 18
+WS_MFMA8_VALU = 24   # the 64-cycle 8-bit 32x32x64 instruction writes its last results later
 WS_VALU_MFMA = 2
 WS_TRANS = 1
 WS_MASK = 4
 WS_PERM = 2
 WS_WAR = 8
+WS_WAR8 = 16
 
 
 class Stream:
@@ -336,7 +339,7 @@ class Block:
         for r in ins.writes:
             if k == "mfma":
                 self.rdy_m[r] = start + 1                     # accumulation chains forward
-                self.rdy_v[r] = start + 1 + WS_MFMA_VALU
+                self.rdy_v[r] = start + 1 + (WS_MFMA_VALU if ins.cost <= 32 else WS_MFMA8_VALU)
             elif k == "trans":
                 self.rdy_v[r] = start + 1 + WS_TRANS
                 self.rdy_m[r] = start + 1 + WS_VALU_MFMA
@@ -357,8 +360,9 @@ class Block:
         if k == "salu" and "m0" in ins.writes:
             self.m0 = start + 2
         if k == "mfma":
+            war = WS_WAR if ins.cost <= 32 else WS_WAR8
             for r in ins.srcab:
-                self.war[r] = max(self.war.get(r, 0), start + 1 + WS_WAR)
+                self.war[r] = max(self.war.get(r, 0), start + 1 + war)
         if k == "lds":
             self.lgkm.append(set(ins.writes))
         return ins
@@ -875,8 +879,9 @@ def drain(dt, parity):
     return b
 
 
-def epilogue(dt):
-    """O / l through LDS to whole-row stores; lse = (m + log2 l) ln 2."""
+def epilogue(dt, oscale=None):
+    """O / l through LDS to whole-row stores; lse = (m + log2 l) ln 2.  With `oscale` (an
+    SGPR operand name) O is multiplied by it as well."""
     b = Block()
     b.put(Ins("s_waitcnt vmcnt(0) lgkmcnt(0)", "wait"))
     b.put(Ins("s_barrier", "barrier"))   # every wave is done with the ring
@@ -888,6 +893,8 @@ def epilogue(dt):
             b.pad(18)
         b.put(valu(f"v_add_f32 {lr}, {lr}, {LACC0[h]}", [lr, LACC0[h]], [lr]))
         b.put(valu(f"v_rcp_f32 {ALPHA[h]}, {lr}", [lr], [ALPHA[h]], kind="trans"))
+        if oscale is not None:
+            b.put(valu(f"v_mul_f32 {ALPHA[h]}, {{{oscale}}}, {ALPHA[h]}", [ALPHA[h]], [ALPHA[h]]))
         b.put(valu(f"v_log_f32 {TMP[h]}, {lr}", [lr], [TMP[h]], kind="trans"))
         b.put(valu(f"v_add_f32 {TMP[h]}, {MRUN[h]}, {TMP[h]}", [MRUN[h], TMP[h]], [TMP[h]]))
         b.put(valu(f"v_mul_f32 {TMP[h]}, 0x3f317218, {TMP[h]}", [TMP[h]], [TMP[h]]))
@@ -1064,6 +1071,15 @@ def write_inc(path=None):
             for causal in (False, True):
                 name = f"FA_W64{'' if d == 128 else 'D64'}_{dt.upper()}_{'CAUSAL' if causal else 'FULL'}"
                 out.append(c_macro(name, asm_text(dt, causal, d)))
+    here = os.path.dirname(os.path.abspath(__file__))
+    sys.path.insert(0, here)
+    try:
+        import gen_fwd_w64_fp8
+    finally:
+        sys.path.remove(here)
+    for causal in (False, True):
+        name = f"FA_W64_E4M3_{'CAUSAL' if causal else 'FULL'}"
+        out.append(c_macro(name, gen_fwd_w64_fp8.asm_text8(causal)))
     out.append("#define FA_W64_CLOBBERS " + ", ".join(f'"{c}"' for c in clobbers()))
     out.append("")
     text = "\n".join(out)

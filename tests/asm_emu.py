@@ -53,6 +53,33 @@ def f16_val(bits):
     return np.asarray(bits, np.uint16).astype(np.uint16).view(np.float16).astype(np.float32)
 
 
+def e4m3_values():
+    """The 256 OCP E4M3 codes as float64 (bias 7, subnormals below 2^-6, 0x7f / 0xff NaN)."""
+    out = np.zeros(256, np.float64)
+    for c in range(256):
+        s, e, m = c >> 7, (c >> 3) & 15, c & 7
+        v = (m / 8.0) * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7)
+        out[c] = np.nan if (c & 0x7F) == 0x7F else (-v if s else v)
+    return out
+
+
+E4M3 = e4m3_values()
+_E4M3_POS = E4M3[:0x7F]                      # codes 0 .. 126, increasing
+
+
+def e4m3_bits(x):
+    """float32 -> E4M3 codes, round to nearest, ties to the even code; |x| above 448
+    saturates (the kernel never converts such values)."""
+    x = np.asarray(x, np.float64)
+    ax = np.minimum(np.abs(x), 448.0)
+    hi = np.searchsorted(_E4M3_POS, ax, side="left").clip(0, 126)
+    lo = (hi - 1).clip(0, 126)
+    dlo, dhi = ax - _E4M3_POS[lo], _E4M3_POS[hi] - ax
+    pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    pick = np.where(ax == _E4M3_POS[hi], hi, pick)
+    return (pick | np.where(x < 0, 0x80, 0)).astype(np.uint32)
+
+
 def f32(u):
     return np.asarray(u, np.uint32).view(np.float32)
 
@@ -393,6 +420,23 @@ class Emu:
         w.v[i + 1] = res[:, 2] | (res[:, 3] << 16)
         w.pend_lgkm.append({("v", i), ("v", i + 1)})
 
+    def op_ds_read_b64_tr_b8(self, w, a, line):
+        """Within each group of 16 lanes, result lane r, byte t gets byte r % 8 of what
+        source lane 2t + r / 8 addressed."""
+        f, i, n = parse_reg(a[0])
+        base = self._lds_addr(w, a[1].split()[0], line, 8)
+        idx = base[:, None] + np.arange(8)[None, :]
+        src = self.lds[idx].reshape(L, 8).copy()                      # [L, 8] bytes
+        res = np.zeros((L, 8), np.uint8)
+        r = np.arange(16)
+        for g in range(4):
+            for t in range(8):
+                res[16 * g + r, t] = src[16 * g + 2 * t + r // 8, r % 8]
+        words = res.view(np.uint32)                                   # [L, 2]
+        w.v[i] = words[:, 0]
+        w.v[i + 1] = words[:, 1]
+        w.pend_lgkm.append({("v", i), ("v", i + 1)})
+
     def op_ds_write_b64(self, w, a, line):
         base = self.vread(w, a[0]).astype(np.int64)
         if base.min() < 0 or base.max() + 8 > len(self.lds):
@@ -443,6 +487,42 @@ class Emu:
             out.append(u32((c + prod[4 * (lanes // 16) + r, lanes % 16]).astype(np.float32)))
         for r in range(4):
             self.vwrite(w, D, out[r], r)
+
+    def _mfma8(self, w, a, sa=None, sb=None):
+        """v_mfma[_scale]_f32_32x32x64_f8f6f4 on E4M3 operands: 8 registers (32 bytes)
+        per lane; byte j of lane-half h of A meets byte j of lane-half h of B, so
+        D[i][c] = sum over (h, j) of A[lane i + 32h][j] B[lane c + 32h][j] (+ C).  With
+        scales, lane x + 32b (low byte, E8M0, bias 127) scales bytes 16b .. 16b+15 of
+        row (A) or column (B) x in both lane-halves."""
+        D, A, B, C = a[:4]
+        lanes = np.arange(L)
+        ab = np.stack([self.vread(w, A, k) for k in range(8)]).T.copy().view(np.uint8)  # [L, 32]
+        bb = np.stack([self.vread(w, B, k) for k in range(8)]).T.copy().view(np.uint8)
+        av, bv = E4M3[ab], E4M3[bb]                                                      # [L, 32]
+        if sa is not None:
+            for blk in range(2):
+                fa = 2.0 ** (sa[blk * 32 + lanes % 32].astype(np.float64) - 127)
+                fb = 2.0 ** (sb[blk * 32 + lanes % 32].astype(np.float64) - 127)
+                av[:, 16 * blk:16 * blk + 16] *= fa[:, None]
+                bv[:, 16 * blk:16 * blk + 16] *= fb[:, None]
+        A_m = np.concatenate([av[:32], av[32:]], axis=1)      # [32 rows, 64]
+        B_m = np.concatenate([bv[:32], bv[32:]], axis=1)      # [32 cols, 64]
+        prod = A_m @ B_m.T
+        out = []
+        for r in range(16):
+            c = np.zeros(L, np.float64) if C == "0" else f32(self.vread(w, C, r)).astype(np.float64)
+            rows = 8 * (r // 4) + 4 * (lanes // 32) + r % 4
+            out.append(u32((c + prod[rows, lanes % 32]).astype(np.float32)))
+        for r in range(16):
+            self.vwrite(w, D, out[r], r)
+
+    def op_v_mfma_f32_32x32x64_f8f6f4(self, w, a, line):
+        self._mfma8(w, a)
+
+    def op_v_mfma_scale_f32_32x32x64_f8f6f4(self, w, a, line):
+        sa = self.vread(w, a[4]) & 0xFF
+        sb = self.vread(w, a[5].split()[0]) & 0xFF
+        self._mfma8(w, a, sa, sb)
 
     def op_v_mfma_f32_16x16x32_bf16(self, w, a, line):
         self._mfma16(w, a, lambda b: bf16_val(b).astype(np.float64))
@@ -505,6 +585,30 @@ class Emu:
         lo = bf16_bits(f32(self.vread(w, a[1])))
         hi = bf16_bits(f32(self.vread(w, a[2])))
         self._w(w, a[0], lo | (hi << 16))
+
+    def op_v_cvt_pk_fp8_f32(self, w, a, line):
+        """Two E4M3 bytes into the low word of the destination, or its high word with
+        op_sel:[0,0,1]; the other word keeps its value."""
+        lo = e4m3_bits(f32(self.vread(w, a[1])))
+        hi = e4m3_bits(f32(self.vread(w, a[2].split()[0])))
+        pair = lo | (hi << 8)
+        old = self.vread(w, a[0])
+        if "op_sel:[0,0,1]" in line:
+            val = (old & 0xFFFF) | (pair << 16)
+        else:
+            val = (old & 0xFFFF0000) | pair
+        self._w(w, a[0], val.astype(np.uint32))
+
+    def op_v_floor_f32(self, w, a, line):
+        self._w(w, a[0], u32(np.floor(f32(self.vread(w, a[1])))))
+
+    def op_v_min_f32(self, w, a, line):
+        self._w(w, a[0], u32(np.minimum(f32(self.vread(w, a[1])), f32(self.vread(w, a[2])))))
+
+    def op_v_cvt_i32_f32(self, w, a, line):
+        x = f32(self.vread(w, a[1])).astype(np.float64)
+        x = np.where(np.isnan(x), 0.0, np.clip(x, -2.0 ** 31, 2.0 ** 31 - 1))
+        self._w(w, a[0], np.trunc(x).astype(np.int64).astype(np.uint32))
 
     def op_v_cvt_pk_f16_f32(self, w, a, line):
         lo = f16_bits(f32(self.vread(w, a[1])))

@@ -61,3 +61,14 @@ def test_masked_step(parity):
     block = gen.tile_step("bf16", parity, True, True, "t")
     cycles, _ = gen.issue_time(block.out)
     assert cycles <= 2900, cycles          # 2848 for this schedule; 3904 with unpipelined masks
+
+
+@pytest.mark.parametrize("parity", range(4))
+def test_fp8_unmasked_step(parity):
+    """The E4M3 body: 18 matrix instructions of 64 cycles per step; the softmax's vector
+    work (the same per score as the 16-bit body, against half the matrix work) bounds it."""
+    import gen_fwd_w64_fp8 as gen8
+    block = gen8.tile_step8(parity, False)
+    cycles, busy = gen.issue_time(block.out)
+    assert busy == 16 * 64 + 2 * 64
+    assert cycles <= 1850, cycles          # 1806-1810 for this schedule
