@@ -1059,12 +1059,25 @@ __device__ __forceinline__ void attn_splitkv_body(const SplitParams& p) {
 
   const long long item = (long long)blockIdx.x * C::NW + wave;
   if (item >= p.items) return;   // no barrier in this kernel: idle waves may leave
-  const int s = (int)(item % p.S);
-  long long rest = item / p.S;
-  const int rb = (int)(rest % p.nrb);
-  rest /= p.nrb;
-  const int g = (int)(rest % p.Hkv);
-  const int b = (int)(rest / p.Hkv);
+  // Dense: the chunks of one (batch, key/value head) are neighbours.  Paged:
+  // the key/value heads are fastest, so that the waves reading the pieces of
+  // one token row of a pool block (one per head) run side by side.
+  int s, rb, g, b;
+  if constexpr (PAGED) {
+    g = (int)(item % p.Hkv);
+    long long rest = item / p.Hkv;
+    s = (int)(rest % p.S);
+    rest /= p.S;
+    rb = (int)(rest % p.nrb);
+    b = (int)(rest / p.nrb);
+  } else {
+    s = (int)(item % p.S);
+    long long rest = item / p.S;
+    rb = (int)(rest % p.nrb);
+    rest /= p.nrb;
+    g = (int)(rest % p.Hkv);
+    b = (int)(rest / p.Hkv);
+  }
 
   // This lane's packed row, its query head and query index.
   const int r = rb * 32 + l32;
