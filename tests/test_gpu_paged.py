@@ -85,6 +85,16 @@ def test_several_new_queries(causal, Nq):
     check("queries", 3, 8, 2, Nq, [Nq, 300, 1025], 128, 16, causal, seed=Nq + causal)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_odd_kv_head_count(causal):
+    """Hkv = 3 with 37 new queries per sequence (4 row blocks of the 3 query heads of a group):
+    work items are numbered with the key/value head fastest, so here the 8 waves of a workgroup
+    straddle chunks and row blocks."""
+    check("odd kv heads", 2, 9, 3, 37, [500, 2100], 128, 16, causal, seed=11 + causal)
+    check("odd kv heads, 3 splits", 3, 9, 3, 37, [37, 500, 2100], 64, 32, causal, seed=13 + causal,
+          splits=3)
+
+
 def test_rows_without_keys():
     """Causal with N_q above a sequence's length, and an empty sequence: O = 0, lse = -inf."""
     check("empty rows", 3, 4, 2, 8, [3, 0, 40], 64, 16, True, seed=5)
