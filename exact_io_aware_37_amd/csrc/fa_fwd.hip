@@ -1445,6 +1445,7 @@ struct BwdParams {
   float scale;      // as given (any finite value)
   float sl2;        // scale * log2 e (sign kept)
   int n_tiles;      // workgroup tiles along the stationary axis
+  int items;        // work items of the kernel launched with these parameters
   int hsplit;       // dK/dV pass: query heads of a group dealt over this many workgroups
 };
 
@@ -1484,7 +1485,7 @@ struct CfgBwdKV {
 };
 
 template <typename T, int D, bool CAUSAL>
-__device__ __forceinline__ void attn_bwd_dkdv_body(const BwdParams& p) {
+__device__ __forceinline__ void attn_bwd_dkdv_body(const BwdParams& p, int item, int n_items) {
   using C = CfgBwdKV<D>;
   using M = Mma16<T>;
   __shared__ __attribute__((aligned(1024))) unsigned char q0s[C::QTB];
@@ -1509,10 +1510,10 @@ __device__ __forceinline__ void attn_bwd_dkdv_body(const BwdParams& p) {
   // fastest.  Causal: the first key tiles see the most queries, so they are
   // listed first, (b, kv head, share) fastest, and the longest items start in
   // the first round of workgroups.
-  const int n_r1 = gridDim.x / p.n_tiles;
-  const int xl = xcd_local((int)blockIdx.x, (int)gridDim.x);
-  const int kt = CAUSAL ? (int)(blockIdx.x / n_r1) : xl % p.n_tiles;
-  const int r1 = CAUSAL ? (int)(blockIdx.x % n_r1) : xl / p.n_tiles;
+  const int n_r1 = n_items / p.n_tiles;
+  const int xl = xcd_local(item, n_items);
+  const int kt = CAUSAL ? item / n_r1 : xl % p.n_tiles;
+  const int r1 = CAUSAL ? item % n_r1 : xl / p.n_tiles;
   const int hs = r1 % p.hsplit;
   const int bg = r1 / p.hsplit;
   const int g = bg % p.Hkv;
@@ -1709,10 +1710,30 @@ __device__ __forceinline__ void attn_bwd_dkdv_body(const BwdParams& p) {
   }
 }
 
+// Causal backward grids are persistent, as the causal forward's: min(items,
+// CUs) workgroups, one per CU, take the ranks bid, 2G - 1 - bid, 2G + bid,
+// 4G - 1 - bid, ... of the longest-first item order (G workgroups), so that
+// no workgroup waits for the dispatcher between short items.  Each item ends
+// with no transfer in flight; the barrier keeps the next item's transfers
+// out of the LDS until every wave has finished reading it.
+template <typename F>
+__device__ __forceinline__ void persistent_items(int n_items, F&& body) {
+  const int G = (int)gridDim.x, bid = (int)blockIdx.x;
+  for (int j = 0;; ++j) {
+    const int r = (j & 1) ? (j + 1) * G - 1 - bid : j * G + bid;
+    if (r >= n_items) break;   // every later rank of this workgroup is larger
+    if (j) __syncthreads();
+    body(r);
+  }
+}
+
 template <typename T, int D, bool CAUSAL>
 __global__ void __launch_bounds__(CfgBwdKV<D>::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dkdv(BwdParams p) {
-  attn_bwd_dkdv_body<T, D, CAUSAL>(p);
+  if constexpr (CAUSAL)
+    persistent_items(p.items, [&](int r) { attn_bwd_dkdv_body<T, D, true>(p, r, p.items); });
+  else
+    attn_bwd_dkdv_body<T, D, false>(p, (int)blockIdx.x, (int)gridDim.x);
 }
 
 // dK, dV = sum over the head shares of their fp32 partials, in share order
@@ -1747,7 +1768,7 @@ struct CfgBwdQ {
 };
 
 template <typename T, int D, bool CAUSAL>
-__device__ __forceinline__ void attn_bwd_dq_body(const BwdParams& p) {
+__device__ __forceinline__ void attn_bwd_dq_body(const BwdParams& p, int item, int n_items) {
   using C = CfgBwdQ<D>;
   using M = Mma16<T>;
   __shared__ __attribute__((aligned(1024))) unsigned char k0s[C::TILEB];
@@ -1780,10 +1801,10 @@ __device__ __forceinline__ void attn_bwd_dq_body(const BwdParams& p) {
   // Work item: (b, query head, query tile).  Non-causal: query tiles fastest.
   // Causal: the last query tiles see the most keys; they are listed first,
   // (b, head) fastest.
-  const int n_bh = gridDim.x / p.n_tiles;
-  const int xl = xcd_local((int)blockIdx.x, (int)gridDim.x);
-  const int qt = CAUSAL ? p.n_tiles - 1 - (int)(blockIdx.x / n_bh) : xl % p.n_tiles;
-  const int bh = CAUSAL ? (int)(blockIdx.x % n_bh) : xl / p.n_tiles;
+  const int n_bh = n_items / p.n_tiles;
+  const int xl = xcd_local(item, n_items);
+  const int qt = CAUSAL ? p.n_tiles - 1 - item / n_bh : xl % p.n_tiles;
+  const int bh = CAUSAL ? item % n_bh : xl / p.n_tiles;
   const int hq = bh % p.Hq;
   const int b = bh / p.Hq;
   const int hkv = hq / p.group;
@@ -1928,7 +1949,10 @@ __device__ __forceinline__ void attn_bwd_dq_body(const BwdParams& p) {
 template <typename T, int D, bool CAUSAL>
 __global__ void __launch_bounds__(CfgBwdQ<D>::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bwd_dq(BwdParams p) {
-  attn_bwd_dq_body<T, D, CAUSAL>(p);
+  if constexpr (CAUSAL)
+    persistent_items(p.items, [&](int r) { attn_bwd_dq_body<T, D, true>(p, r, p.items); });
+  else
+    attn_bwd_dq_body<T, D, false>(p, (int)blockIdx.x, (int)gridDim.x);
 }
 
 // ------------------------------------------------------------- fp32 path
@@ -2366,10 +2390,16 @@ int run_bwd(BwdParams p, long long rows, hipStream_t stream) {
   (void)hipGetLastError();
   const long long pblocks = (rows * (D / 8) + 255) / 256;
   hipLaunchKernelGGL((attn_bwd_prep<T, D>), dim3((unsigned)pblocks), dim3(256), 0, stream, p, rows);
+  // Causal grids: one persistent workgroup per CU at most.
+  int cus = 0x7fffffff;
+  if (CAUSAL) {
+    const int st = cu_count(stream, &cus);
+    if (st != FA_OK) return st;
+  }
   BwdParams pk = p;
   pk.n_tiles = (p.Nkv + CfgBwdKV<D>::BKV - 1) / CfgBwdKV<D>::BKV;
-  hipLaunchKernelGGL((attn_bwd_dkdv<T, D, CAUSAL>),
-                     dim3((unsigned)((long long)p.B * p.Hkv * p.hsplit * pk.n_tiles)),
+  pk.items = p.B * p.Hkv * p.hsplit * pk.n_tiles;
+  hipLaunchKernelGGL((attn_bwd_dkdv<T, D, CAUSAL>), dim3((unsigned)min(pk.items, cus)),
                      dim3(CfgBwdKV<D>::NT), 0, stream, pk);
   if (p.hsplit > 1) {
     const long long n4 = (long long)p.B * p.Hkv * p.Nkv * D / 4;
@@ -2379,7 +2409,8 @@ int run_bwd(BwdParams p, long long rows, hipStream_t stream) {
   }
   BwdParams pq = p;
   pq.n_tiles = (p.Nq + CfgBwdQ<D>::BR - 1) / CfgBwdQ<D>::BR;
-  hipLaunchKernelGGL((attn_bwd_dq<T, D, CAUSAL>), dim3((unsigned)((long long)p.B * p.Hq * pq.n_tiles)),
+  pq.items = p.B * p.Hq * pq.n_tiles;
+  hipLaunchKernelGGL((attn_bwd_dq<T, D, CAUSAL>), dim3((unsigned)min(pq.items, cus)),
                      dim3(CfgBwdQ<D>::NT), 0, stream, pq);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
@@ -2809,6 +2840,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   p.scale = scale;
   p.sl2 = scale * kLog2e;
   p.n_tiles = 0;
+  p.items = 0;
   const long long rows = (long long)B * Hq * N_q;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == FA_BF16) return dispatch_bwd<__bf16>(p, rows, d, causal != 0, s);
